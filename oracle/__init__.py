@@ -1,0 +1,126 @@
+"""ctypes binding for the fp64 attention oracle (``oracle.c``).
+
+TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. The GPU path never
+imports it, and it never imports the GPU path.
+
+All arrays are float64, C-contiguous, ``[B,H,N,d]`` (statistics ``[B,H,N]``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# A test that plants a mistake in a copy of oracle.c points this at the copy.
+_LIB_OVERRIDE = os.environ.get("ORACLE_LIB")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def compile_c(src: str, out: str) -> None:
+    """gcc, fp64, OpenMP, no fast-math and no FMA contraction."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+           "-ffp-contract=off", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so``."""
+    if force or not os.path.exists(_LIB):
+        compile_c(_SRC, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB):
+                build(force=False)
+            lib = ctypes.CDLL(_LIB)
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_fwd.argtypes = [_dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_double, ctypes.c_int, _dp, _dp]
+        lib.oracle_fwd_rows.argtypes = [_dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_int64,
+                                        _i64p, _dp, _dp]
+        lib.oracle_bwd.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                                   _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if a.ndim != 4:
+        raise ValueError("expected a [B,H,N,d] array")
+    return a
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_dp)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs with."""
+    return int(_load().oracle_num_threads())
+
+
+def fwd(q, k, v, scale: float, causal: bool):
+    """Standard attention forward: returns (O [B,H,N,d], lse [B,H,N])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one shape")
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), int(bool(causal)),
+                       _ptr(o), _ptr(lse))
+    return o, lse
+
+
+def fwd_rows(q, k, v, scale: float, causal: bool, rows):
+    """Forward for selected flat rows ``(b*H + h)*N + i``: returns (O_rows [n,d], lse_rows [n])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= B * H * N):
+        raise ValueError("row index out of range")
+    o = np.empty((rows.size, d), dtype=np.float64)
+    lse = np.empty(rows.size, dtype=np.float64)
+    _load().oracle_fwd_rows(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale),
+                            int(bool(causal)), rows.size,
+                            rows.ctypes.data_as(_i64p), _ptr(o), _ptr(lse))
+    return o, lse
+
+
+def bwd(q, k, v, dout, scale: float, causal: bool) -> dict:
+    """Forward plus analytic backward of ``L = sum(dout * O)``.
+
+    Returns a dict with o, lse, dq, dk, dv, D_pdp (sum_j P_ij dP_ij) and D_odo (dO_i . O_i).
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, d = q.shape
+    for t in (k, v, dout):
+        if t.shape != q.shape:
+            raise ValueError("q, k, v, dout must share one shape")
+    out = {name: np.empty_like(q) for name in ("o", "dq", "dk", "dv")}
+    for name in ("lse", "D_pdp", "D_odo"):
+        out[name] = np.empty((B, H, N), dtype=np.float64)
+    _load().oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d, float(scale),
+                       int(bool(causal)), _ptr(out["o"]), _ptr(out["lse"]), _ptr(out["dq"]),
+                       _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["D_pdp"]), _ptr(out["D_odo"]))
+    return out

@@ -1,0 +1,197 @@
+/*
+ * fp64 CPU oracle for exact scaled-dot-product attention, forward and backward.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library. The GPU path shares no
+ * code with it, and nothing in the GPU path may call it.
+ *
+ * What it computes is standard attention as the pages define it: "FlashAttention:
+ * making attention fast by respecting the memory hierarchy" (groundtruth.day,
+ * paragraph on what attention costs) describes the full N-by-N grid of scores,
+ * the softmax over each row of that grid and the multiplication by the values;
+ * the michaelc-yu summary of Dao et al. ("What FlashAttention targets") states
+ * that the method must give the same outputs as this naive formulation. This
+ * file is that naive formulation, one query row (or, in the backward, one key
+ * column) at a time, in double precision, with no tiling, no online softmax
+ * and no reordering beyond the definition:
+ *
+ *   S_ij  = scale * q_i . k_j                 (causal: only j <= i is kept)
+ *   m_i   = max_j S_ij,  l_i = sum_j exp(S_ij - m_i)
+ *   P_ij  = exp(S_ij - m_i) / l_i,  lse_i = m_i + ln l_i   (natural log)
+ *   O_i   = sum_j P_ij v_j
+ *
+ * The pages name the backward only as recomputation from saved softmax
+ * statistics (michaelc-yu summary, "Backward / recomputation"); the gradient
+ * itself is the chain rule through the definition above, with the softmax
+ * Jacobian dP_ij/dS_ik = P_ij (delta_jk - P_ik):
+ *
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   D_i   = sum_j P_ij dP_ij            (also returned: dO_i . O_i, equal in exact arithmetic)
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i
+ *
+ * Masked pairs (causal, j > i) have P_ij = 0 exactly and contribute nothing.
+ * All tensors are contiguous [B,H,N,d] (lse and D: [B,H,N]) fp64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+
+static double dot(const double* a, const double* b, int d)
+{
+    double s = 0.0;
+    for (int c = 0; c < d; ++c) s += a[c] * b[c];
+    return s;
+}
+
+/* Number of keys query row i may attend to. */
+static int keys_allowed(int N, int causal, int i) { return causal ? i + 1 : N; }
+
+/*
+ * One query row of the forward: fills p[0..N) with the probabilities P_i.
+ * (zero where masked), o_i[0..d) with O_i and *lse_i with lse_i.
+ * Q, K, V point at one head ([N,d] each).
+ */
+static void forward_row(const double* Q, const double* K, const double* V, int N, int d,
+                        double scale, int causal, int i, double* p, double* o_i, double* lse_i)
+{
+    const int nk = keys_allowed(N, causal, i);
+    double m = -INFINITY;
+    for (int j = 0; j < nk; ++j) {
+        p[j] = scale * dot(Q + (size_t)i * d, K + (size_t)j * d, d);
+        if (p[j] > m) m = p[j];
+    }
+    double l = 0.0;
+    for (int j = 0; j < nk; ++j) {
+        p[j] = exp(p[j] - m);
+        l += p[j];
+    }
+    for (int j = 0; j < nk; ++j) p[j] /= l;
+    for (int j = nk; j < N; ++j) p[j] = 0.0;
+    for (int c = 0; c < d; ++c) o_i[c] = 0.0;
+    for (int j = 0; j < nk; ++j)
+        for (int c = 0; c < d; ++c) o_i[c] += p[j] * V[(size_t)j * d + c];
+    *lse_i = m + log(l);
+}
+
+/* Forward for every row of every head. */
+void oracle_fwd(const double* q, const double* k, const double* v, int B, int H, int N, int d,
+                double scale, int causal, double* o, double* lse)
+{
+    const int64_t rows = (int64_t)B * H * N;
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < rows; ++r) {
+            const int64_t bh = r / N;
+            const int i = (int)(r % N);
+            const size_t head = (size_t)bh * N * d;
+            forward_row(q + head, k + head, v + head, N, d, scale, causal, i, p,
+                        o + (size_t)r * d, lse + r);
+        }
+        free(p);
+    }
+}
+
+/*
+ * Forward for a list of rows only. rows[t] is the flat row index (b*H + h)*N + i;
+ * o_rows is [nrows, d] and lse_rows [nrows].
+ */
+void oracle_fwd_rows(const double* q, const double* k, const double* v, int B, int H, int N, int d,
+                     double scale, int causal, int64_t nrows, const int64_t* rows,
+                     double* o_rows, double* lse_rows)
+{
+    (void)B; (void)H;
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < nrows; ++t) {
+            const int64_t bh = rows[t] / N;
+            const int i = (int)(rows[t] % N);
+            const size_t head = (size_t)bh * N * d;
+            forward_row(q + head, k + head, v + head, N, d, scale, causal, i, p,
+                        o_rows + (size_t)t * d, lse_rows + t);
+        }
+        free(p);
+    }
+}
+
+/*
+ * Forward and backward for every head.
+ * Outputs: o, lse (as oracle_fwd), dq, dk, dv ([B,H,N,d]), D_pdp (sum_j P_ij dP_ij)
+ * and D_odo (dO_i . O_i), both [B,H,N].
+ *
+ * Pass 1 runs over query rows: P_i, O_i, lse_i, dP_i, D_i, dS_i and dQ_i.
+ * Pass 2 runs over key columns: with lse_i and D_i of every row known, it forms
+ * column j of P, dP and dS (P_ij = exp(S_ij - lse_i), the same value as pass 1's
+ * exp(S_ij - m_i) / l_i) and sums dV_j and dK_j.
+ */
+void oracle_bwd(const double* q, const double* k, const double* v, const double* dout,
+                int B, int H, int N, int d, double scale, int causal,
+                double* o, double* lse, double* dq, double* dk, double* dv,
+                double* D_pdp, double* D_odo)
+{
+    const int64_t rows = (int64_t)B * H * N;
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)N);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < rows; ++r) {
+            const int64_t bh = r / N;
+            const int i = (int)(r % N);
+            const size_t head = (size_t)bh * N * d;
+            const double *Q = q + head, *K = k + head, *V = v + head, *dO = dout + head;
+            const int nk = keys_allowed(N, causal, i);
+            forward_row(Q, K, V, N, d, scale, causal, i, p, o + (size_t)r * d, lse + r);
+            double Dp = 0.0;
+            for (int j = 0; j < nk; ++j) {
+                dp[j] = dot(dO + (size_t)i * d, V + (size_t)j * d, d);
+                Dp += p[j] * dp[j];
+            }
+            D_pdp[r] = Dp;
+            D_odo[r] = dot(dO + (size_t)i * d, o + (size_t)r * d, d);
+            double* dq_i = dq + (size_t)r * d;
+            for (int c = 0; c < d; ++c) dq_i[c] = 0.0;
+            for (int j = 0; j < nk; ++j) {
+                const double ds = p[j] * (dp[j] - Dp);
+                for (int c = 0; c < d; ++c) dq_i[c] += ds * K[(size_t)j * d + c];
+            }
+            for (int c = 0; c < d; ++c) dq_i[c] *= scale;
+        }
+        free(p);
+        free(dp);
+    }
+    /* pass 2: one key column at a time */
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t bh = r / N;
+        const int j = (int)(r % N);
+        const size_t head = (size_t)bh * N * d;
+        const double *Q = q + head, *K = k + head, *V = v + head, *dO = dout + head;
+        const double* lse_h = lse + (size_t)bh * N;
+        const double* D_h = D_pdp + (size_t)bh * N;
+        double* dk_j = dk + (size_t)r * d;
+        double* dv_j = dv + (size_t)r * d;
+        for (int c = 0; c < d; ++c) { dk_j[c] = 0.0; dv_j[c] = 0.0; }
+        const int i0 = causal ? j : 0;   /* queries that may attend to key j */
+        for (int i = i0; i < N; ++i) {
+            const double pij = exp(scale * dot(Q + (size_t)i * d, K + (size_t)j * d, d) - lse_h[i]);
+            const double dpij = dot(dO + (size_t)i * d, V + (size_t)j * d, d);
+            const double ds = pij * (dpij - D_h[i]);
+            for (int c = 0; c < d; ++c) {
+                dv_j[c] += pij * dO[(size_t)i * d + c];
+                dk_j[c] += ds * Q[(size_t)i * d + c];
+            }
+        }
+        for (int c = 0; c < d; ++c) dk_j[c] *= scale;
+    }
+}

@@ -1,0 +1,62 @@
+"""Planted mistakes: each mutant is a copy of the oracle's C source with one
+plausible error (a dropped term, a wrong sign, a wrong index or operand, an
+off-by-one in the causal mask). The pin suite must fail on every one of them,
+which shows that the pins constrain every part of the oracle.
+
+Runs on the CPU only; the mutants are built in a temporary directory.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+# (name, original text, replacement) -- every original must occur exactly once
+MUTANTS = [
+    ("fwd_scale_dropped", "p[j] = scale * dot(Q + (size_t)i * d, K + (size_t)j * d, d);",
+     "p[j] = dot(Q + (size_t)i * d, K + (size_t)j * d, d);"),
+    ("causal_ignored", "return causal ? i + 1 : N;", "return N;"),
+    ("causal_off_by_one", "return causal ? i + 1 : N;", "return causal ? (i + 2 < N ? i + 2 : N) : N;"),
+    ("lse_max_dropped", "*lse_i = m + log(l);", "*lse_i = log(l);"),
+    ("normalisation_dropped", "for (int j = 0; j < nk; ++j) p[j] /= l;", ""),
+    ("o_uses_k", "o_i[c] += p[j] * V[(size_t)j * d + c];", "o_i[c] += p[j] * K[(size_t)j * d + c];"),
+    ("score_transposed_pass2",
+     "exp(scale * dot(Q + (size_t)i * d, K + (size_t)j * d, d) - lse_h[i]);",
+     "exp(scale * dot(Q + (size_t)j * d, K + (size_t)i * d, d) - lse_h[i]);"),
+    ("dp_transposed", "dp[j] = dot(dO + (size_t)i * d, V + (size_t)j * d, d);",
+     "dp[j] = dot(dO + (size_t)j * d, V + (size_t)i * d, d);"),
+    ("D_drops_p", "Dp += p[j] * dp[j];", "Dp += dp[j];"),
+    ("dS_sign", "const double ds = p[j] * (dp[j] - Dp);", "const double ds = p[j] * (dp[j] + Dp);"),
+    ("dq_uses_v", "dq_i[c] += ds * K[(size_t)j * d + c];", "dq_i[c] += ds * V[(size_t)j * d + c];"),
+    ("dq_scale_dropped", "for (int c = 0; c < d; ++c) dq_i[c] *= scale;", ""),
+    ("dk_uses_dO", "dk_j[c] += ds * Q[(size_t)i * d + c];", "dk_j[c] += ds * dO[(size_t)i * d + c];"),
+    ("dk_scale_dropped", "for (int c = 0; c < d; ++c) dk_j[c] *= scale;", ""),
+    ("dv_uses_q", "dv_j[c] += pij * dO[(size_t)i * d + c];", "dv_j[c] += pij * Q[(size_t)i * d + c];"),
+    ("column_causal_off_by_one", "const int i0 = causal ? j : 0;", "const int i0 = causal ? j + 1 : 0;"),
+    ("dS_uses_pass1_D_minus", "const double ds = pij * (dpij - D_h[i]);", "const double ds = pij * dpij;"),
+]
+
+
+def test_mutants_are_well_formed():
+    src = open(SRC).read()
+    for name, old, _ in MUTANTS:
+        assert src.count(old) == 1, name
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new, tmp_path):
+    src = open(SRC).read()
+    mutated = tmp_path / "oracle_mutant.c"
+    mutated.write_text(src.replace(old, new, 1))
+    lib = str(tmp_path / "liboracle_mutant.so")
+    oracle.compile_c(str(mutated), lib)
+    env = dict(os.environ, ORACLE_LIB=lib, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"

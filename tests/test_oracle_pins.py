@@ -1,0 +1,295 @@
+"""Pins for the fp64 oracle: each test checks it against something other than
+itself (closed forms, invariants, brute force, an independent library, finite
+differences), so that a dropped term, a wrong sign or index, or a transposed
+operand anywhere in it fails at least one test.
+
+The method's definition (standard attention, same outputs as the naive
+formulation) is stated on "FlashAttention: making attention fast by respecting
+the memory hierarchy" (paragraphs on the cost of attention and on tiling) and
+in the michaelc-yu summary ("What FlashAttention targets"). The backward is
+the chain rule through that definition ("Backward / recomputation" names it
+only).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from seedgen import normal_f64
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def rnd(seed, tid, shape):
+    return normal_f64(seed, tid, int(np.prod(shape))).reshape(shape)
+
+
+def qkv(seed, B, H, N, d):
+    return rnd(seed, 0, (B, H, N, d)), rnd(seed, 1, (B, H, N, d)), rnd(seed, 2, (B, H, N, d))
+
+
+# ---------------------------------------------------------------- probabilities
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one(causal):
+    """With d = N and V = identity, O_i is row i of P exactly (one non-zero term per sum)."""
+    N = 24
+    q, k, _ = qkv(11, 2, 3, N, N)
+    v = np.broadcast_to(np.eye(N), (2, 3, N, N)).copy()
+    P, _ = oracle.fwd(q * 0.7, k, v, 0.5, causal)
+    assert np.all(P >= 0.0)
+    assert np.max(np.abs(P.sum(-1) - 1.0)) <= 1e-12
+    if causal:
+        iu = np.triu_indices(N, 1)
+        assert np.all(P[..., iu[0], iu[1]] == 0.0), "future keys must get exactly zero weight"
+        assert np.all(P[..., np.arange(N), np.arange(N)] > 0.0)
+
+
+def test_probabilities_brute_force():
+    """Each P_ij against a pure-Python softmax of fsum dot products on a tiny head."""
+    N, d, scale = 5, 3, 0.8
+    q, k, _ = qkv(12, 1, 1, N, d)
+    v = np.eye(N).reshape(1, 1, N, N)
+    # widen d to N by zero padding q/k columns so V can be the identity
+    qp = np.zeros((1, 1, N, N)); qp[..., :d] = q
+    kp = np.zeros((1, 1, N, N)); kp[..., :d] = k
+    P, lse = oracle.fwd(qp, kp, v, scale, False)
+    for i in range(N):
+        s = [scale * math.fsum(q[0, 0, i, c] * k[0, 0, j, c] for c in range(d)) for j in range(N)]
+        z = math.fsum(math.exp(x) for x in s)
+        for j in range(N):
+            assert abs(P[0, 0, i, j] - math.exp(s[j]) / z) <= 1e-15
+        assert abs(lse[0, 0, i] - math.log(z)) <= 1e-14
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v_gives_constant_o(causal):
+    q, k, _ = qkv(13, 2, 2, 33, 8)
+    c = rnd(13, 20, (8,))
+    v = np.broadcast_to(c, (2, 2, 33, 8)).copy()
+    o, _ = oracle.fwd(q, k, v, 1 / math.sqrt(8), causal)
+    assert np.max(np.abs(o - c)) <= 1e-14
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_queries_give_uniform_weights(causal):
+    """Q = 0 makes every score zero: O_i is the mean of the visible V rows, lse_i = ln(count)."""
+    B, H, N, d = 1, 2, 17, 6
+    _, k, v = qkv(14, B, H, N, d)
+    q = np.zeros_like(k)
+    o, lse = oracle.fwd(q, k, v, 0.3, causal)
+    for i in range(N):
+        n_vis = i + 1 if causal else N
+        np.testing.assert_allclose(o[:, :, i], v[:, :, :n_vis].mean(axis=2), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[:, :, i], math.log(n_vis), rtol=0, atol=1e-14)
+
+
+def test_single_token():
+    """N = 1: softmax over one key is 1, so O = V and lse = scale * q.k."""
+    q, k, v = qkv(15, 3, 2, 1, 16)
+    o, lse = oracle.fwd(q, k, v, 0.25, False)
+    np.testing.assert_array_equal(o, v)
+    np.testing.assert_allclose(lse, 0.25 * np.einsum("bhnd,bhnd->bhn", q, k), rtol=0, atol=1e-14)
+
+
+def test_hand_worked_two_tokens():
+    """A 2-token, 1-dim head solved by hand.
+
+    q = [ln 3, 0], k = [1, 0], v = [4, 8], scale = 1, dO = [1, 0].
+    Scores: row 0 = [ln 3, 0], row 1 = [0, 0].
+    Non-causal: P_0 = [3/4, 1/4], P_1 = [1/2, 1/2]; O = [5, 6]; lse = [ln 4, ln 2].
+    Causal: P_0 = [1, 0], P_1 = [1/2, 1/2]; O = [4, 6]; lse = [ln 3, ln 2].
+    Backward of L = O_0 (non-causal): dV = P_0 = [3/4, 1/4]; dP_0 = [4, 8];
+    D_0 = 3 + 2 = 5 = dO_0 O_0; dS_0 = P_0 (dP_0 - 5) = [-3/4, 3/4];
+    dQ_0 = -3/4 * 1 + 3/4 * 0 = -3/4; dQ_1 = 0; dK = dS_0 * q_0 = [-3/4 ln 3, 3/4 ln 3].
+    Causal: only key 0 is visible to row 0, so dS_0 = 0 and dQ = dK = 0, dV = [1, 0].
+    """
+    L3 = math.log(3.0)
+    q = np.array([L3, 0.0]).reshape(1, 1, 2, 1)
+    k = np.array([1.0, 0.0]).reshape(1, 1, 2, 1)
+    v = np.array([4.0, 8.0]).reshape(1, 1, 2, 1)
+    do = np.array([1.0, 0.0]).reshape(1, 1, 2, 1)
+    r = oracle.bwd(q, k, v, do, 1.0, False)
+    np.testing.assert_allclose(r["o"].ravel(), [5.0, 6.0], atol=1e-15)
+    np.testing.assert_allclose(r["lse"].ravel(), [math.log(4.0), math.log(2.0)], atol=1e-15)
+    np.testing.assert_allclose(r["dv"].ravel(), [0.75, 0.25], atol=1e-15)
+    np.testing.assert_allclose(r["dq"].ravel(), [-0.75, 0.0], atol=1e-15)
+    np.testing.assert_allclose(r["dk"].ravel(), [-0.75 * L3, 0.75 * L3], atol=1e-15)
+    np.testing.assert_allclose(r["D_pdp"].ravel(), [5.0, 0.0], atol=1e-14)
+    rc = oracle.bwd(q, k, v, do, 1.0, True)
+    np.testing.assert_allclose(rc["o"].ravel(), [4.0, 6.0], atol=1e-15)
+    np.testing.assert_allclose(rc["lse"].ravel(), [L3, math.log(2.0)], atol=1e-15)
+    np.testing.assert_allclose(rc["dv"].ravel(), [1.0, 0.0], atol=1e-15)
+    np.testing.assert_allclose(rc["dq"].ravel(), [0.0, 0.0], atol=1e-15)
+    np.testing.assert_allclose(rc["dk"].ravel(), [0.0, 0.0], atol=1e-15)
+
+
+def test_lse_shift():
+    """Appending a coordinate with q = 1 and k = c/scale adds c to every score:
+    P and O do not change and lse grows by exactly c."""
+    B, H, N, d, scale, c = 1, 2, 19, 5, 0.4, 2.75
+    q, k, v = qkv(16, B, H, N, d)
+    o0, lse0 = oracle.fwd(q, k, v, scale, False)
+    q1 = np.concatenate([q, np.ones((B, H, N, 1))], -1)
+    k1 = np.concatenate([k, np.full((B, H, N, 1), c / scale)], -1)
+    v1 = np.concatenate([v, np.zeros((B, H, N, 1))], -1)
+    o1, lse1 = oracle.fwd(q1, k1, v1, scale, False)
+    np.testing.assert_allclose(o1[..., :d], o0, atol=1e-13)
+    np.testing.assert_allclose(lse1, lse0 + c, atol=1e-13)
+
+
+# ---------------------------------------------------------------- online softmax equals two-pass
+
+def online_softmax_attention(q, k, v, scale, causal, block):
+    """Test-only fp64 online softmax over key blocks of size ``block`` (running max m,
+    running sum l, running output rescaled by exp(m_old - m_new)), the reading of the
+    tiling paragraph and the "running total" analogy on the groundtruth.day page."""
+    B, H, N, d = q.shape
+    o = np.zeros_like(q)
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                m, l, acc = -np.inf, 0.0, np.zeros(d)
+                nk = i + 1 if causal else N
+                for j0 in range(0, nk, block):
+                    j1 = min(nk, j0 + block)
+                    s = scale * (k[b, h, j0:j1] @ q[b, h, i])
+                    m_new = max(m, s.max())
+                    alpha = math.exp(m - m_new) if m != -np.inf else 0.0
+                    p = np.exp(s - m_new)
+                    l = alpha * l + p.sum()
+                    acc = alpha * acc + p @ v[b, h, j0:j1]
+                    m = m_new
+                o[b, h, i] = acc / l
+                lse[b, h, i] = m + math.log(l)
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("block", [1, 7, 64, 200])
+def test_online_softmax_matches_two_pass(causal, block):
+    q, k, v = qkv(17, 1, 2, 70, 8)
+    o_ref, lse_ref = oracle.fwd(q, k, v, 0.35, causal)
+    o, lse = online_softmax_attention(q, k, v, 0.35, causal, block)
+    tol = 1e-14 if block >= 70 else 1e-13
+    assert np.max(np.abs(o - o_ref)) <= tol * max(1.0, np.max(np.abs(o_ref)))
+    assert np.max(np.abs(lse - lse_ref)) <= tol * max(1.0, np.max(np.abs(lse_ref)))
+
+
+# ---------------------------------------------------------------- causal and equivariance
+
+def test_causal_ignores_future():
+    """Changing K_j, V_j for every j > i0 leaves rows i <= i0 bitwise unchanged."""
+    N, i0 = 40, 17
+    q, k, v = qkv(18, 1, 2, N, 8)
+    o0, l0 = oracle.fwd(q, k, v, 0.5, True)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, i0 + 1:] = rnd(18, 30, k2[:, :, i0 + 1:].shape) * 5
+    v2[:, :, i0 + 1:] = rnd(18, 31, v2[:, :, i0 + 1:].shape) * 5
+    o1, l1 = oracle.fwd(q, k2, v2, 0.5, True)
+    np.testing.assert_array_equal(o1[:, :, :i0 + 1], o0[:, :, :i0 + 1])
+    np.testing.assert_array_equal(l1[:, :, :i0 + 1], l0[:, :, :i0 + 1])
+    assert np.max(np.abs(o1[:, :, i0 + 1:] - o0[:, :, i0 + 1:])) > 1e-3
+
+
+def test_permutation_equivariance():
+    """Non-causal: permuting K and V rows together changes nothing; permuting Q rows permutes O."""
+    N = 23
+    q, k, v = qkv(19, 1, 2, N, 6)
+    o0, l0 = oracle.fwd(q, k, v, 0.6, False)
+    perm = np.argsort(rnd(19, 32, (N,)))
+    o1, l1 = oracle.fwd(q, k[:, :, perm], v[:, :, perm], 0.6, False)
+    np.testing.assert_allclose(o1, o0, atol=1e-14)
+    np.testing.assert_allclose(l1, l0, atol=1e-14)
+    o2, l2 = oracle.fwd(q[:, :, perm], k, v, 0.6, False)
+    np.testing.assert_array_equal(o2, o0[:, :, perm])
+    np.testing.assert_array_equal(l2, l0[:, :, perm])
+
+
+def test_fwd_rows_matches_fwd():
+    q, k, v = qkv(20, 2, 3, 31, 8)
+    o, lse = oracle.fwd(q, k, v, 0.5, True)
+    rows = np.array([0, 5, 30, 31, 100, 185])
+    o_r, lse_r = oracle.fwd_rows(q, k, v, 0.5, True, rows)
+    np.testing.assert_array_equal(o_r, o.reshape(-1, 8)[rows])
+    np.testing.assert_array_equal(lse_r, lse.reshape(-1)[rows])
+
+
+# ---------------------------------------------------------------- independent library
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_torch_cpu_fp64(causal):
+    """torch's CPU float64 scaled_dot_product_attention and autograd: an independent implementation."""
+    torch = pytest.importorskip("torch")
+    B, H, N, d, scale = 2, 3, 29, 16, 0.25
+    q, k, v = qkv(21, B, H, N, d)
+    do = rnd(21, 3, (B, H, N, d))
+    r = oracle.bwd(q, k, v, do, scale, causal)
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    to.backward(torch.tensor(do))
+    np.testing.assert_allclose(r["o"], to.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(r["dq"], tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(r["dk"], tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(r["dv"], tv.grad.numpy(), atol=1e-12)
+    s = scale * torch.tensor(q) @ torch.tensor(k).transpose(-1, -2)
+    if causal:
+        s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    np.testing.assert_allclose(r["lse"], torch.logsumexp(s, -1).numpy(), atol=1e-12)
+
+
+# ---------------------------------------------------------------- backward
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_finite_differences(causal):
+    """Central differences of L = sum(dO * O) with step 1e-5 on a tiny problem."""
+    B, H, N, d, scale, h = 1, 2, 7, 4, 0.7, 1e-5
+    q, k, v = qkv(22, B, H, N, d)
+    do = rnd(22, 3, (B, H, N, d))
+    r = oracle.bwd(q, k, v, do, scale, causal)
+
+    def loss(q_, k_, v_):
+        return float(np.sum(do * oracle.fwd(q_, k_, v_, scale, causal)[0]))
+
+    for name, x, g in (("q", q, r["dq"]), ("k", k, r["dk"]), ("v", v, r["dv"])):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        err = np.linalg.norm(fd - g) / np.linalg.norm(g)
+        assert err <= 1e-7, f"d{name}: relative error {err}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    """D_i = sum_j P_ij dP_ij equals dO_i . O_i; sum_j dV_j = sum_i dO_i (rows of P sum to 1);
+    sum_j dK_j = 0 (rows of dS sum to 0)."""
+    q, k, v = qkv(23, 2, 2, 37, 8)
+    do = rnd(23, 3, q.shape)
+    r = oracle.bwd(q, k, v, do, 0.3, causal)
+    np.testing.assert_allclose(r["D_pdp"], r["D_odo"], atol=1e-12)
+    np.testing.assert_allclose(r["dv"].sum(2), do.sum(2), atol=1e-12)
+    np.testing.assert_allclose(r["dk"].sum(2), 0.0, atol=1e-12)
+    o, lse = oracle.fwd(q, k, v, 0.3, causal)
+    np.testing.assert_array_equal(r["o"], o)
+    np.testing.assert_array_equal(r["lse"], lse)
+
+
+def test_backward_causal_first_key_row():
+    """Causal row 0 sees only key 0 (P_00 = 1), so dS_00 = 0 and dQ_0 = 0; the last key is
+    seen only by the last row, so dV_{N-1} = P_{N-1,N-1} dO_{N-1} with 0 < P <= 1."""
+    q, k, v = qkv(24, 1, 2, 9, 4)
+    do = rnd(24, 3, q.shape)
+    r = oracle.bwd(q, k, v, do, 0.5, True)
+    np.testing.assert_allclose(r["dq"][:, :, 0], 0.0, atol=1e-15)
+    ratio = r["dv"][:, :, -1] / do[:, :, -1]
+    np.testing.assert_allclose(ratio, ratio[..., :1] * np.ones_like(ratio), rtol=1e-13)
+    assert np.all((ratio > 0) & (ratio <= 1))
