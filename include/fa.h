@@ -1,0 +1,111 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact IO-aware attention (FlashAttention) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation: for every batch b and head h, with S = scale * Q K^T,
+ *   O = softmax(S) V   (softmax over each row of S; causal keeps key j <= query i)
+ * computed exactly, in tiles that stay on chip, without ever writing the
+ * N x N score matrix to device memory (groundtruth.day, "FlashAttention:
+ * making attention fast by respecting the memory hierarchy": paragraphs on the
+ * cost of attention, on tiling with an online softmax, and on the payoff in
+ * linear memory). The forward saves one softmax statistic per query row, the
+ * natural-log logsumexp lse_i = ln sum_j exp(S_ij), and the backward
+ * recomputes the score and probability tiles on chip from Q, K, V and lse
+ * (michaelc-yu summary of Dao et al., "Backward / recomputation").
+ *
+ * Layout: q, k, v, o, dout, dq, dk, dv are contiguous [B, H, N, d] arrays
+ * (d innermost) of the element type named by `dtype`; lse is a contiguous
+ * [B, H, N] float array. Every pointer is a device pointer, 16-byte aligned.
+ *
+ * Ownership: every buffer belongs to the caller. The library keeps no pointer
+ * after a call returns, allocates no device memory, has no global mutable
+ * state and is reentrant. Outputs must not overlap inputs.
+ *
+ * Execution: a call only enqueues kernels on `stream` (a hipStream_t; NULL is
+ * the default stream) and returns without synchronising. Device faults show
+ * up at the caller's next synchronisation.
+ *
+ * Errors: every argument is checked before any HIP call. The library never
+ * prints, aborts or throws across this boundary; it returns a status code.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v, o, dout, dq, dk, dv. Accumulation is always fp32. */
+typedef enum {
+    FA_BF16 = 0, /* bfloat16; MFMA bf16 path */
+    FA_FP16 = 1, /* IEEE half; MFMA f16 path */
+    FA_FP32 = 2  /* IEEE single; exact fp32 vector path, d = 64 only */
+} fa_dtype;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,  /* null or misaligned pointer, B/H/N < 1, causal not 0/1,
+                                scale not finite and > 0, overlapping buffers, size overflow */
+    FA_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}, unknown dtype, fp32 with d = 128,
+                                unknown dQ strategy */
+    FA_ERR_WORKSPACE = 3,    /* workspace null or smaller than fa_bwd_workspace_size() */
+    FA_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError after launch) */
+} fa_status;
+
+/* How fa_bwd_dq() forms dQ. */
+typedef enum {
+    FA_DQ_DEFAULT = 0,   /* the strategy measured fastest for the shape */
+    FA_DQ_ATOMIC = 1,    /* fp32 atomic adds into a workspace accumulator, then a convert pass */
+    FA_DQ_SEPARATE = 2   /* a second kernel per query block recomputes the tiles and writes dQ */
+} fa_dq_strategy;
+
+/*
+ * Forward pass.
+ *   q, k, v : inputs, [B,H,N,d] of `dtype`.
+ *   o       : output, [B,H,N,d] of `dtype`, O = softmax(scale Q K^T (+ causal mask)) V.
+ *   lse     : output, [B,H,N] float, lse_i = ln sum_j exp(scale q_i.k_j) over visible keys.
+ *   scale   : score multiplier (usually 1/sqrt(d)); must be finite and > 0.
+ *   causal  : 0 = every key visible, 1 = key j visible to query i iff j <= i.
+ *   stream  : hipStream_t to enqueue on.
+ * Any N >= 1 is accepted (a partial last tile is masked). Returns a fa_status.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd() and fa_bwd_dq() need for this shape with any
+ * dQ strategy: D_i = dO_i . O_i ([B,H,N] float) plus the fp32 dQ accumulator
+ * ([B,H,N,d] float), each rounded up to 256 bytes. Returns 0 for invalid shapes.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype);
+
+/*
+ * Backward pass of L = sum(dout * O): writes dq, dk, dv ([B,H,N,d] of `dtype`).
+ *   q, k, v, o, lse : the forward's inputs and outputs (o and lse exactly as fa_fwd wrote them).
+ *   dout            : upstream gradient dL/dO, [B,H,N,d] of `dtype`.
+ *   workspace       : caller-owned device memory of at least fa_bwd_workspace_size() bytes,
+ *                     256-byte aligned; its contents on entry do not matter.
+ * Reads only q, k, v, o, dout and lse; recomputes every score and probability tile.
+ * Uses the default dQ strategy. Returns a fa_status.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa_bwd() with an explicit fa_dq_strategy (ignored for FA_FP32, which has one path). */
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              const float* lse, void* dq, void* dk, void* dv,
+              int B, int H, int N, int d, float scale, int causal, int dtype, int dq_strategy,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a fa_status value. Never NULL. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

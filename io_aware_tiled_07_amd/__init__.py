@@ -1,0 +1,167 @@
+"""Python binding of libfa.so: exact IO-aware attention on MI355X.
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels behind the C ABI (``include/fa.h``). PyTorch provides device memory and
+the current stream. There is no fallback: if ``libfa.so`` is missing or a call
+fails, an exception is raised.
+
+The raw entry points keep the C names (``fa_fwd``, ``fa_bwd``, ``fa_bwd_dq``,
+``fa_bwd_workspace_size``, ``fa_status_string``) and take caller-allocated
+torch tensors; ``fwd`` and ``bwd`` allocate their outputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FA_BF16", "FA_FP16", "FA_FP32", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED",
+    "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_DQ_DEFAULT", "FA_DQ_ATOMIC", "FA_DQ_SEPARATE",
+    "FaError", "library_path", "load", "fa_status_string", "fa_bwd_workspace_size",
+    "fa_fwd", "fa_bwd", "fa_bwd_dq", "fwd", "bwd", "dtype_code",
+]
+
+FA_BF16, FA_FP16, FA_FP32 = 0, 1, 2
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
+FA_DQ_DEFAULT, FA_DQ_ATOMIC, FA_DQ_SEPARATE = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfa.so")
+_lib = None
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+class FaError(RuntimeError):
+    """A non-zero fa_status from libfa.so."""
+
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {fa_status_string(status)} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libfa.so (built by ``io_aware_tiled_07_amd.build``); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.fa_status_string.argtypes = [_i]
+        lib.fa_status_string.restype = ctypes.c_char_p
+        lib.fa_bwd_workspace_size.argtypes = [_i, _i, _i, _i, _i]
+        lib.fa_bwd_workspace_size.restype = _sz
+        lib.fa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _vp]
+        lib.fa_fwd.restype = _i
+        lib.fa_bwd.argtypes = [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]
+        lib.fa_bwd.restype = _i
+        lib.fa_bwd_dq.argtypes = [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _i, _i, _vp, _sz, _vp]
+        lib.fa_bwd_dq.restype = _i
+        _lib = lib
+    return _lib
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, d: int, dtype: int) -> int:
+    return int(load().fa_bwd_workspace_size(B, H, N, d, dtype))
+
+
+def dtype_code(t) -> int:
+    import torch
+    codes = {torch.bfloat16: FA_BF16, torch.float16: FA_FP16, torch.float32: FA_FP32}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _check_bhnd(name, t, shape=None, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fa_fwd(q, k, v, o, lse, causal: bool = False, scale=None, stream=None) -> None:
+    """Enqueue the forward into caller-allocated ``o`` ([B,H,N,d]) and ``lse`` ([B,H,N] float32)."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,N,d]")
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_bhnd(name, t, q.shape, q.dtype)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    st = load().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       B, H, N, d, _scale(scale, d), int(bool(causal)), dtype_code(q), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd")
+
+
+def fa_bwd_dq(q, k, v, o, do, lse, dq, dk, dv, causal: bool = False, scale=None,
+              dq_strategy: int = FA_DQ_DEFAULT, workspace=None, stream=None) -> None:
+    """Enqueue the backward into caller-allocated ``dq``, ``dk``, ``dv``. ``workspace`` is a
+    device tensor of at least ``fa_bwd_workspace_size`` bytes (allocated here if None)."""
+    import torch
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_bhnd(name, t, q.shape, q.dtype)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    code = dtype_code(q)
+    need = fa_bwd_workspace_size(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_bhnd("workspace", workspace)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load().fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                          _scale(scale, d), int(bool(causal)), code, int(dq_strategy),
+                          workspace.data_ptr(), nbytes, _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dq")
+
+
+def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, causal: bool = False, scale=None, workspace=None,
+           stream=None) -> None:
+    """``fa_bwd_dq`` with the default dQ strategy."""
+    fa_bwd_dq(q, k, v, o, do, lse, dq, dk, dv, causal, scale, FA_DQ_DEFAULT, workspace, stream)
+
+
+def fwd(q, k, v, causal: bool = False, scale=None, stream=None):
+    """Allocate O and lse and run the forward. Returns (o, lse)."""
+    import torch
+    B, H, N, _ = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, causal, scale, stream)
+    return o, lse
+
+
+def bwd(q, k, v, o, do, lse, causal: bool = False, scale=None, dq_strategy: int = FA_DQ_DEFAULT,
+        workspace=None, stream=None):
+    """Allocate dQ, dK, dV and run the backward. Returns (dq, dk, dv)."""
+    import torch
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd_dq(q, k, v, o, do, lse, dq, dk, dv, causal, scale, dq_strategy, workspace, stream)
+    return dq, dk, dv

@@ -1,0 +1,152 @@
+// C ABI of libfa.so (declared in include/fa.h): argument validation, dispatch
+// over (dtype, head dim, causal, dQ strategy) and workspace layout. Every check
+// runs before the first HIP call, so each error path can be exercised on a
+// host without a GPU.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 27;
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;
+};
+Range range(const void* p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int elt_bytes(int dtype) { return dtype == FA_FP32 ? 4 : 2; }
+
+// Shape, dtype, head-dim and scalar checks shared by the forward and backward.
+int check_common(int B, int H, int N, int d, float scale, int causal, int dtype, bool backward) {
+    if (dtype != FA_BF16 && dtype != FA_FP16 && dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (dtype == FA_FP32) {
+        if (d != 64) return FA_ERR_UNSUPPORTED;
+    } else if (backward) {
+        if (d != 64) return FA_ERR_UNSUPPORTED;
+    } else if (d != 64 && d != 128) {
+        return FA_ERR_UNSUPPORTED;
+    }
+    const int64_t bh = (int64_t)B * H;
+    if ((int64_t)N > kMaxN || bh > kMaxGrid || bh * ((N + 31) / 32) > kMaxGrid) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported dtype / head dim / strategy";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+        case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
+        default: return "unknown fa_status";
+    }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, int dtype, void* stream) {
+    int st = check_common(B, H, N, d, scale, causal, dtype, /*backward=*/false);
+    if (st != FA_OK) return st;
+    const void* ptrs[] = {q, k, v, o, lse};
+    for (const void* p : ptrs)
+        if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
+    const size_t tbytes = (size_t)B * H * N * d * elt_bytes(dtype);
+    const size_t lbytes = (size_t)B * H * N * sizeof(float);
+    const Range ro = range(o, tbytes), rl = range(lse, lbytes);
+    const Range ins[] = {range(q, tbytes), range(k, tbytes), range(v, tbytes)};
+    for (const Range& r : ins)
+        if (overlap(ro, r) || overlap(rl, r)) return FA_ERR_INVALID_ARG;
+    if (overlap(ro, rl)) return FA_ERR_INVALID_ARG;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();  // clear a stale error so the check below sees only this launch
+    hipError_t e;
+    if (dtype == FA_FP32)
+        e = fa::fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+                        static_cast<float*>(o), lse, B, H, N, scale, causal != 0, s);
+    else
+        e = fa::fwd_mfma(q, k, v, o, lse, B, H, N, d, scale, causal != 0, dtype, s);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
+    if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+    if (dtype != FA_BF16 && dtype != FA_FP16 && dtype != FA_FP32) return 0;
+    const size_t rows = (size_t)B * H * N;
+    size_t bytes = round_up(rows * sizeof(float), 256);
+    if (dtype != FA_FP32) bytes += round_up(rows * (size_t)d * sizeof(float), 256);
+    return bytes;
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+              void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+              int dq_strategy, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_common(B, H, N, d, scale, causal, dtype, /*backward=*/true);
+    if (st != FA_OK) return st;
+    if (dq_strategy != FA_DQ_DEFAULT && dq_strategy != FA_DQ_ATOMIC && dq_strategy != FA_DQ_SEPARATE)
+        return FA_ERR_UNSUPPORTED;
+    const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+    for (const void* p : ptrs)
+        if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
+    const size_t need = fa_bwd_workspace_size(B, H, N, d, dtype);
+    if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+
+    const size_t tbytes = (size_t)B * H * N * d * elt_bytes(dtype);
+    const size_t lbytes = (size_t)B * H * N * sizeof(float);
+    const Range outs[] = {range(dq, tbytes), range(dk, tbytes), range(dv, tbytes), range(workspace, need)};
+    const Range ins[] = {range(q, tbytes), range(k, tbytes), range(v, tbytes), range(o, tbytes),
+                         range(dout, tbytes), range(lse, lbytes)};
+    for (int i = 0; i < 4; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return FA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t rows = (size_t)B * H * N;
+    float* delta = static_cast<float*>(workspace);
+    float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(rows * sizeof(float), 256));
+    (void)hipGetLastError();
+    hipError_t e;
+    if (dtype == FA_FP32) {
+        e = fa::bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+                        static_cast<const float*>(o), static_cast<const float*>(dout), lse, static_cast<float*>(dq),
+                        static_cast<float*>(dk), static_cast<float*>(dv), B, H, N, scale, causal != 0, delta, s);
+    } else {
+        // Default strategy: fp32 atomics into the workspace accumulator.
+        const int mode = dq_strategy == FA_DQ_SEPARATE ? 2 : 1;
+        e = fa::bwd_mfma(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, dtype, mode, delta,
+                         dq_acc, s);
+    }
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream) {
+    return fa_bwd_dq(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, FA_DQ_DEFAULT,
+                     workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+// Device-side building blocks shared by the attention kernels for gfx950:
+// vector types, element traits (bf16 / fp16 MFMA and rounding), the swizzled
+// LDS tile addressing and the cross-lane helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Finite floor for the running row maximum: a row whose visible scores are all
+// masked so far keeps m = kMaskFloor, so exp2(m_old - m_new) is 1 and every
+// exp2(-inf - m) is 0, never NaN.
+constexpr float kMaskFloor = -1.0e30f;
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& x) {
+    static_assert(sizeof(To) == sizeof(From), "size mismatch");
+    return __builtin_bit_cast(To, x);
+}
+
+// ---------------------------------------------------------------- element traits
+// 16-bit element types: the 32x32x16 MFMA with fp32 accumulation, and
+// round-to-nearest-even conversion of fp32 pairs into a packed 32-bit word
+// (low half = first element).
+struct Bf16 {
+    static constexpr int kDtype = 0;
+    __device__ __forceinline__ static f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(a), bitcast<bf16x8>(b), c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(a), bitcast<bf16x8>(b), c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static uint32_t pack2(float lo, float hi) {
+        f32x2 v = {lo, hi};
+        return bitcast<uint32_t>(__builtin_convertvector(v, bf16x2));
+    }
+    __device__ __forceinline__ static float to_f32(uint16_t x) {
+        return __uint_as_float(((uint32_t)x) << 16);
+    }
+};
+
+struct F16 {
+    static constexpr int kDtype = 1;
+    __device__ __forceinline__ static f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<f16x8>(a), bitcast<f16x8>(b), c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8>(a), bitcast<f16x8>(b), c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static uint32_t pack2(float lo, float hi) {
+        f32x2 v = {lo, hi};
+        return bitcast<uint32_t>(__builtin_convertvector(v, f16x2));
+    }
+    __device__ __forceinline__ static float to_f32(uint16_t x) {
+        return (float)bitcast<_Float16>(x);
+    }
+};
+
+// ---------------------------------------------------------------- LDS tiles
+// A tile of R rows x D 16-bit elements lives in LDS as R rows of D/8 16-byte
+// chunks. Chunk c of row r is stored at chunk position c ^ f(r) of that row.
+// f is chosen so that (a) the 16 rows an MFMA operand read touches with one
+// chunk column, and (b) the 4 rows x 2 adjacent chunks a transposed 64-bit
+// read touches, fall on distinct LDS banks.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+    static_assert(D == 64 || D == 128, "head dim");
+    if constexpr (D == 64) {
+        const int f = (row & 6) | ((row >> 3) & 1);
+        return row * 128 + ((chunk ^ f) << 4);
+    } else {
+        const int f = ((row & 3) << 2) | ((row >> 2) & 3);
+        return row * 256 + ((chunk ^ f) << 4);
+    }
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const char* base, int off) {
+    return *reinterpret_cast<const u32x4*>(base + off);
+}
+__device__ __forceinline__ void lds_write16(char* base, int off, const u32x4& v) {
+    *reinterpret_cast<u32x4*>(base + off) = v;
+}
+
+// Transposed 64-bit LDS read (gfx950 ds_read_b64_tr_b16). Within each group
+// of 16 lanes, lane L receives element (L % 4) of the 8-byte pieces addressed
+// by lanes L/4, L/4 + 4, L/4 + 8 and L/4 + 12 of its group, in that order.
+// If lane c of a group addresses row k0 + c/4, columns n0 + 4(c%4) .. +3 of a
+// row-major 16-bit matrix, lane L receives column n0 + L of rows k0 .. k0+3.
+__device__ __forceinline__ u32x2 lds_read_tr(const char* base, int off) {
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off));
+    return bitcast<u32x2>(r);
+}
+
+// ---------------------------------------------------------------- cross-lane
+// v_permlane32_swap exchanges the upper 32 lanes of its first operand with the
+// lower 32 lanes of its second. Called with the same value twice, each lane
+// ends up holding its own value and that of lane (l ^ 32), one in each result
+// register, so a symmetric combination of the two gives the pair result.
+__device__ __forceinline__ float pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+}
+
+// Row swap inside a 32-row MFMA block: exchanges bits 2 and 3 of the row index.
+// Loading operand row m from source row perm32(m) makes accumulator register i
+// of lane half h hold source row 16*(i/8) + 8*h + (i%8), which is exactly the
+// k-index order the next MFMA wants for its B operand.
+__device__ __forceinline__ int perm32(int m) {
+    return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+}  // namespace fa

@@ -1,0 +1,29 @@
+// Host-side entry points of the kernel files, called by the C ABI layer
+// (fa_api.cpp) after it has validated every argument. Each returns the
+// hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+// 16-bit forward (dtype 0 = bf16, 1 = fp16), d in {64, 128}.
+hipError_t fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                    int N, int d, float scale, bool causal, int dtype, hipStream_t stream);
+
+// 16-bit backward. dq_mode: 1 = fp32 atomics into dq_acc then convert, 2 = separate dQ kernel.
+// delta: [B,H,N] float scratch, dq_acc: [B,H,N,d] float scratch (atomic mode only).
+hipError_t bwd_mfma(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                    float scale, bool causal, int dtype, int dq_mode, float* delta, float* dq_acc,
+                    hipStream_t stream);
+
+// fp32 forward and backward, d = 64.
+hipError_t fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+                   int N, float scale, bool causal, hipStream_t stream);
+hipError_t bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* dout,
+                   const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, float scale,
+                   bool causal, float* delta, hipStream_t stream);
+
+}  // namespace fa

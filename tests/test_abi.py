@@ -1,0 +1,132 @@
+"""libfa.so on the host: it loads, exports every function include/fa.h declares,
+and rejects every invalid argument before touching the GPU (so these calls run
+without one). No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import io_aware_tiled_07_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+A = 0x100000  # fake, 16-byte aligned device addresses: never dereferenced on these paths
+GAP = 1 << 30
+
+
+def ptrs(n):
+    return [A + i * GAP for i in range(n)]
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.library_path()):
+        pytest.skip("libfa.so not built")
+    return fa.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_workspace_size", "fa_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert fa.fa_status_string(code)
+    assert "unknown" in fa.fa_status_string(99)
+
+
+def test_workspace_size(lib):
+    def up(x):
+        return (x + 255) // 256 * 256
+    assert fa.fa_bwd_workspace_size(8, 12, 1024, 64, fa.FA_BF16) == up(8 * 12 * 1024 * 4) + up(8 * 12 * 1024 * 64 * 4)
+    assert fa.fa_bwd_workspace_size(1, 1, 7, 64, fa.FA_FP32) == up(7 * 4)
+    assert fa.fa_bwd_workspace_size(0, 1, 7, 64, fa.FA_BF16) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 7, 64, 9) == 0
+
+
+def fwd(lib, q=None, k=None, v=None, o=None, lse=None, B=2, H=3, N=100, d=64, scale=0.125, causal=0, dtype=0):
+    p = ptrs(5)
+    args = [p[0] if q is None else q, p[1] if k is None else k, p[2] if v is None else v,
+            p[3] if o is None else o, p[4] if lse is None else lse]
+    return lib.fa_fwd(*[ctypes.c_void_p(x) for x in args], B, H, N, d, ctypes.c_float(scale), causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(v=A + 8), fa.FA_ERR_INVALID_ARG),          # misaligned
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-0.5), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=2, d=128), fa.FA_ERR_UNSUPPORTED),    # fp32 path is d = 64 only
+    (dict(o=A), fa.FA_ERR_INVALID_ARG),               # o aliases q
+    (dict(lse=A + GAP + 64), fa.FA_ERR_INVALID_ARG),  # lse inside k
+    (dict(N=(1 << 27) + 1), fa.FA_ERR_INVALID_ARG),
+])
+def test_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def bwd(lib, B=2, H=3, N=100, d=64, scale=0.125, causal=0, dtype=0, strategy=0, ws=None, ws_bytes=None, **over):
+    names = ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"]
+    p = dict(zip(names, ptrs(9)))
+    p.update({k: v for k, v in over.items() if k in names})
+    need = fa.fa_bwd_workspace_size(B, H, N, d, dtype) if dtype in (0, 1, 2) else 0
+    ws = A + 9 * GAP if ws is None else ws
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return lib.fa_bwd_dq(*[ctypes.c_void_p(p[n]) for n in names], B, H, N, d, ctypes.c_float(scale), causal,
+                         dtype, strategy, ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(do=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=A + 4 * GAP + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(d=128), fa.FA_ERR_UNSUPPORTED),            # 16-bit backward is d = 64
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(strategy=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=0), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 9 * GAP + 4), fa.FA_ERR_WORKSPACE),  # misaligned workspace
+    (dict(dq=A + 2 * GAP), fa.FA_ERR_INVALID_ARG),    # dq aliases v
+    (dict(dv=A + 6 * GAP), fa.FA_ERR_INVALID_ARG),    # dv aliases dq
+    (dict(ws=A + 5 * GAP), fa.FA_ERR_INVALID_ARG),    # workspace overlaps lse
+    (dict(causal=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+])
+def test_bwd_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_fa_bwd_is_default_strategy(lib):
+    p = [ctypes.c_void_p(x) for x in ptrs(9)]
+    st = lib.fa_bwd(*p, 2, 3, 100, 96, ctypes.c_float(0.125), 0, 0, ctypes.c_void_p(A + 9 * GAP),
+                    ctypes.c_size_t(1 << 20), None)
+    assert st == fa.FA_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import importlib
+    monkeypatch.setattr(fa, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(fa, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        fa.load()
+    importlib.reload(fa)

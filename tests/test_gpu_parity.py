@@ -1,0 +1,233 @@
+"""GPU parity: libfa.so (through the C ABI) against the fp64 oracle on the
+same seeded inputs, on every workload shape, plus edge cases, determinism,
+GPU-side invariants and the O(N) memory claim.
+
+Workloads (B, H, N, d; dtype; causal): tiny 1,1,128,64 fp32 both; BERT-large
+shaped 8,16,512,64 bf16 non-causal; GPT-2-small shaped 8,12,1024,64 bf16
+causal (the benchmarked one); long causal 1,16,{4096,8192,16384},64 bf16;
+64K wide-head 1,8,65536,128 bf16 x0.5 non-causal (forward only).
+"""
+import numpy as np
+import pytest
+
+import io_aware_tiled_07_amd as fa
+import oracle
+import seedgen
+from _parity import check, inputs, log, scale_for, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load()
+    yield
+
+
+def run_fwd_bwd(seed, shape, dtype, causal, strategy=fa.FA_DQ_DEFAULT, mul=1.0):
+    drawn = inputs(seed, shape, dtype, mul)
+    q, k, v, do = to_dev(drawn)
+    sc = scale_for(shape[-1])
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=sc)
+    dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=causal, scale=sc, dq_strategy=strategy)
+    torch.cuda.synchronize()
+    return drawn, (o, lse, dq, dk, dv)
+
+
+def check_all(drawn, outs, dtype, causal, heads=None):
+    qd, kd, vd, dod = (d.f64 for d in drawn)
+    B, H, N, d = qd.shape
+    o, lse, dq, dk, dv = outs
+    if heads is not None:  # oracle on a subset of (b, h) heads only
+        sel = [(b, h) for b, h in heads]
+        pick = lambda a: np.stack([a[b, h] for b, h in sel])[None]
+        qd, kd, vd, dod = pick(qd), pick(kd), pick(vd), pick(dod)
+        gpick = lambda t: torch.stack([t[b, h] for b, h in sel])[None]
+        o, lse, dq, dk, dv = (gpick(t) for t in (o, lse, dq, dk, dv))
+    r = oracle.bwd(qd, kd, vd, dod, scale_for(d), causal)
+    for name, g, ref in (("o", o, r["o"]), ("lse", lse, r["lse"]), ("dq", dq, r["dq"]),
+                         ("dk", dk, r["dk"]), ("dv", dv, r["dv"])):
+        check(name, g, ref, dtype)
+
+
+# ---------------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_fp32(causal):
+    log(f"tiny fp32 causal={causal}")
+    drawn, outs = run_fwd_bwd(1001, (1, 1, 128, 64), "fp32", causal)
+    check_all(drawn, outs, "fp32", causal)
+
+
+@pytest.mark.parametrize("strategy", [fa.FA_DQ_ATOMIC, fa.FA_DQ_SEPARATE])
+def test_bert_large_shape(strategy):
+    log(f"BERT-large shape bf16 non-causal strategy={strategy}")
+    drawn, outs = run_fwd_bwd(1002, (8, 16, 512, 64), "bf16", False, strategy)
+    check_all(drawn, outs, "bf16", False)
+
+
+@pytest.mark.parametrize("strategy", [fa.FA_DQ_ATOMIC, fa.FA_DQ_SEPARATE])
+def test_gpt2_shape_causal(strategy):
+    log(f"GPT-2 shape bf16 causal strategy={strategy}")
+    drawn, outs = run_fwd_bwd(1003, (8, 12, 1024, 64), "bf16", True, strategy)
+    check_all(drawn, outs, "bf16", True)
+
+
+@pytest.mark.parametrize("shape,causal", [((8, 16, 512, 64), False), ((8, 12, 1024, 64), True)])
+def test_fp16_shapes(shape, causal):
+    log(f"fp16 {shape} causal={causal}")
+    drawn, outs = run_fwd_bwd(1002 if not causal else 1003, shape, "fp16", causal)
+    check_all(drawn, outs, "fp16", causal)
+
+
+@pytest.mark.parametrize("N", [4096, 8192, 16384])
+def test_long_causal(N):
+    """Full GPU run; the oracle checks one seeded head completely (fwd and bwd)
+    and 32 seeded forward rows of every head."""
+    log(f"long causal N={N}")
+    shape = (1, 16, N, 64)
+    drawn, outs = run_fwd_bwd(1004, shape, "bf16", True)
+    h = int(seedgen.choice_rows(1004, 17 + N, 16, 1)[0])
+    check_all(drawn, outs, "bf16", True, heads=[(0, h)])
+    rows = np.concatenate([hh * N + seedgen.choice_rows(1004, 40 + hh, N, 32) for hh in range(16)])
+    o_ref, lse_ref = oracle.fwd_rows(drawn[0].f64, drawn[1].f64, drawn[2].f64, scale_for(64), True, rows)
+    check("o_rows", outs[0].reshape(-1, 64)[torch.from_numpy(rows).cuda()], o_ref, "bf16")
+    check("lse_rows", outs[1].reshape(-1)[torch.from_numpy(rows).cuda()], lse_ref, "bf16")
+
+
+def test_wide_64k_forward():
+    """64K tokens, d = 128, forward only: 256 seeded rows (32 per head) against the oracle."""
+    log("64K wide forward")
+    B, H, N, d = 1, 8, 65536, 128
+    drawn = inputs(1005, (B, H, N, d), "bf16", mul=0.5, with_do=False)
+    q, k, v = to_dev(drawn)
+    o, lse = fa.fwd(q, k, v, causal=False, scale=scale_for(d))
+    torch.cuda.synchronize()
+    rows = np.concatenate([hh * N + seedgen.choice_rows(1005, 16 + hh, N, 32) for hh in range(H)])
+    o_ref, lse_ref = oracle.fwd_rows(drawn[0].f64, drawn[1].f64, drawn[2].f64, scale_for(d), False, rows)
+    idx = torch.from_numpy(rows).cuda()
+    check("o_rows", o.reshape(-1, d)[idx], o_ref, "bf16")
+    check("lse_rows", lse.reshape(-1)[idx], lse_ref, "bf16")
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_wide_64k_constant_v():
+    """Constant V makes every output row equal that constant, whatever the weights."""
+    B, H, N, d = 1, 8, 65536, 128
+    drawn = inputs(1005, (B, H, N, d), "bf16", mul=0.5, with_do=False)
+    q, k, _ = to_dev(drawn)
+    c = torch.linspace(-2, 2, d, dtype=torch.float32).to(torch.bfloat16)
+    v = c.cuda().expand(B, H, N, d).contiguous()
+    o, _ = fa.fwd(q, k, v, causal=False, scale=scale_for(d))
+    err = (o.float() - c.cuda().float()).abs().max().item()
+    log(f"  constant V: max|O - c| = {err:.3e}")
+    assert err <= 2e-2
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("N", [1, 7, 129, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_forward(N, causal, d):
+    log(f"ragged fwd N={N} causal={causal} d={d}")
+    drawn = inputs(2000 + N, (1, 3, N, d), "bf16", with_do=False)
+    q, k, v = to_dev(drawn)
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale_for(d))
+    o_ref, lse_ref = oracle.fwd(drawn[0].f64, drawn[1].f64, drawn[2].f64, scale_for(d), causal)
+    check("o", o, o_ref, "bf16")
+    check("lse", lse, lse_ref, "bf16")
+
+
+@pytest.mark.parametrize("N", [1, 7, 129, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("strategy", [fa.FA_DQ_ATOMIC, fa.FA_DQ_SEPARATE])
+def test_ragged_backward(N, causal, strategy):
+    log(f"ragged bwd N={N} causal={causal} strategy={strategy}")
+    drawn, outs = run_fwd_bwd(3000 + N, (2, 2, N, 64), "bf16", causal, strategy)
+    check_all(drawn, outs, "bf16", causal)
+
+
+@pytest.mark.parametrize("N", [1, 7, 129])
+def test_ragged_fp32(N):
+    drawn, outs = run_fwd_bwd(4000 + N, (1, 2, N, 64), "fp32", True)
+    check_all(drawn, outs, "fp32", True)
+
+
+def test_custom_scale():
+    drawn = inputs(5000, (2, 2, 200, 64), "bf16", with_do=False)
+    q, k, v = to_dev(drawn)
+    o, lse = fa.fwd(q, k, v, causal=True, scale=0.3)
+    o_ref, lse_ref = oracle.fwd(drawn[0].f64, drawn[1].f64, drawn[2].f64, 0.3, True)
+    check("o", o, o_ref, "bf16")
+    check("lse", lse, lse_ref, "bf16")
+
+
+# ---------------------------------------------------------------- determinism and invariants
+
+def test_forward_is_deterministic():
+    drawn = inputs(1003, (8, 12, 1024, 64), "bf16", with_do=False)
+    q, k, v = to_dev(drawn)
+    o1, l1 = fa.fwd(q, k, v, causal=True)
+    o2, l2 = fa.fwd(q, k, v, causal=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_backward_determinism():
+    """dK, dV (and dQ with the separate pass) repeat bitwise; atomic dQ may differ
+    in the last bits from run to run but stays within tolerance of the oracle."""
+    drawn = inputs(1002, (2, 4, 512, 64), "bf16")
+    q, k, v, do = to_dev(drawn)
+    o, lse = fa.fwd(q, k, v)
+    a = fa.bwd(q, k, v, o, do, lse, dq_strategy=fa.FA_DQ_SEPARATE)
+    b = fa.bwd(q, k, v, o, do, lse, dq_strategy=fa.FA_DQ_SEPARATE)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    c = fa.bwd(q, k, v, o, do, lse, dq_strategy=fa.FA_DQ_ATOMIC)
+    assert torch.equal(a[1], c[1]) and torch.equal(a[2], c[2])
+
+
+def test_backward_invariants():
+    """sum_j dV_j = sum_i dO_i (rows of P sum to 1) and sum_j dK_j = 0 (rows of dS sum to 0)."""
+    drawn, (o, lse, dq, dk, dv) = run_fwd_bwd(1002, (8, 16, 512, 64), "bf16", False)
+    do = drawn[3].torch("cuda").float()
+    sv = dv.float().sum(2)
+    ref = do.sum(2)
+    assert ((sv - ref).norm() / ref.norm()).item() < 1e-2
+    sk = dk.float().sum(2)
+    assert (sk.norm() / dk.float().norm()).item() < 2e-2
+
+
+def test_lse_bounds():
+    """max_j S_ij <= lse_i <= max_j S_ij + ln(visible keys)."""
+    drawn = inputs(1003, (1, 4, 1024, 64), "bf16", with_do=False)
+    q, k, v = to_dev(drawn)
+    _, lse = fa.fwd(q, k, v, causal=True)
+    s = (q.float() @ k.float().transpose(-1, -2).contiguous()) * scale_for(64)
+    s = s.masked_fill(torch.triu(torch.ones(1024, 1024, dtype=torch.bool, device="cuda"), 1), float("-inf"))
+    m = s.max(-1).values
+    n_vis = torch.arange(1, 1025, device="cuda").float()
+    assert (lse >= m - 1e-3).all() and (lse <= m + torch.log(n_vis) + 1e-3).all()
+
+
+def test_peak_memory_grows_linearly():
+    """fwd + bwd peak device memory at N = 4096, 8192, 16384 (1 x 16 heads, d = 64):
+    each doubling of N about doubles it (an N x N score matrix would quadruple it)."""
+    peaks = []
+    for N in (4096, 8192, 16384):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        q, k, v, do = (torch.randn(1, 16, N, 64, device="cuda", dtype=torch.bfloat16) for _ in range(4))
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        o, lse = fa.fwd(q, k, v, causal=True)
+        dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=True)
+        torch.cuda.synchronize()
+        peaks.append(torch.cuda.max_memory_allocated() - base)
+        del q, k, v, do, o, lse, dq, dk, dv
+    ratios = [peaks[i + 1] / peaks[i] for i in range(2)]
+    log(f"  peak bytes {peaks} ratios {ratios}")
+    assert all(1.8 <= r <= 2.2 for r in ratios)
+    assert peaks[-1] < 16 * 16384 * 16384 * 4 / 10  # far below one fp32 score matrix for all heads
