@@ -79,16 +79,37 @@ struct F16 {
 // chunk column, and (b) the 4 rows x 2 adjacent chunks a transposed 64-bit
 // read touches, fall on distinct LDS banks.
 template <int D>
-__device__ __forceinline__ int tile_off(int row, int chunk) {
+__device__ __forceinline__ int swz(int row) {
     static_assert(D == 64 || D == 128, "head dim");
-    if constexpr (D == 64) {
-        const int f = (row & 6) | ((row >> 3) & 1);
-        return row * 128 + ((chunk ^ f) << 4);
-    } else {
-        const int f = ((row & 3) << 2) | ((row >> 2) & 3);
-        return row * 256 + ((chunk ^ f) << 4);
-    }
+    if constexpr (D == 64) return (row & 6) | ((row >> 3) & 1);
+    else return ((row & 3) << 2) | ((row >> 2) & 3);
 }
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+    return row * (2 * D) + ((chunk ^ swz<D>(row)) << 4);
+}
+
+// ---------------------------------------------------------------- async staging
+// global_load_lds_dwordx4: each lane copies 16 bytes from its own global
+// address straight into LDS at lds_base + 16 * lane (lds_base is wave-uniform).
+// Completion is tracked by the wave's vmcnt, not by lgkmcnt.
+__device__ __forceinline__ void dma16(const void* src, char* lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier without the memory fence __syncthreads() adds (that fence
+// waits for every outstanding global load, which would drain the prefetch
+// ring). The asm memory clobber keeps the compiler from moving LDS accesses
+// across it; callers order their own LDS-DMA and LDS writes with the waits above.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ u32x4 lds_read16(const char* base, int off) {
     return *reinterpret_cast<const u32x4*>(base + off);
@@ -105,6 +126,33 @@ __device__ __forceinline__ void lds_write16(char* base, int off, const u32x4& v)
 __device__ __forceinline__ u32x2 lds_read_tr(const char* base, int off) {
     i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off));
     return bitcast<u32x2>(r);
+}
+
+// The same transposed read issued from inline asm. The compiler's wait pass
+// treats the intrinsic above as a possible reader of in-flight LDS-DMA data
+// and puts a vmcnt(0) in front of it, which would drain the prefetch ring; the
+// asm form is invisible to that pass. Its result is NOT covered by the
+// compiler's lgkmcnt bookkeeping: call lds_wait_all() on the registers before
+// they are used. `addr` is an LDS byte address, OFF an immediate byte offset.
+template <int OFF>
+__device__ __forceinline__ u32x2 tr_read(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
+}
+
+// s_waitcnt lgkmcnt(0) that every use of x0 .. x3 must follow.
+__device__ __forceinline__ void lds_wait_all(u32x4& x0, u32x4& x1) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x0), "+v"(x1));
+}
+__device__ __forceinline__ void lds_wait_all(u32x4& x0, u32x4& x1, u32x4& x2, u32x4& x3) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3));
 }
 
 // ---------------------------------------------------------------- cross-lane

@@ -38,10 +38,15 @@ namespace fa {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBr = 32 * kWaves;  // query rows per workgroup
-constexpr int kBc = 64;           // keys per block
+constexpr int kBc = 64;  // keys per block
+
+// Tuning knobs (compile-time): query rows per wave = 32 * QT, waves per workgroup = NW.
+#ifndef FA_FWD_QT
+#define FA_FWD_QT 1
+#endif
+#ifndef FA_FWD_NW
+#define FA_FWD_NW 4
+#endif
 
 struct FwdArgs {
     const uint16_t* q;
@@ -67,16 +72,22 @@ __device__ __forceinline__ void map_block(int bid, const FwdArgs& a, int& bh, in
     }
 }
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
+template <typename T, int D, bool CAUSAL, int QT, int NW>
+__global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     constexpr int KS = D / 16;           // k-steps of the score MFMA
     constexpr int DT = D / 32;           // 32-wide output tiles
     constexpr int CH = D / 8;            // 16-byte chunks per row
-    constexpr int LPT = kBc * CH / kThreads;  // chunks per thread per tensor per block
-    constexpr int TB = kBc * D * 2;      // bytes per K or V block
-    __shared__ __attribute__((aligned(16))) char smem[4 * TB];
+    constexpr int STAGES = D == 64 ? 3 : 2;
+    constexpr int TB = kBc * D * 2;      // bytes of one K or V block
+    constexpr int SB = 2 * TB;           // one ring stage: K block, then V block
+    constexpr int KCH = TB / 1024;       // 1 KiB DMA chunks per block
+    constexpr int CPW = 2 * KCH / NW;    // DMA instructions per wave per stage
+    constexpr int ROWS = 32 * QT;        // query rows per wave
+    constexpr int BR = ROWS * NW;        // query rows per workgroup
+    static_assert(CPW * NW == 2 * KCH, "stage must split evenly over the waves");
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int h = lane >> 5, l32 = lane & 31;
     int bh, qb;
     map_block(blockIdx.x, a, bh, qb);
@@ -86,156 +97,207 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     const uint16_t* __restrict__ K = a.k + head;
     const uint16_t* __restrict__ V = a.v + head;
 
-    const int q0 = qb * kBr + wave * 32;  // first query row of this wave
-    const int qrow = q0 + l32;            // query row owned by this lane (and lane ^ 32)
+    const int q0 = qb * BR + wave * ROWS;  // first query row of this wave
     const bool wave_active = q0 < N;
 
-    // Q fragment: B operand of S^T = K Q^T (column = query, k = head dim).
-    u32x4 qf[KS];
-    {
-        const uint16_t* qp = Q + (size_t)min(qrow, N - 1) * D + 8 * h;
+    // Q fragments: B operand of S^T = K Q^T (column = query, k = head dim).
+    u32x4 qf[QT][KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+    for (int t = 0; t < QT; ++t) {
+        const uint16_t* qp = Q + (size_t)min(q0 + 32 * t + l32, N - 1) * D + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[t][ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
     }
 
     const int nkb_all = (N + kBc - 1) / kBc;
-    const int nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * kBr) - 1) / kBc + 1) : nkb_all;
+    const int nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * BR) - 1) / kBc + 1) : nkb_all;
 
-    f32x16 oacc[DT];
+    f32x16 oacc[QT][DT];
+    float m_run[QT], l_run[QT];
 #pragma unroll
-    for (int u = 0; u < DT; ++u) oacc[u] = f32x16{};
-    float m_run = kMaskFloor, l_run = 0.f;
+    for (int t = 0; t < QT; ++t) {
+        m_run[t] = kMaskFloor;
+        l_run[t] = 0.f;
+#pragma unroll
+        for (int u = 0; u < DT; ++u) oacc[t][u] = f32x16{};
+    }
 
-    u32x4 kr[LPT], vr[LPT];
-    auto gload = [&](int kb) {
+    // Ring of STAGES key/value blocks filled by LDS-DMA. Chunk j (1 KiB) of a
+    // stage is written by wave j % NW; lane l of it carries granule 64*(j % KCH) + l
+    // of the K (j < KCH) or V block, i.e. row r, stored chunk sc, logical chunk
+    // sc ^ swz(r) of the block.
+    auto issue = [&](int kb, int st) {
+        char* sb = smem + st * SB;
 #pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int x = tid + kThreads * u, r = x / CH, c = x % CH;
-            const size_t g = (size_t)min(kb * kBc + r, N - 1) * D + c * 8;
-            kr[u] = *reinterpret_cast<const u32x4*>(K + g);
-            vr[u] = *reinterpret_cast<const u32x4*>(V + g);
+        for (int u = 0; u < CPW; ++u) {
+            const int chunk = u * NW + wave;
+            const int p = (chunk % KCH) * 64 + lane;
+            const int r = p / CH, c = (p % CH) ^ swz<D>(r);
+            const uint16_t* src = (chunk < KCH ? K : V) + (size_t)min(kb * kBc + r, N - 1) * D + c * 8;
+            dma16(src, sb + chunk * 1024);
         }
     };
-    auto swrite = [&](int buf) {
-        char* kb_ = smem + buf * 2 * TB;
-        char* vb_ = kb_ + TB;
-#pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int x = tid + kThreads * u, r = x / CH, c = x % CH;
-            lds_write16(kb_, tile_off<D>(r, c), kr[u]);
-            lds_write16(vb_, tile_off<D>(r, c), vr[u]);
-        }
-    };
 
-    gload(0);
-    swrite(0);
-    __syncthreads();
-
-    // Lane-constant parts of the transposed V read: 16-lane group g, lane L in group.
+    // Transposed V read: lane L of 16-lane group g addresses row 16c + 8h + L/4 (+4 for
+    // the second half of the operand), columns 32u + 16(g&1) + 4(L&3). The row
+    // swizzle depends only on row bits 1..3, so the 16c part is an immediate offset.
     const int g16 = lane >> 4, L16 = lane & 15;
-    const int tr_row = 8 * h + (L16 >> 2);
-    const int tr_col = 16 * (g16 & 1) + 4 * (L16 & 3);  // plus 32*u
-    const int tr_half = (L16 & 1) * 8;
+    uint32_t tr_addr[DT][2];
+#pragma unroll
+    for (int u = 0; u < DT; ++u)
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi)
+            tr_addr[u][hi] = (uint32_t)(TB + tile_off<D>(8 * h + (L16 >> 2) + 4 * hi,
+                                                         (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
+                                        (L16 & 1) * 8);
+    const uint32_t smem_addr = lds_addr(smem);
     const int s_row = perm32(l32);
 
+    issue(0, 0);
+    if (STAGES == 3 && nkb > 1) issue(1, 1);
+
     for (int kb = 0; kb < nkb; ++kb) {
-        const int buf = kb & 1;
-        const char* kbuf = smem + buf * 2 * TB;
+        // this wave's share of block kb has landed; then every wave's has, and
+        // every wave is done reading the stage the next issue overwrites
+        if (STAGES == 3 && kb + 1 < nkb) wait_vmcnt<CPW>();
+        else wait_vmcnt<0>();
+        barrier();
+        if constexpr (STAGES == 3) {
+            if (kb + 2 < nkb) issue(kb + 2, (kb + 2) % 3);
+        } else {
+            if (kb + 1 < nkb) issue(kb + 1, (kb + 1) & 1);
+        }
+        const char* kbuf = smem + (kb % STAGES) * SB;
         const char* vbuf = kbuf + TB;
-        if (kb + 1 < nkb) gload(kb + 1);
         const int key0 = kb * kBc;
-        const bool compute = wave_active && (!CAUSAL || key0 <= q0 + 31);
-        if (compute) {
-            // ---- S^T (64 keys x 32 queries): two 32x32 tiles
-            f32x16 s[2] = {f32x16{}, f32x16{}};
+        if (!wave_active || (CAUSAL && key0 > q0 + ROWS - 1)) continue;
+
+        // ---- S^T (64 keys x 32 queries per query tile): two 32x32 tiles each.
+        // All K operand reads go out first so their LDS latency overlaps.
+        u32x4 ka[KS][2];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const u32x4 ka = lds_read16(kbuf, tile_off<D>(32 * t + s_row, 2 * ks + h));
-                    s[t] = T::mfma32(ka, qf[ks], s[t]);
-                }
+            for (int kt = 0; kt < 2; ++kt) ka[ks][kt] = lds_read16(kbuf, tile_off<D>(32 * kt + s_row, 2 * ks + h));
+        f32x16 s[QT][2];
+#pragma unroll
+        for (int t = 0; t < QT; ++t) s[t][0] = s[t][1] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int t = 0; t < QT; ++t) s[t][kt] = T::mfma32(ka[ks][kt], qf[t][ks], s[t][kt]);
+
+        // V^T operands for the whole block, issued before the softmax so they land meanwhile
+        u32x4 va[4][DT];
+        {
+            const uint32_t stage_addr = smem_addr + (uint32_t)((kb % STAGES) * SB);
+#pragma unroll
+            for (int u = 0; u < DT; ++u) {
+                const uint32_t a0 = stage_addr + tr_addr[u][0], a1 = stage_addr + tr_addr[u][1];
+                u32x2 lo, hi;
+                lo = tr_read<0 * 16 * 2 * D>(a0); hi = tr_read<0 * 16 * 2 * D>(a1); va[0][u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                lo = tr_read<1 * 16 * 2 * D>(a0); hi = tr_read<1 * 16 * 2 * D>(a1); va[1][u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                lo = tr_read<2 * 16 * 2 * D>(a0); hi = tr_read<2 * 16 * 2 * D>(a1); va[2][u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                lo = tr_read<3 * 16 * 2 * D>(a0); hi = tr_read<3 * 16 * 2 * D>(a1); va[3][u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
-            // ---- mask: causal diagonal block and ragged end of the sequence
-            const bool need_mask = (CAUSAL && key0 + kBc - 1 > q0) || (key0 + kBc > N);
+        }
+
+        uint32_t pk[QT][2][8];
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+            // ---- mask: causal diagonal block and ragged end of the sequence.
+            // Register i of key tile kt holds key key0 + 32 kt + 16 (i/8) + 8 h + i%8.
+            const bool need_mask = (CAUSAL && key0 + kBc - 1 > q0 + 32 * t) || (key0 + kBc > N);
             if (need_mask) {
+                const int qrow = q0 + 32 * t + l32;
+                const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - key0 - 8 * h;  // last visible offset
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
+                for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = key0 + 32 * t + 16 * (i >> 3) + 8 * h + (i & 7);
-                        if ((CAUSAL && key > qrow) || key >= N) s[t][i] = -INFINITY;
-                    }
-                }
+                    for (int i = 0; i < 16; ++i)
+                        if (32 * kt + 16 * (i >> 3) + (i & 7) > lim) s[t][kt][i] = -INFINITY;
             }
             // ---- online softmax (base 2)
-            float mx = s[0][0];
+            float mx = s[t][0][0];
 #pragma unroll
-            for (int i = 1; i < 16; i += 2) mx = max3(mx, s[0][i], s[0][i + 1]);
+            for (int i = 1; i < 16; i += 2) mx = max3(mx, s[t][0][i], s[t][0][i + 1]);
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) mx = max3(mx, s[1][i], s[1][i + 1]);
+            for (int i = 0; i < 16; i += 2) mx = max3(mx, s[t][1][i], s[t][1][i + 1]);
             mx = pair_max(mx);
-            const float m_new = fmaxf(m_run, mx * a.c);
-            const float alpha = fast_exp2(m_run - m_new);
+            const float m_new = fmaxf(m_run[t], mx * a.c);
+            const float alpha = fast_exp2(m_run[t] - m_new);
             float lsum = 0.f;
-            uint32_t pk[2][8];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
                 for (int w = 0; w < 8; ++w) {
-                    const float p0 = fast_exp2(__builtin_fmaf(s[t][2 * w], a.c, -m_new));
-                    const float p1 = fast_exp2(__builtin_fmaf(s[t][2 * w + 1], a.c, -m_new));
+                    const float p0 = fast_exp2(__builtin_fmaf(s[t][kt][2 * w], a.c, -m_new));
+                    const float p1 = fast_exp2(__builtin_fmaf(s[t][kt][2 * w + 1], a.c, -m_new));
                     lsum += p0 + p1;
-                    pk[t][w] = T::pack2(p0, p1);
+                    pk[t][kt][w] = T::pack2(p0, p1);
                 }
             }
-            l_run = alpha * l_run + lsum;
+            l_run[t] = alpha * l_run[t] + lsum;
             if (__ballot(alpha != 1.f)) {
 #pragma unroll
-                for (int u = 0; u < DT; ++u) oacc[u] *= alpha;
+                for (int u = 0; u < DT; ++u) oacc[t][u] *= alpha;
             }
-            m_run = m_new;
-            // ---- O^T (D x 32 queries) += V^T P^T over four 16-key chunks
+            m_run[t] = m_new;
+        }
+        // ---- O^T (D x 32 queries) += V^T P^T over four 16-key chunks
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u32x4 pb = {pk[c >> 1][4 * (c & 1) + 0], pk[c >> 1][4 * (c & 1) + 1],
-                                  pk[c >> 1][4 * (c & 1) + 2], pk[c >> 1][4 * (c & 1) + 3]};
-                const int row = 16 * c + tr_row;
+        for (int c = 0; c < 4; ++c) {
+            if constexpr (DT == 2) lds_wait_all(va[c][0], va[c][1]);
+            else lds_wait_all(va[c][0], va[c][1], va[c][2], va[c][3]);
 #pragma unroll
-                for (int u = 0; u < DT; ++u) {
-                    const int col = 32 * u + tr_col;
-                    const u32x2 lo = lds_read_tr(vbuf, tile_off<D>(row, col >> 3) + tr_half);
-                    const u32x2 hi = lds_read_tr(vbuf, tile_off<D>(row + 4, col >> 3) + tr_half);
-                    const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-                    oacc[u] = T::mfma32(va, pb, oacc[u]);
+            for (int u = 0; u < DT; ++u) {
+#pragma unroll
+                for (int t = 0; t < QT; ++t) {
+                    const u32x4 pb = {pk[t][c >> 1][4 * (c & 1) + 0], pk[t][c >> 1][4 * (c & 1) + 1],
+                                      pk[t][c >> 1][4 * (c & 1) + 2], pk[t][c >> 1][4 * (c & 1) + 3]};
+                    oacc[t][u] = T::mfma32(va[c][u], pb, oacc[t][u]);
                 }
             }
         }
-        if (kb + 1 < nkb) swrite(buf ^ 1);
-        __syncthreads();
     }
 
     // ---- epilogue: O = O_acc / l, lse = ln2 * (m + log2 l)
-    const float l_tot = pair_sum(l_run);
-    if (wave_active && qrow < N) {
-        const float inv = 1.f / l_tot;
-        uint16_t* op = a.o + head + (size_t)qrow * D + 4 * h;
 #pragma unroll
-        for (int u = 0; u < DT; ++u) {
+    for (int t = 0; t < QT; ++t) {
+        const float l_tot = pair_sum(l_run[t]);
+        const int qrow = q0 + 32 * t + l32;
+        if (wave_active && qrow < N) {
+            const float inv = 1.f / l_tot;
+            uint16_t* op = a.o + head + (size_t)qrow * D + 4 * h;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const u32x2 w = {T::pack2(oacc[u][4 * g] * inv, oacc[u][4 * g + 1] * inv),
-                                 T::pack2(oacc[u][4 * g + 2] * inv, oacc[u][4 * g + 3] * inv)};
-                *reinterpret_cast<u32x2*>(op + 32 * u + 8 * g) = w;
+            for (int u = 0; u < DT; ++u) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const u32x2 w = {T::pack2(oacc[t][u][4 * g] * inv, oacc[t][u][4 * g + 1] * inv),
+                                     T::pack2(oacc[t][u][4 * g + 2] * inv, oacc[t][u][4 * g + 3] * inv)};
+                    *reinterpret_cast<u32x2*>(op + 32 * u + 8 * g) = w;
+                }
             }
+            if (h == 0) a.lse[(size_t)bh * N + qrow] = (m_run[t] + __log2f(l_tot)) * kLn2;
         }
-        if (h == 0) a.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
     }
 }
 
+template <int D>
+struct FwdShape {  // rows per wave (as 32-row tiles) and waves per workgroup for head dim D
+    static constexpr int QT = D == 64 ? FA_FWD_QT : 1;
+    static constexpr int NW = FA_FWD_NW;
+    static constexpr int BR = 32 * QT * NW;
+};
+
 template <typename T, int D, bool C>
-hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_kernel<T, D, C>), dim3(a.BH * a.nqb), dim3(kThreads), 0, stream, a);
+hipError_t launch(FwdArgs a, hipStream_t stream) {
+    using S = FwdShape<D>;
+    a.nqb = (a.N + S::BR - 1) / S::BR;
+    a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+    hipLaunchKernelGGL((fwd_kernel<T, D, C, S::QT, S::NW>), dim3(a.BH * a.nqb), dim3(64 * S::NW), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -257,8 +319,8 @@ hipError_t fwd_mfma(const void* q, const void* k, const void* v, void* o, float*
     a.lse = lse;
     a.BH = B * H;
     a.N = N;
-    a.nqb = (N + kBr - 1) / kBr;
-    a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+    a.nqb = 0;
+    a.heads_per_xcd = 0;
     a.c = scale * kLog2e;
     return dtype == 0 ? dispatch_d<Bf16>(a, d, causal, stream) : dispatch_d<F16>(a, d, causal, stream);
 }
