@@ -1,13 +1,18 @@
 """Benchmark: exact attention forward + backward through libfa.so on one MI355X.
 
-One step = one pass of the whole path over one batch: fa_fwd (O, lse) then
-fa_bwd (dQ, dK, dV), on the GPT-2-small-shaped causal workload
-(B=8, H=12, N=1024, d=64, bf16, scale 1/8) unless --workload says otherwise.
-Inputs are seeded synthetic Gaussians already resident in device memory.
+One step = one pass of the whole path over one batch: fa_fwd (O, lse), then
+fa_bwd_prep (D, lse*log2e) and fa_bwd_main (dQ, dK, dV), on the GPT-2-small
+shaped causal workload (B=8, H=12, N=1024, d=64, bf16, scale 1/8) unless
+--workload says otherwise. Inputs are seeded synthetic Gaussians already
+resident in device memory when the timed region starts.
 
 FLOP counting: forward 4*B*H*N^2*d, forward+backward 10*B*H*N^2*d, both halved
-for causal. The backward alone is credited 10*B*H*N^2*d (its five products).
-Prints one JSON line.
+for causal. The backward alone is credited with its five matrix products,
+10*B*H*N^2*d (halved for causal), whatever the kernels recompute.
+
+Every launch of the timed region is bracketed by HIP events on the stream the
+library enqueues on, so each stage's average duration is measured live; the
+roofline entry is the dominant one. Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -23,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA, published
-PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector, published
 
 WORKLOADS = {
     "gpt2_small_causal": dict(B=8, H=12, N=1024, d=64, causal=True, dtype="bf16", seed=1003, mul=1.0),
@@ -32,11 +37,60 @@ WORKLOADS = {
     "tiny_fp32": dict(B=1, H=1, N=128, d=64, causal=False, dtype="fp32", seed=1001, mul=1.0),
 }
 
+# kernel names as rocprofv3 reports them, per stage of the default strategy
+KERNELS = {"fwd": "fwd_kernel", "prep": "bwd_prep_kernel", "main": "bwd_fused_kernel"}
+
 
 def flops(w, which):
     base = w["B"] * w["H"] * w["N"] ** 2 * w["d"]
     mult = {"fwd": 4, "bwd": 10, "step": 10, "step_alg": 14}[which]
     return mult * base * (0.5 if w["causal"] else 1.0)
+
+
+def score_entries(N):
+    """Entries of one head's N x N score grid (what standard attention writes out)."""
+    return N * N
+
+
+def io_bytes(w):
+    """Forward HBM bytes per launch: FlashAttention's compulsory traffic (read Q, K, V,
+    write O and lse) and standard attention's (the same, plus writing the N x N scores,
+    reading them for the softmax, writing the probabilities and reading them for PV),
+    both at the workload's element size, scores and probabilities at that size too."""
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    elt = 4 if w["dtype"] == "fp32" else 2
+    fa_b = B * H * (4 * N * d * elt + 4 * N)
+    std_b = B * H * (4 * N * d + 4 * score_entries(N)) * elt
+    return fa_b, std_b
+
+
+def cpu_baseline(w, shape, scale, causal, min_seconds=10.0):
+    """The fp64 oracle (as it stands) on the host cores: whole fwd+bwd passes over the
+    same seeded inputs, repeated until at least ``min_seconds`` have elapsed, or over a
+    subset of (batch, head) pairs when one pass would take longer than that."""
+    import oracle
+    import seedgen
+    B, H, N, d = shape
+    heads = B * H
+    drawn = [seedgen.draw(w["seed"], t, shape, w["dtype"], mul=w["mul"]).f64.reshape(heads, N, d) for t in range(4)]
+    # time one head first to size the sample
+    one = [x[:1].reshape(1, 1, N, d) for x in drawn]
+    t0 = time.perf_counter()
+    oracle.bwd(*one, scale, causal)
+    t_head = max(time.perf_counter() - t0, 1e-6)
+    nh = max(1, min(heads, int(min_seconds / t_head)))
+    sample = [x[:nh].reshape(1, nh, N, d) for x in drawn]
+    reps, t_total = 0, 0.0
+    while t_total < min_seconds and reps < 1000:
+        t0 = time.perf_counter()
+        oracle.bwd(*sample, scale, causal)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    credited = flops(dict(w, B=1, H=nh), "step") * reps
+    return {"value": round(credited / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} fwd+bwd pass(es) of the fp64 oracle over {nh} of {heads} (batch, head) pairs "
+                      f"of the same workload, {t_total:.2f} s; credited with the 10*N^2*d rule"}
 
 
 def main():
@@ -49,8 +103,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernel is "
-              "measured on one GPU's share at its real shape.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the kernels are measured on "
+              "one GPU's share of the work at its real shape; see the sharding notes in the design document.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -74,80 +129,72 @@ def main():
     strategy = {"default": fa.FA_DQ_DEFAULT, "atomic": fa.FA_DQ_ATOMIC, "separate": fa.FA_DQ_SEPARATE}[args.dq]
     stream = torch.cuda.current_stream()
 
-    def step():
+    def run(evs=None):
+        if evs: evs[0].record(stream)
         fa.fa_fwd(q, k, v, o, lse, causal, scale, stream)
-        fa.fa_bwd_dq(q, k, v, o, do, lse, dq, dk, dv, causal, scale, strategy, ws, stream)
+        if evs: evs[1].record(stream)
+        fa.fa_bwd_prep(o, do, lse, ws, strategy, stream)
+        if evs: evs[2].record(stream)
+        fa.fa_bwd_main(q, k, v, o, do, lse, dq, dk, dv, ws, causal, scale, strategy, stream)
+        if evs: evs[3].record(stream)
 
     for _ in range(args.warmup):
-        step()
+        run()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
-        fa.fa_fwd(q, k, v, o, lse, causal, scale, stream)
-        ev[i][1].record(stream)
-        fa.fa_bwd_dq(q, k, v, o, do, lse, dq, dk, dv, causal, scale, strategy, ws, stream)
-        ev[i][2].record(stream)
+        run(ev[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
-    ms_step = total_ms / K
-    fwd_mean, bwd_mean = statistics.mean(fwd_ms), statistics.mean(bwd_ms)
+    ms_step = t_start.elapsed_time(t_end) / K
+    stage_ms = {name: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in ev)
+                for j, name in enumerate(("fwd", "prep", "main"))}
 
     tf_step = flops(w, "step") / (ms_step * 1e-3) / 1e12
-    tf_fwd = flops(w, "fwd") / (fwd_mean * 1e-3) / 1e12
-    tf_bwd = flops(w, "bwd") / (bwd_mean * 1e-3) / 1e12
-    dom = "bwd" if bwd_mean >= fwd_mean else "fwd"
-    dom_ms = bwd_mean if dom == "bwd" else fwd_mean
-    dom_tf = tf_bwd if dom == "bwd" else tf_fwd
+    tf_fwd = flops(w, "fwd") / (stage_ms["fwd"] * 1e-3) / 1e12
+    bwd_ms = stage_ms["prep"] + stage_ms["main"]
+    tf_bwd = flops(w, "bwd") / (bwd_ms * 1e-3) / 1e12
+    fp32 = w["dtype"] == "fp32"
+    peak = PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+
+    # roofline of the dominant kernel: algorithmic FLOP per launch / its average duration
+    dom = "main" if stage_ms["main"] >= stage_ms["fwd"] else "fwd"
+    dom_flop = flops(w, "bwd") if dom == "main" else flops(w, "fwd")
+    dom_tf = dom_flop / (stage_ms[dom] * 1e-3) / 1e12
+    single = not (dom == "main" and (args.dq == "atomic" or fp32))
     roofline = {
-        "bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
-        "kernel": "fa_bwd (bwd_pre + bwd_main + dq pass)" if dom == "bwd" else "fa_fwd (fwd_kernel)",
-        "flop_per_launch": flops(w, dom), "avg_launch_ms": round(dom_ms, 5),
+        "bound": "mfma", "achieved": round(dom_tf, 2), "peak": peak, "unit": "TFLOP/s",
+        "frac": round(dom_tf / peak, 4), "traffic": None,
+        "kernel": KERNELS[dom] if single else f"fa_bwd_main ({'atomic main + convert' if not fp32 else 'fp32'})",
+        "flop_per_launch": dom_flop, "avg_launch_ms": round(stage_ms[dom], 5),
+        "flop_rule": "fwd 4*B*H*N^2*d, bwd 10*B*H*N^2*d (five products), halved for causal",
     }
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        sample = dict(w)
-        # a bounded sample of the same workload: whole heads, as many as fit ~10-30 s of oracle work
-        heads = B * H
-        per_head = 16 * N * N * d * (0.5 if causal else 1.0)  # oracle fwd+bwd flops per head
-        budget = 60e9 * max(1, oracle.num_threads()) / 8      # ~20 s at the oracle's measured speed
-        nh = max(1, min(heads, int(budget // per_head)))
-        qd, kd, vd, dod = (seedgen.draw(w["seed"], t, shape, w["dtype"], mul=w["mul"]).f64.reshape(heads, 1, N, d)[:nh]
-                           .reshape(1, nh, N, d) for t in range(4))
-        t0 = time.perf_counter()
-        oracle.bwd(qd, kd, vd, dod, scale, causal)
-        t_or = time.perf_counter() - t0
-        credited = 10 * nh * N * N * d * (0.5 if causal else 1.0)
-        cpu = {"value": round(credited / t_or / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-               "kind": "oracle", "sample": f"{nh} of {heads} (batch, head) pairs, one fwd+bwd each, "
-                                           f"fp64 oracle, {t_or:.2f} s; credited with the same 10*N^2*d rule"}
-        del sample
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, shape, scale, causal)
 
     cfg = {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "causal": causal, "dtype": w["dtype"],
-           "scale": scale, "dq_strategy": args.dq, "global_batch": B, "seq_len": N, "parallelism": "none"}
+           "scale": scale, "dq_strategy": args.dq}
     out = {
         "metric": "attention TFLOP/s fwd+bwd (10*B*H*N^2*d, halved for causal)",
         "value": round(tf_step, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w["dtype"], "data": "synthetic seeded N(0,1)", "config": cfg,
-        "fwd": {"ms": round(fwd_mean, 5), "tflops": round(tf_fwd, 3), "frac_peak": round(tf_fwd / PEAK_BF16_TFLOPS, 4)},
-        "fwd_bwd": {"tflops_10x": round(tf_step, 3), "frac_peak": round(tf_step / PEAK_BF16_TFLOPS, 4),
+        "dtype": w["dtype"], "data": "synthetic: seeded i.i.d. N(0,1) inputs of the workload's shape",
+        "config": cfg,
+        "fwd": {"ms": round(stage_ms["fwd"], 5), "tflops": round(tf_fwd, 3), "frac_peak": round(tf_fwd / peak, 4)},
+        "bwd": {"ms": round(bwd_ms, 5), "prep_ms": round(stage_ms["prep"], 5), "main_ms": round(stage_ms["main"], 5),
+                "tflops_10x": round(tf_bwd, 3)},
+        "fwd_bwd": {"tflops_10x": round(tf_step, 3), "frac_peak": round(tf_step / peak, 4),
                     "tflops_14x_algorithmic": round(flops(w, "step_alg") / (ms_step * 1e-3) / 1e12, 3)},
-        "bwd": {"ms": round(bwd_mean, 5), "tflops_10x": round(tf_bwd, 3)},
+        "io_fwd": {"flash_bytes": io_bytes(w)[0], "standard_bytes": io_bytes(w)[1],
+                   "standard_over_flash": round(io_bytes(w)[1] / io_bytes(w)[0], 2)},
         "roofline": roofline, "cpu_baseline": cpu, "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(out), flush=True)

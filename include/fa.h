@@ -50,15 +50,17 @@ typedef enum {
                                 scale not finite and > 0, overlapping buffers, size overflow */
     FA_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}, unknown dtype, fp32 with d = 128,
                                 unknown dQ strategy */
-    FA_ERR_WORKSPACE = 3,    /* workspace null or smaller than fa_bwd_workspace_size() */
+    FA_ERR_WORKSPACE = 3,    /* workspace null, not 256-byte aligned, or smaller than
+                                fa_bwd_workspace_size() */
     FA_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError after launch) */
 } fa_status;
 
 /* How fa_bwd_dq() forms dQ. */
 typedef enum {
-    FA_DQ_DEFAULT = 0,   /* the strategy measured fastest for the shape */
+    FA_DQ_DEFAULT = 0,   /* the strategy measured fastest on MI355X: FA_DQ_SEPARATE */
     FA_DQ_ATOMIC = 1,    /* fp32 atomic adds into a workspace accumulator, then a convert pass */
-    FA_DQ_SEPARATE = 2   /* a second kernel per query block recomputes the tiles and writes dQ */
+    FA_DQ_SEPARATE = 2   /* query workgroups recompute the tiles and write dQ directly, in the
+                            same launch as the dK/dV workgroups */
 } fa_dq_strategy;
 
 /*
@@ -75,9 +77,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd() and fa_bwd_dq() need for this shape with any
- * dQ strategy: D_i = dO_i . O_i ([B,H,N] float) plus the fp32 dQ accumulator
- * ([B,H,N,d] float), each rounded up to 256 bytes. Returns 0 for invalid shapes.
+ * Bytes of device workspace the backward needs for this shape, whatever the
+ * dQ strategy: D_i = dO_i . O_i ([B,H,N] float), lse_i * log2(e) ([B,H,N]
+ * float) and, for bf16/fp16, the fp32 dQ accumulator of FA_DQ_ATOMIC
+ * ([B,H,N,d] float), each part rounded up to 256 bytes. All O(N). Returns 0
+ * for invalid shapes.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype);
 
@@ -87,8 +91,10 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype);
  *   dout            : upstream gradient dL/dO, [B,H,N,d] of `dtype`.
  *   workspace       : caller-owned device memory of at least fa_bwd_workspace_size() bytes,
  *                     256-byte aligned; its contents on entry do not matter.
- * Reads only q, k, v, o, dout and lse; recomputes every score and probability tile.
- * Uses the default dQ strategy. Returns a fa_status.
+ * Reads only q, k, v, o, dout and lse; recomputes every score and probability tile
+ * on chip from them (michaelc-yu summary of Dao et al., "Backward / recomputation").
+ * 16-bit inputs need d = 64. Uses the default dQ strategy. Equivalent to
+ * fa_bwd_prep() followed by fa_bwd_main(). Returns a fa_status.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv,
@@ -100,6 +106,28 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const 
               const float* lse, void* dq, void* dk, void* dv,
               int B, int H, int N, int d, float scale, int causal, int dtype, int dq_strategy,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * First stage of the backward, for callers that schedule the stages themselves:
+ * one pass over o and dout that writes D_i = dO_i . O_i and lse_i * log2(e) into
+ * the workspace (and, for FA_DQ_ATOMIC, zeroes its fp32 dQ accumulator). For
+ * FA_FP32 it validates and returns (the fp32 backward forms D in fa_bwd_main).
+ * Arguments as fa_bwd_dq(). Returns a fa_status.
+ */
+int fa_bwd_prep(const void* o, const void* dout, const float* lse, int B, int H, int N, int d, int dtype,
+                int dq_strategy, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Second stage of the backward: dq, dk, dv from q, k, v, dout and a workspace that
+ * fa_bwd_prep() filled, on the same stream, for the same o, dout, lse and strategy
+ * (a workspace prepared for another strategy gives wrong results). For bf16/fp16
+ * with the default strategy this is a single kernel launch. Arguments as
+ * fa_bwd_dq(). Returns a fa_status.
+ */
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv,
+                int B, int H, int N, int d, float scale, int causal, int dtype, int dq_strategy,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a fa_status value. Never NULL. */
 const char* fa_status_string(int status);

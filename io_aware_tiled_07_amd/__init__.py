@@ -6,8 +6,8 @@ the current stream. There is no fallback: if ``libfa.so`` is missing or a call
 fails, an exception is raised.
 
 The raw entry points keep the C names (``fa_fwd``, ``fa_bwd``, ``fa_bwd_dq``,
-``fa_bwd_workspace_size``, ``fa_status_string``) and take caller-allocated
-torch tensors; ``fwd`` and ``bwd`` allocate their outputs.
+``fa_bwd_prep``, ``fa_bwd_main``, ``fa_bwd_workspace_size``, ``fa_status_string``)
+and take caller-allocated torch tensors; ``fwd`` and ``bwd`` allocate their outputs.
 """
 from __future__ import annotations
 
@@ -19,7 +19,7 @@ __all__ = [
     "FA_BF16", "FA_FP16", "FA_FP32", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED",
     "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_DQ_DEFAULT", "FA_DQ_ATOMIC", "FA_DQ_SEPARATE",
     "FaError", "library_path", "load", "fa_status_string", "fa_bwd_workspace_size",
-    "fa_fwd", "fa_bwd", "fa_bwd_dq", "fwd", "bwd", "dtype_code",
+    "fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_prep", "fa_bwd_main", "fwd", "bwd", "dtype_code",
 ]
 
 FA_BF16, FA_FP16, FA_FP32 = 0, 1, 2
@@ -62,6 +62,10 @@ def load():
         lib.fa_bwd.restype = _i
         lib.fa_bwd_dq.argtypes = [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _i, _i, _vp, _sz, _vp]
         lib.fa_bwd_dq.restype = _i
+        lib.fa_bwd_main.argtypes = [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _i, _i, _vp, _sz, _vp]
+        lib.fa_bwd_main.restype = _i
+        lib.fa_bwd_prep.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]
+        lib.fa_bwd_prep.restype = _i
         _lib = lib
     return _lib
 
@@ -119,10 +123,7 @@ def fa_fwd(q, k, v, o, lse, causal: bool = False, scale=None, stream=None) -> No
         raise FaError(st, "fa_fwd")
 
 
-def fa_bwd_dq(q, k, v, o, do, lse, dq, dk, dv, causal: bool = False, scale=None,
-              dq_strategy: int = FA_DQ_DEFAULT, workspace=None, stream=None) -> None:
-    """Enqueue the backward into caller-allocated ``dq``, ``dk``, ``dv``. ``workspace`` is a
-    device tensor of at least ``fa_bwd_workspace_size`` bytes (allocated here if None)."""
+def _bwd_args(q, k, v, o, do, lse, dq, dk, dv, workspace):
     import torch
     B, H, N, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
@@ -133,13 +134,49 @@ def fa_bwd_dq(q, k, v, o, do, lse, dq, dk, dv, causal: bool = False, scale=None,
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check_bhnd("workspace", workspace)
-    nbytes = workspace.numel() * workspace.element_size()
+    return code, workspace, workspace.numel() * workspace.element_size()
+
+
+def fa_bwd_dq(q, k, v, o, do, lse, dq, dk, dv, causal: bool = False, scale=None,
+              dq_strategy: int = FA_DQ_DEFAULT, workspace=None, stream=None) -> None:
+    """Enqueue the backward into caller-allocated ``dq``, ``dk``, ``dv``. ``workspace`` is a
+    device tensor of at least ``fa_bwd_workspace_size`` bytes (allocated here if None)."""
+    B, H, N, d = q.shape
+    code, workspace, nbytes = _bwd_args(q, k, v, o, do, lse, dq, dk, dv, workspace)
     st = load().fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
                           _scale(scale, d), int(bool(causal)), code, int(dq_strategy),
                           workspace.data_ptr(), nbytes, _stream(stream))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_dq")
+
+
+def fa_bwd_prep(o, do, lse, workspace, dq_strategy: int = FA_DQ_DEFAULT, stream=None) -> None:
+    """First backward stage: D and lse*log2(e) (and the atomic accumulator's zeroing) into ``workspace``."""
+    import torch
+    B, H, N, d = o.shape
+    _check_bhnd("o", o)
+    _check_bhnd("do", do, o.shape, o.dtype)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    _check_bhnd("workspace", workspace)
+    st = load().fa_bwd_prep(o.data_ptr(), do.data_ptr(), lse.data_ptr(), B, H, N, d, dtype_code(o),
+                            int(dq_strategy), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_prep")
+
+
+def fa_bwd_main(q, k, v, o, do, lse, dq, dk, dv, workspace, causal: bool = False, scale=None,
+                dq_strategy: int = FA_DQ_DEFAULT, stream=None) -> None:
+    """Second backward stage: dQ, dK, dV from a workspace ``fa_bwd_prep`` filled."""
+    B, H, N, d = q.shape
+    code, workspace, nbytes = _bwd_args(q, k, v, o, do, lse, dq, dk, dv, workspace)
+    st = load().fa_bwd_main(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                            _scale(scale, d), int(bool(causal)), code, int(dq_strategy),
+                            workspace.data_ptr(), nbytes, _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_main")
 
 
 def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, causal: bool = False, scale=None, workspace=None,

@@ -48,6 +48,53 @@ int check_common(int B, int H, int N, int d, float scale, int causal, int dtype,
     return FA_OK;
 }
 
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+bool known_strategy(int s) { return s == FA_DQ_DEFAULT || s == FA_DQ_ATOMIC || s == FA_DQ_SEPARATE; }
+
+// Workspace of the backward: D ([B,H,N] float), lse * log2(e) ([B,H,N] float)
+// and, for 16-bit inputs, the fp32 dQ accumulator of the atomic strategy
+// ([B,H,N,d] float); each part starts on a 256-byte boundary.
+struct Workspace {
+    size_t delta, lse2, dq_acc, bytes;
+};
+Workspace layout(int B, int H, int N, int d, int dtype) {
+    const size_t rows = (size_t)B * H * N;
+    Workspace w;
+    w.delta = 0;
+    w.lse2 = round_up(rows * sizeof(float), 256);
+    w.dq_acc = w.lse2 + round_up(rows * sizeof(float), 256);
+    w.bytes = w.dq_acc + (dtype == FA_FP32 ? 0 : round_up(rows * (size_t)d * sizeof(float), 256));
+    return w;
+}
+
+// Every check of fa_bwd_main / fa_bwd_dq, before any HIP call.
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+              void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+              int dq_strategy, void* workspace, size_t workspace_bytes) {
+    int st = check_common(B, H, N, d, scale, causal, dtype, /*backward=*/true);
+    if (st != FA_OK) return st;
+    if (!known_strategy(dq_strategy)) return FA_ERR_UNSUPPORTED;
+    const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+    for (const void* p : ptrs)
+        if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
+    const Workspace w = layout(B, H, N, d, dtype);
+    if (workspace == nullptr || !aligned256(workspace) || workspace_bytes < w.bytes) return FA_ERR_WORKSPACE;
+
+    const size_t tbytes = (size_t)B * H * N * d * elt_bytes(dtype);
+    const size_t lbytes = (size_t)B * H * N * sizeof(float);
+    const Range outs[] = {range(dq, tbytes), range(dk, tbytes), range(dv, tbytes), range(workspace, w.bytes)};
+    const Range ins[] = {range(q, tbytes), range(k, tbytes), range(v, tbytes), range(o, tbytes),
+                         range(dout, tbytes), range(lse, lbytes)};
+    for (int i = 0; i < 4; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return FA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
+    }
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,54 +139,75 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
     if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
     if (dtype != FA_BF16 && dtype != FA_FP16 && dtype != FA_FP32) return 0;
-    const size_t rows = (size_t)B * H * N;
-    size_t bytes = round_up(rows * sizeof(float), 256);
-    if (dtype != FA_FP32) bytes += round_up(rows * (size_t)d * sizeof(float), 256);
-    return bytes;
+    const Workspace w = layout(B, H, N, d, dtype);
+    return w.bytes;
 }
 
-int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-              void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
-              int dq_strategy, void* workspace, size_t workspace_bytes, void* stream) {
-    int st = check_common(B, H, N, d, scale, causal, dtype, /*backward=*/true);
+int fa_bwd_prep(const void* o, const void* dout, const float* lse, int B, int H, int N, int d, int dtype,
+                int dq_strategy, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_common(B, H, N, d, 1.f, 0, dtype, /*backward=*/true);
     if (st != FA_OK) return st;
-    if (dq_strategy != FA_DQ_DEFAULT && dq_strategy != FA_DQ_ATOMIC && dq_strategy != FA_DQ_SEPARATE)
-        return FA_ERR_UNSUPPORTED;
-    const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+    if (!known_strategy(dq_strategy)) return FA_ERR_UNSUPPORTED;
+    const void* ptrs[] = {o, dout, lse};
     for (const void* p : ptrs)
         if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
-    const size_t need = fa_bwd_workspace_size(B, H, N, d, dtype);
-    if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
-
+    const Workspace w = layout(B, H, N, d, dtype);
+    if (workspace == nullptr || !aligned256(workspace) || workspace_bytes < w.bytes) return FA_ERR_WORKSPACE;
     const size_t tbytes = (size_t)B * H * N * d * elt_bytes(dtype);
-    const size_t lbytes = (size_t)B * H * N * sizeof(float);
-    const Range outs[] = {range(dq, tbytes), range(dk, tbytes), range(dv, tbytes), range(workspace, need)};
-    const Range ins[] = {range(q, tbytes), range(k, tbytes), range(v, tbytes), range(o, tbytes),
-                         range(dout, tbytes), range(lse, lbytes)};
-    for (int i = 0; i < 4; ++i) {
-        for (const Range& r : ins)
-            if (overlap(outs[i], r)) return FA_ERR_INVALID_ARG;
-        for (int j = i + 1; j < 4; ++j)
-            if (overlap(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
-    }
+    const Range rw = range(workspace, w.bytes);
+    if (overlap(rw, range(o, tbytes)) || overlap(rw, range(dout, tbytes)) ||
+        overlap(rw, range(lse, (size_t)B * H * N * sizeof(float))))
+        return FA_ERR_INVALID_ARG;
 
+    if (dtype == FA_FP32) return FA_OK;  // the fp32 backward forms D itself in fa_bwd_main
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t rows = (size_t)B * H * N;
-    float* delta = static_cast<float*>(workspace);
-    float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(rows * sizeof(float), 256));
+    char* base = static_cast<char*>(workspace);
+    float* delta = reinterpret_cast<float*>(base + w.delta);
+    (void)hipGetLastError();
+    hipError_t e;
+    if (dq_strategy == FA_DQ_ATOMIC)
+        e = fa::bwd_atomic_prep(o, dout, B, H, N, dtype, delta, reinterpret_cast<float*>(base + w.dq_acc), s);
+    else
+        e = fa::bwd_prep(o, dout, lse, B, H, N, dtype, delta, reinterpret_cast<float*>(base + w.lse2), s);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+                int dq_strategy, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, dq_strategy, workspace,
+                       workspace_bytes);
+    if (st != FA_OK) return st;
+    const Workspace w = layout(B, H, N, d, dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* base = static_cast<char*>(workspace);
+    float* delta = reinterpret_cast<float*>(base + w.delta);
     (void)hipGetLastError();
     hipError_t e;
     if (dtype == FA_FP32) {
         e = fa::bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
                         static_cast<const float*>(o), static_cast<const float*>(dout), lse, static_cast<float*>(dq),
                         static_cast<float*>(dk), static_cast<float*>(dv), B, H, N, scale, causal != 0, delta, s);
+    } else if (dq_strategy == FA_DQ_ATOMIC) {
+        e = fa::bwd_atomic_main(q, k, v, dout, lse, dq, dk, dv, B, H, N, scale, causal != 0, dtype, delta,
+                                reinterpret_cast<float*>(base + w.dq_acc), s);
     } else {
-        // Default strategy: fp32 atomics into the workspace accumulator.
-        const int mode = dq_strategy == FA_DQ_SEPARATE ? 2 : 1;
-        e = fa::bwd_mfma(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, dtype, mode, delta,
-                         dq_acc, s);
+        e = fa::bwd_fused(q, k, v, dout, delta, reinterpret_cast<const float*>(base + w.lse2), dq, dk, dv, B, H, N,
+                          scale, causal != 0, dtype, s);
     }
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+              void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+              int dq_strategy, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, dq_strategy, workspace,
+                       workspace_bytes);
+    if (st != FA_OK) return st;
+    st = fa_bwd_prep(o, dout, lse, B, H, N, d, dtype, dq_strategy, workspace, workspace_bytes, stream);
+    if (st != FA_OK) return st;
+    return fa_bwd_main(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, dq_strategy, workspace,
+                       workspace_bytes, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,

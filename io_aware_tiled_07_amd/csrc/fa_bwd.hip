@@ -1,28 +1,41 @@
-// Backward pass of exact attention for 16-bit inputs on gfx950 (MFMA).
+// Backward pass of exact attention for 16-bit inputs on gfx950 (MFMA), with
+// dQ formed in a pass of its own (the default FA_DQ_SEPARATE strategy).
 //
 // The backward never reads a stored score or probability matrix: it
-// recomputes each tile on chip from Q, K and the saved per-row statistic
-// lse (michaelc-yu summary of Dao et al., "Backward / recomputation"):
-//   P_ij  = exp(scale q_i.k_j - lse_i)
-//   dP_ij = dO_i . v_j,  D_i = dO_i . O_i,  dS_ij = P_ij (dP_ij - D_i)
-//   dV_j  = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j
-// (the chain rule through the softmax; D_i = sum_j P_ij dP_ij equals dO_i . O_i).
+// recomputes each tile on chip from Q, K and the per-row statistic lse that
+// the forward saved (michaelc-yu summary of Dao et al., "Backward /
+// recomputation"). With S = scale Q K^T and L = sum(dO * O), the chain rule
+// through the row softmax gives
+//   P_ij  = exp(S_ij - lse_i)
+//   dP_ij = dO_i . v_j,   D_i = dO_i . O_i  (= sum_j P_ij dP_ij)
+//   dS_ij = P_ij (dP_ij - D_i)
+//   dV_j  = sum_i P_ij dO_i,   dK_j = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j
 //
-// Kernels, all on the caller's stream:
-//  1. bwd_pre: D_i = dO_i . O_i in fp32 (and, for atomic dQ, zero the fp32 dQ
-//     accumulator).
-//  2. bwd_main: one workgroup per (batch*head, block of 128 keys); each of its
-//     4 waves owns 32 keys and keeps their K and V rows in VGPRs and their dK, dV
-//     in fp32 accumulators for the whole kernel. It walks 32-query tiles (causal:
-//     only tiles at or below the diagonal) staged through LDS, forming
-//       S = Q K^T and dP = dO V^T            (MFMA, lane = key, 16 queries each)
-//       dV^T += dO^T P and dK^T += Q^T dS    (MFMA; dO^T, Q^T via ds_read_b64_tr_b16)
-//     With atomic dQ, dS^T goes to LDS and the 4 waves compute the tile's
-//     dQ = dS K (16x16x32 MFMA) and add it to the fp32 accumulator with
-//     global float atomics.
-//  3a. atomic dQ: bwd_dq_convert scales and rounds the accumulator into dq.
-//  3b. separate dQ: bwd_dq, one workgroup per 128 queries, streams K/V blocks
-//     like the forward and forms S^T, dP^T and dQ^T += K^T dS^T in registers.
+// Two launches on the caller's stream:
+//  1. bwd_prep: D_i and lse_i * log2(e) for every query row, into the
+//     workspace (memory bound: reads O and dO once).
+//  2. bwd_fused: one grid holding two kinds of workgroups, which share no
+//     data and run side by side:
+//     * key workgroups (128 keys, 32 per wave): K and V rows of the wave stay
+//       in VGPRs, dK^T and dV^T in fp32 accumulators. Query tiles (Q, dO and
+//       their statistics) stream HBM -> LDS through a 3-stage LDS-DMA ring; per
+//       32 queries a wave forms S = Q K^T and dP = dO V^T (lane = key), then
+//       P and dS in registers, then dV^T += dO^T P and dK^T += Q^T dS with the
+//       dO^T / Q^T operands read transposed from LDS (ds_read_b64_tr_b16).
+//     * query workgroups (128 queries, 32 per wave): Q and dO rows stay in
+//       VGPRs, K and V blocks of 64 keys stream through the same kind of ring
+//       (the forward's layout); a wave forms S^T = K Q^T and dP^T = V dO^T
+//       (lane = query), dS^T in registers, and dQ^T += K^T dS^T with K^T read
+//       transposed from LDS.
+//     Work is handed out longest first, alternating the two kinds, and every
+//     workgroup of one (batch, head) goes to the same XCD so its tensors are
+//     reused from that XCD's L2.
+//  Causal: tiles wholly above the diagonal are skipped; only tiles crossing it
+//  (or the ragged end of the sequence) are masked element by element.
+//
+// The dQ pass recomputes S and dP (7 matrix products in total instead of 5),
+// which on this chip costs less than fp32 atomics for dQ (measured; the atomic
+// strategy lives in fa_bwd_atomic.hip).
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -31,37 +44,69 @@ namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBkv = 128;  // keys per workgroup of bwd_main (32 per wave)
-constexpr int kBq = 32;    // queries per step of bwd_main
+constexpr int D = 64;          // head dim of the backward
+constexpr int KS = D / 16;     // k-steps over the head dim (32x32x16 MFMA)
+constexpr int DT = D / 32;     // 32-wide tiles of the head dim
+constexpr int CH = D / 8;      // 16-byte chunks per row
+constexpr int kRowB = 2 * D;   // bytes per tile row
 
-struct BwdArgs {
+// key workgroups
+constexpr int kKvKeys = 128;                 // keys per workgroup (32 per wave)
+#ifndef FA_BWD_QH
+#define FA_BWD_QH 2
+#endif
+constexpr int QH = FA_BWD_QH;                // 32-query halves per ring stage
+constexpr int kKvQRows = 32 * QH;            // query rows per ring stage
+constexpr int kKvTileB = kKvQRows * kRowB;   // bytes of the Q (or dO) part of a stage
+constexpr int kKvStatB = 256;                // 64 floats of lse*log2e, then 64 of D
+constexpr int kKvStage = 2 * kKvTileB + 2 * kKvStatB;
+constexpr int kKvCpw = 2 * (kKvTileB / 1024) / 4;  // 16-byte DMA instructions per wave per stage
+
+// query workgroups
+constexpr int kQRows = 128;                  // queries per workgroup (32 per wave)
+constexpr int kQKeys = 64;                   // keys per ring stage
+constexpr int kQTileB = kQKeys * kRowB;      // bytes of the K (or V) part of a stage
+constexpr int kQStage = 2 * kQTileB;
+constexpr int kQCpw = 2 * (kQTileB / 1024) / 4;
+
+constexpr int kStages = 3;
+constexpr int kSmem = kStages * (kKvStage > kQStage ? kKvStage : kQStage);
+
+struct FusedArgs {
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* v;
-    const uint16_t* o;
     const uint16_t* dout;
-    const float* lse;
+    const float* lse2;   // lse * log2(e), [BH][N]
+    const float* delta;  // D, [BH][N]
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
-    float* delta;
-    float* dq_acc;
     int BH, N;
-    int nblk;           // workgroups per head along the sequence
+    int nblk;           // workgroups of each kind per head (ceil(N / 128))
     int heads_per_xcd;  // > 0: XCD-aware mapping
     float c;            // scale * log2(e)
     float scale;
 };
 
-// ---------------------------------------------------------------- 1. prologue
-template <typename T, int D, bool ZERO_ACC>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
-    constexpr int LPR = D / 8;               // lanes per row, 8 elements each
-    constexpr int RPB = kThreads / LPR;      // rows per workgroup
+struct PrepArgs {
+    const uint16_t* o;
+    const uint16_t* dout;
+    const float* lse;
+    float* delta;
+    float* lse2;
+    int64_t rows;
+};
+
+// ---------------------------------------------------------------- 1. prep
+// 8 lanes per row, 8 elements each; 32 rows per workgroup.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(PrepArgs a) {
+    constexpr int LPR = D / 8;
+    constexpr int RPB = kThreads / LPR;
     const int tid = threadIdx.x, part = tid % LPR;
-    const int64_t rows = (int64_t)a.BH * a.N;
     const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
-    const int64_t r = row < rows ? row : rows - 1;
+    const int64_t r = row < a.rows ? row : a.rows - 1;
     const u32x4 ov = *reinterpret_cast<const u32x4*>(a.o + r * D + part * 8);
     const u32x4 dv = *reinterpret_cast<const u32x4*>(a.dout + r * D + part * 8);
     float acc = 0.f;
@@ -72,17 +117,17 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (row < rows) {
+    if (row < a.rows) {
         if (part == 0) a.delta[row] = acc;
-        if (ZERO_ACC) {
-            float4* p = reinterpret_cast<float4*>(a.dq_acc + row * D + part * 8);
-            p[0] = float4{0.f, 0.f, 0.f, 0.f};
-            p[1] = float4{0.f, 0.f, 0.f, 0.f};
-        }
+        if (part == 1) a.lse2[row] = a.lse[row] * kLog2e;
     }
 }
 
-__device__ __forceinline__ void map_block(int bid, const BwdArgs& a, bool longest_first_low, int& bh, int& blk) {
+// ---------------------------------------------------------------- 2. fused
+// Workgroup -> (head, kind, block). Slot s of a head alternates key and query
+// workgroups; within each kind the longest runs first (causal: key block 0 and
+// the last query block see the most tiles).
+__device__ __forceinline__ void map_fused(int bid, const FusedArgs& a, bool causal, int& bh, bool& is_q, int& blk) {
     int s;
     if (a.heads_per_xcd > 0) {
         const int xcd = bid & 7, slot = bid >> 3;
@@ -92,136 +137,156 @@ __device__ __forceinline__ void map_block(int bid, const BwdArgs& a, bool longes
         s = bid / a.BH;
         bh = bid % a.BH;
     }
-    blk = longest_first_low ? s : a.nblk - 1 - s;
+    is_q = s & 1;
+    const int i = s >> 1;
+    blk = is_q ? (causal ? a.nblk - 1 - i : i) : i;
 }
 
-// Byte offset of 16-byte chunk `chunk` (of 4) of key row `r` in the dS^T tile
-// ([128 keys][32 queries] 16-bit); the XOR keeps both the per-key writes and the
-// transposed reads free of bank conflicts.
-__device__ __forceinline__ int dst_off(int r, int chunk) { return r * 64 + ((chunk ^ ((r >> 2) & 3)) << 4); }
-
-// ---------------------------------------------------------------- 2. main kernel
-template <typename T, int D, bool CAUSAL, bool DQ_ATOMIC>
-__global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
-    static_assert(D == 64, "bwd_main is written for head dim 64");
-    constexpr int KS = D / 16, DT = D / 32, CH = D / 8;
-    constexpr int QT = kBq * D * 2;                 // bytes of one staged Q or dO tile
-    constexpr int STAT = 2 * QT;                    // lse*log2e [32] then D [32], floats
-    constexpr int BUF = 2 * QT + 2 * kBq * 4;
-    constexpr int DST = 2 * BUF;
-    constexpr int LDS = DST + (DQ_ATOMIC ? kBkv * kBq * 2 : 0);
-    __shared__ __attribute__((aligned(16))) char smem[LDS];
-
+// Key workgroup: dK and dV of 128 keys.
+template <typename T, bool CAUSAL>
+__device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
-    int bh, kb;
-    map_block(blockIdx.x, a, /*longest_first_low=*/CAUSAL, bh, kb);
     const int N = a.N;
     const size_t head = (size_t)bh * N * D;
     const uint16_t* __restrict__ Q = a.q + head;
-    const uint16_t* __restrict__ K = a.k + head;
-    const uint16_t* __restrict__ V = a.v + head;
     const uint16_t* __restrict__ dO = a.dout + head;
-    const float* __restrict__ lse = a.lse + (size_t)bh * N;
+    const float* __restrict__ lse2 = a.lse2 + (size_t)bh * N;
     const float* __restrict__ delta = a.delta + (size_t)bh * N;
 
-    const int kw0 = kb * kBkv + wave * 32;   // first key of this wave
-    const int key = kw0 + l32;               // key owned by this lane (and lane ^ 32)
-    u32x4 kf[KS], vf[KS];
-    {
-        const size_t kr = (size_t)min(key, N - 1) * D + 8 * h;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            kf[ks] = *reinterpret_cast<const u32x4*>(K + kr + 16 * ks);
-            vf[ks] = *reinterpret_cast<const u32x4*>(V + kr + 16 * ks);
-        }
-    }
-    // B operand of dQ = dS K (16x16x32): K[keys 32ks + 8 g16 + e][dim 16 wave + L16]
-    u32x4 ktf[DQ_ATOMIC ? 4 : 1];
-    const int dq_dim = 16 * wave + L16;
-    if constexpr (DQ_ATOMIC) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            uint16_t x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                x[e] = K[(size_t)min(kb * kBkv + 32 * ks + 8 * g16 + e, N - 1) * D + dq_dim];
-            ktf[ks] = u32x4{x[0] | ((uint32_t)x[1] << 16), x[2] | ((uint32_t)x[3] << 16),
-                            x[4] | ((uint32_t)x[5] << 16), x[6] | ((uint32_t)x[7] << 16)};
-        }
-    }
-
+    const int kw0 = kb * kKvKeys + wave * 32;  // first key of this wave
+    const int key = kw0 + l32;                 // key of this lane (and of lane ^ 32)
     f32x16 dk[DT], dv[DT];
 #pragma unroll
     for (int u = 0; u < DT; ++u) { dk[u] = f32x16{}; dv[u] = f32x16{}; }
 
-    const int nqt = (N + kBq - 1) / kBq;
-    const int t0 = CAUSAL ? (kb * kBkv) / kBq : 0;
+    const int ng = (N + kKvQRows - 1) / kKvQRows;          // query groups of kKvQRows rows
+    const int g0 = CAUSAL ? (kb * kKvKeys) / kKvQRows : 0;  // first group touching these keys
 
-    // staging of one query tile: 32 rows of Q and dO (one 16-byte chunk per thread)
-    // plus lse*log2e and D for its 32 rows
-    const int st_r = tid / CH, st_c = tid % CH;
-    u32x4 qreg, doreg;
-    float sreg = 0.f;
-    auto gload = [&](int t) {
-        const size_t g = (size_t)min(t * kBq + st_r, N - 1) * D + st_c * 8;
-        qreg = *reinterpret_cast<const u32x4*>(Q + g);
-        doreg = *reinterpret_cast<const u32x4*>(dO + g);
-        if (tid < kBq) sreg = lse[min(t * kBq + tid, N - 1)] * kLog2e;
-        else if (tid < 2 * kBq) sreg = delta[min(t * kBq + tid - kBq, N - 1)];
+    // Ring stage layout: [Q rows][dO rows][lse2 x64][D x64]. Chunk j (1 KiB) of
+    // the Q/dO part is written by wave j % 4; lane l of it carries tile row
+    // 8 (j % (kKvTileB/1024)) + l / 8, stored chunk l % 8.
+    auto issue = [&](int g, int st) {
+        char* sb = smem + st * kKvStage;
+        const int r0 = g * kKvQRows;
+#pragma unroll
+        for (int u = 0; u < kKvCpw; ++u) {
+            const int chunk = u * 4 + wave;
+            constexpr int TC = kKvTileB / 1024;
+            const int p = (chunk % TC) * 64 + lane;
+            const int r = p / CH, c = (p % CH) ^ swz<D>(r);
+            const uint16_t* src = (chunk < TC ? Q : dO) + (size_t)min(r0 + r, N - 1) * D + c * 8;
+            dma16(src, sb + chunk * 1024);
+        }
+        if (wave < 2) {
+            const float* src = (wave == 0 ? lse2 : delta) + min(r0 + lane, N - 1);
+            dma4(src, sb + 2 * kKvTileB + wave * kKvStatB);
+        }
     };
-    auto swrite = [&](int buf) {
-        char* base = smem + buf * BUF;
-        lds_write16(base, tile_off<D>(st_r, st_c), qreg);
-        lds_write16(base + QT, tile_off<D>(st_r, st_c), doreg);
-        if (tid < 2 * kBq) reinterpret_cast<float*>(base + STAT)[tid] = sreg;
-    };
 
-    if (t0 < nqt) {
-        gload(t0);
-        swrite(0);
-    }
-    __syncthreads();
-
+    // Transposed-read addresses (relative to a stage): lane L of 16-lane group g
+    // reads row 8h + L/4 (+4 for the upper half of the operand), columns
+    // 32u + 16(g&1) + 4(L&3) of the Q or dO rows; query chunks add 16 rows.
+    uint32_t tr_off[DT][2];
+#pragma unroll
+    for (int u = 0; u < DT; ++u)
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi)
+            tr_off[u][hi] = (uint32_t)(tile_off<D>(8 * h + (L16 >> 2) + 4 * hi,
+                                                   (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
+                                       (L16 & 1) * 8);
     const int s_row = perm32(l32);
-    const int tr_row = 8 * h + (L16 >> 2);
-    const int tr_col = 16 * (g16 & 1) + 4 * (L16 & 3);
-    const int tr_half = (L16 & 1) * 8;
+    uint32_t a_off[KS];  // Q / dO operand rows for S and dP, k-step ks
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a_off[ks] = (uint32_t)tile_off<D>(s_row, 2 * ks + h);
+    const uint32_t smem_addr = lds_addr(smem);
 
-    for (int t = t0; t < nqt; ++t) {
-        const int buf = (t - t0) & 1;
-        const char* qs = smem + buf * BUF;
-        const char* dos = qs + QT;
-        const float* st = reinterpret_cast<const float*>(qs + STAT);
-        if (t + 1 < nqt) gload(t + 1);
-        const int qt0 = t * kBq;
-        const bool active = kw0 < N && (!CAUSAL || kw0 <= qt0 + kBq - 1);
-        if (active) {
+    if (g0 < ng) issue(g0, 0);
+    if (g0 + 1 < ng) issue(g0 + 1, 1);
+    // K and V rows: B operands of S = Q K^T and dP = dO V^T (k = head dim).
+    // Loaded after the first ring stages are requested so the latencies overlap;
+    // the full wait then tells the compiler's wait pass that no load into a
+    // register is pending inside the loop (else it drains the ring there).
+    u32x4 kf[KS], vf[KS];
+    {
+        const size_t kr = head + (size_t)min(key, N - 1) * D + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            kf[ks] = *reinterpret_cast<const u32x4*>(a.k + kr + 16 * ks);
+            vf[ks] = *reinterpret_cast<const u32x4*>(a.v + kr + 16 * ks);
+        }
+    }
+    wait_vmcnt<0>();
+
+    int st = 0;
+    for (int g = g0; g < ng; ++g) {
+        if (g + 1 < ng) {
+            if (wave < 2) wait_vmcnt<kKvCpw + 1>();
+            else wait_vmcnt<kKvCpw>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        barrier();
+        if (g + 2 < ng) issue(g + 2, st == 0 ? 2 : st - 1);
+        const uint32_t sbase = smem_addr + (uint32_t)(st * kKvStage);
+#pragma unroll
+        for (int hh = 0; hh < QH; ++hh) {
+            const int qt0 = g * kKvQRows + 32 * hh;
+            const bool active = kw0 < N && qt0 < N && (!CAUSAL || qt0 + 31 >= kw0);
+            if (!active) continue;
+            const uint32_t qb = sbase + (uint32_t)(hh * 32 * kRowB);
+            const uint32_t db = qb + (uint32_t)kKvTileB;
+            // ---- S = Q K^T, dP = dO V^T (32 queries x 32 keys; lane = key)
+            u32x4 qa[KS], da[KS];
+            qa[0] = ds_read128<0>(qb + a_off[0]);
+            qa[1] = ds_read128<0>(qb + a_off[1]);
+            qa[2] = ds_read128<0>(qb + a_off[2]);
+            qa[3] = ds_read128<0>(qb + a_off[3]);
+            da[0] = ds_read128<0>(db + a_off[0]);
+            da[1] = ds_read128<0>(db + a_off[1]);
+            da[2] = ds_read128<0>(db + a_off[2]);
+            da[3] = ds_read128<0>(db + a_off[3]);
+            // statistics of this lane's 16 queries: 8h + 0..7 and 16 + 8h + 0..7
+            const uint32_t stb = sbase + (uint32_t)(2 * kKvTileB + 4 * (32 * hh + 8 * h));
+            f32x4 lv[4], dl[4];
+            lv[0] = ds_read128f<0>(stb);
+            lv[1] = ds_read128f<16>(stb);
+            lv[2] = ds_read128f<64>(stb);
+            lv[3] = ds_read128f<80>(stb);
+            dl[0] = ds_read128f<kKvStatB>(stb);
+            dl[1] = ds_read128f<kKvStatB + 16>(stb);
+            dl[2] = ds_read128f<kKvStatB + 64>(stb);
+            dl[3] = ds_read128f<kKvStatB + 80>(stb);
+            lgkm_wait<8>();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) { settle(qa[ks]); settle(da[ks]); }
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 qa = lds_read16(qs, tile_off<D>(s_row, 2 * ks + h));
-                const u32x4 da = lds_read16(dos, tile_off<D>(s_row, 2 * ks + h));
-                s = T::mfma32(qa, kf[ks], s);
-                dp = T::mfma32(da, vf[ks], dp);
+                s = T::mfma32(qa[ks], kf[ks], s);
+                dp = T::mfma32(da[ks], vf[ks], dp);
             }
-            // statistics of this lane's 16 queries: 8h + 0..7 and 16 + 8h + 0..7
-            float lv[16], dl[16];
+            lgkm_wait<0>();
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const f32x4 l0 = *reinterpret_cast<const f32x4*>(st + 16 * half + 8 * h);
-                const f32x4 l1 = *reinterpret_cast<const f32x4*>(st + 16 * half + 8 * h + 4);
-                const f32x4 d0 = *reinterpret_cast<const f32x4*>(st + kBq + 16 * half + 8 * h);
-                const f32x4 d1 = *reinterpret_cast<const f32x4*>(st + kBq + 16 * half + 8 * h + 4);
+            for (int j = 0; j < 4; ++j) { settle(lv[j]); settle(dl[j]); }
+            // transposed operands for dV^T += dO^T P and dK^T += Q^T dS, issued
+            // now so they land during the elementwise work
+            u32x2 dtr[2][DT][2], qtr[2][DT][2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    lv[8 * half + e] = l0[e];
-                    lv[8 * half + 4 + e] = l1[e];
-                    dl[8 * half + e] = d0[e];
-                    dl[8 * half + 4 + e] = d1[e];
-                }
-            }
-            const bool need_mask = (CAUSAL && kw0 + 31 > qt0) || kw0 + 32 > N || qt0 + kBq > N;
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int u = 0; u < DT; ++u)
+#pragma unroll
+                    for (int hi = 0; hi < 2; ++hi) {
+                        if (c == 0) {
+                            dtr[c][u][hi] = tr_read<0>(db + tr_off[u][hi]);
+                            qtr[c][u][hi] = tr_read<0>(qb + tr_off[u][hi]);
+                        } else {
+                            dtr[c][u][hi] = tr_read<16 * kRowB>(db + tr_off[u][hi]);
+                            qtr[c][u][hi] = tr_read<16 * kRowB>(qb + tr_off[u][hi]);
+                        }
+                    }
+            const bool need_mask = (CAUSAL && kw0 + 31 > qt0) || kw0 + 32 > N || qt0 + 32 > N;
             uint32_t pw[8], dsw[8];
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
@@ -229,70 +294,39 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int i = 2 * w + e;
-                    float pv = fast_exp2(__builtin_fmaf(s[i], a.c, -lv[i]));
+                    const float l2 = lv[i >> 2][i & 3];
+                    float pv = fast_exp2(__builtin_fmaf(s[i], a.c, -l2));
                     if (need_mask) {
                         const int qi = qt0 + 16 * (i >> 3) + 8 * h + (i & 7);
                         if ((CAUSAL && key > qi) || key >= N || qi >= N) pv = 0.f;
                     }
                     p[e] = pv;
-                    ds[e] = pv * (dp[i] - dl[i]);
+                    ds[e] = pv * (dp[i] - dl[i >> 2][i & 3]);
                 }
                 pw[w] = T::pack2(p[0], p[1]);
                 dsw[w] = T::pack2(ds[0], ds[1]);
             }
+            lgkm_wait<0>();
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int u = 0; u < DT; ++u)
+#pragma unroll
+                    for (int hi = 0; hi < 2; ++hi) { settle(dtr[c][u][hi]); settle(qtr[c][u][hi]); }
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const u32x4 pc = {pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]};
                 const u32x4 sc = {dsw[4 * c], dsw[4 * c + 1], dsw[4 * c + 2], dsw[4 * c + 3]};
-                const int row = 16 * c + tr_row;
 #pragma unroll
                 for (int u = 0; u < DT; ++u) {
-                    const int col = 32 * u + tr_col;
-                    const u32x2 d_lo = lds_read_tr(dos, tile_off<D>(row, col >> 3) + tr_half);
-                    const u32x2 d_hi = lds_read_tr(dos, tile_off<D>(row + 4, col >> 3) + tr_half);
-                    const u32x2 q_lo = lds_read_tr(qs, tile_off<D>(row, col >> 3) + tr_half);
-                    const u32x2 q_hi = lds_read_tr(qs, tile_off<D>(row + 4, col >> 3) + tr_half);
-                    dv[u] = T::mfma32(u32x4{d_lo[0], d_lo[1], d_hi[0], d_hi[1]}, pc, dv[u]);
-                    dk[u] = T::mfma32(u32x4{q_lo[0], q_lo[1], q_hi[0], q_hi[1]}, sc, dk[u]);
-                }
-            }
-            if constexpr (DQ_ATOMIC) {
-                char* dst = smem + DST;
-                const int r = 32 * wave + l32;
-                lds_write16(dst, dst_off(r, h), u32x4{dsw[0], dsw[1], dsw[2], dsw[3]});
-                lds_write16(dst, dst_off(r, 2 + h), u32x4{dsw[4], dsw[5], dsw[6], dsw[7]});
-            }
-        }
-        if constexpr (DQ_ATOMIC) {
-            __syncthreads();
-            const char* dst = smem + DST;
-#pragma unroll
-            for (int qh = 0; qh < 2; ++qh) {
-                f32x4 acc = f32x4{};
-                bool any = false;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const int kwk = kb * kBkv + 32 * ks;
-                    if (kwk < N && (!CAUSAL || kwk <= qt0 + kBq - 1)) {
-                        const int row = 32 * ks + 8 * g16 + (L16 >> 2);
-                        const int col = 16 * qh + 4 * (L16 & 3);
-                        const u32x2 lo = lds_read_tr(dst, dst_off(row, col >> 3) + tr_half);
-                        const u32x2 hi = lds_read_tr(dst, dst_off(row + 4, col >> 3) + tr_half);
-                        acc = T::mfma16(u32x4{lo[0], lo[1], hi[0], hi[1]}, ktf[ks], acc);
-                        any = true;
-                    }
-                }
-                if (any) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int qi = qt0 + 16 * qh + 4 * g16 + i;
-                        if (qi < N) unsafeAtomicAdd(a.dq_acc + ((size_t)bh * N + qi) * D + dq_dim, acc[i]);
-                    }
+                    const u32x4 dA = {dtr[c][u][0][0], dtr[c][u][0][1], dtr[c][u][1][0], dtr[c][u][1][1]};
+                    const u32x4 qA = {qtr[c][u][0][0], qtr[c][u][0][1], qtr[c][u][1][0], qtr[c][u][1][1]};
+                    dv[u] = T::mfma32(dA, pc, dv[u]);
+                    dk[u] = T::mfma32(qA, sc, dk[u]);
                 }
             }
         }
-        if (t + 1 < nqt) swrite(buf ^ 1);
-        __syncthreads();
+        st = st == 2 ? 0 : st + 1;
     }
 
     if (key < N) {
@@ -301,55 +335,74 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int u = 0; u < DT; ++u) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int i = 4 * g;
-                *reinterpret_cast<u32x2*>(dkp + 32 * u + 8 * g) =
+            for (int gg = 0; gg < 4; ++gg) {
+                const int i = 4 * gg;
+                *reinterpret_cast<u32x2*>(dkp + 32 * u + 8 * gg) =
                     u32x2{T::pack2(dk[u][i] * a.scale, dk[u][i + 1] * a.scale),
                           T::pack2(dk[u][i + 2] * a.scale, dk[u][i + 3] * a.scale)};
-                *reinterpret_cast<u32x2*>(dvp + 32 * u + 8 * g) =
+                *reinterpret_cast<u32x2*>(dvp + 32 * u + 8 * gg) =
                     u32x2{T::pack2(dv[u][i], dv[u][i + 1]), T::pack2(dv[u][i + 2], dv[u][i + 3])};
             }
         }
     }
 }
 
-// ---------------------------------------------------------------- 3a. dQ convert
-template <typename T>
-__global__ __launch_bounds__(kThreads) void bwd_dq_convert_kernel(const float* __restrict__ acc,
-                                                                  uint16_t* __restrict__ dq, int64_t n8,
-                                                                  float scale) {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= n8) return;
-    const float4 x0 = reinterpret_cast<const float4*>(acc)[2 * i];
-    const float4 x1 = reinterpret_cast<const float4*>(acc)[2 * i + 1];
-    reinterpret_cast<u32x4*>(dq)[i] = u32x4{T::pack2(x0.x * scale, x0.y * scale), T::pack2(x0.z * scale, x0.w * scale),
-                                            T::pack2(x1.x * scale, x1.y * scale), T::pack2(x1.z * scale, x1.w * scale)};
-}
-
-// ---------------------------------------------------------------- 3b. separate dQ kernel
-constexpr int kDqBr = 128;  // queries per workgroup (32 per wave)
-constexpr int kDqBc = 64;   // keys per block
-
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
-    constexpr int KS = D / 16, DT = D / 32, CH = D / 8;
-    constexpr int LPT = kDqBc * CH / kThreads;
-    constexpr int TB = kDqBc * D * 2;
-    __shared__ __attribute__((aligned(16))) char smem[4 * TB];
-
+// Query workgroup: dQ of 128 queries.
+template <typename T, bool CAUSAL>
+__device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int h = lane >> 5, l32 = lane & 31;
-    int bh, qb;
-    map_block(blockIdx.x, a, /*longest_first_low=*/false, bh, qb);
+    const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
     const int N = a.N;
     const size_t head = (size_t)bh * N * D;
     const uint16_t* __restrict__ K = a.k + head;
     const uint16_t* __restrict__ V = a.v + head;
 
-    const int q0 = qb * kDqBr + wave * 32;
+    const int q0 = qb * kQRows + wave * 32;  // first query of this wave
     const int qrow = q0 + l32;
     const bool wave_active = q0 < N;
     const int qload = min(qrow, N - 1);
+
+    const int nkb_all = (N + kQKeys - 1) / kQKeys;
+    const int nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * kQRows) - 1) / kQKeys + 1) : nkb_all;
+
+    f32x16 dqa[DT];
+#pragma unroll
+    for (int u = 0; u < DT; ++u) dqa[u] = f32x16{};
+
+    // Ring stage layout: [K block][V block], each 64 rows in the swizzled layout.
+    auto issue = [&](int kb, int st) {
+        char* sb = smem + st * kQStage;
+#pragma unroll
+        for (int u = 0; u < kQCpw; ++u) {
+            const int chunk = u * 4 + wave;
+            constexpr int TC = kQTileB / 1024;
+            const int p = (chunk % TC) * 64 + lane;
+            const int r = p / CH, c = (p % CH) ^ swz<D>(r);
+            const uint16_t* src = (chunk < TC ? K : V) + (size_t)min(kb * kQKeys + r, N - 1) * D + c * 8;
+            dma16(src, sb + chunk * 1024);
+        }
+    };
+
+    const int s_row = perm32(l32);
+    uint32_t a_off[2][KS];  // K / V operand rows for S^T and dP^T: key tile kt, k-step ks
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a_off[kt][ks] = (uint32_t)tile_off<D>(32 * kt + s_row, 2 * ks + h);
+    uint32_t tr_off[DT][2];  // K^T operand for dQ^T += K^T dS^T; key chunks add 16 rows
+#pragma unroll
+    for (int u = 0; u < DT; ++u)
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi)
+            tr_off[u][hi] = (uint32_t)(tile_off<D>(8 * h + (L16 >> 2) + 4 * hi,
+                                                   (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
+                                       (L16 & 1) * 8);
+    const uint32_t smem_addr = lds_addr(smem);
+
+    issue(0, 0);
+    if (nkb > 1) issue(1, 1);
+    // Q and dO rows: B operands of S^T = K Q^T and dP^T = V dO^T (k = head dim);
+    // loaded and waited for as in the key workgroups.
     u32x4 qf[KS], dof[KS];
     {
         const size_t off = head + (size_t)qload * D + 8 * h;
@@ -359,100 +412,95 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
             dof[ks] = *reinterpret_cast<const u32x4*>(a.dout + off + 16 * ks);
         }
     }
-    const float lse2 = a.lse[(size_t)bh * N + qload] * kLog2e;
-    const float Di = a.delta[(size_t)bh * N + qload];
+    const float l2q = a.lse2[(size_t)bh * N + qload];
+    const float Dq = a.delta[(size_t)bh * N + qload];
+    wait_vmcnt<0>();
 
-    const int nkb_all = (N + kDqBc - 1) / kDqBc;
-    const int nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * kDqBr) - 1) / kDqBc + 1) : nkb_all;
-
-    f32x16 dqa[DT];
-#pragma unroll
-    for (int u = 0; u < DT; ++u) dqa[u] = f32x16{};
-
-    u32x4 kr[LPT], vr[LPT];
-    auto gload = [&](int kb) {
-#pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int x = tid + kThreads * u, r = x / CH, c = x % CH;
-            const size_t g = (size_t)min(kb * kDqBc + r, N - 1) * D + c * 8;
-            kr[u] = *reinterpret_cast<const u32x4*>(K + g);
-            vr[u] = *reinterpret_cast<const u32x4*>(V + g);
-        }
-    };
-    auto swrite = [&](int buf) {
-        char* kb_ = smem + buf * 2 * TB;
-        char* vb_ = kb_ + TB;
-#pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-            const int x = tid + kThreads * u, r = x / CH, c = x % CH;
-            lds_write16(kb_, tile_off<D>(r, c), kr[u]);
-            lds_write16(vb_, tile_off<D>(r, c), vr[u]);
-        }
-    };
-
-    gload(0);
-    swrite(0);
-    __syncthreads();
-
-    const int g16 = lane >> 4, L16 = lane & 15;
-    const int tr_row = 8 * h + (L16 >> 2);
-    const int tr_col = 16 * (g16 & 1) + 4 * (L16 & 3);
-    const int tr_half = (L16 & 1) * 8;
-    const int s_row = perm32(l32);
-
+    int st = 0;
     for (int kb = 0; kb < nkb; ++kb) {
-        const int buf = kb & 1;
-        const char* kbuf = smem + buf * 2 * TB;
-        const char* vbuf = kbuf + TB;
-        if (kb + 1 < nkb) gload(kb + 1);
-        const int key0 = kb * kDqBc;
-        if (wave_active && (!CAUSAL || key0 <= q0 + 31)) {
-            f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+        if (kb + 1 < nkb) wait_vmcnt<kQCpw>();
+        else wait_vmcnt<0>();
+        barrier();
+        if (kb + 2 < nkb) issue(kb + 2, st == 0 ? 2 : st - 1);
+        const uint32_t kbase = smem_addr + (uint32_t)(st * kQStage);
+        const uint32_t vbase = kbase + (uint32_t)kQTileB;
+        st = st == 2 ? 0 : st + 1;
+        const int key0 = kb * kQKeys;
+        if (!wave_active || (CAUSAL && key0 > q0 + 31)) continue;
+
+        // ---- S^T = K Q^T and dP^T = V dO^T (64 keys x 32 queries; lane = query)
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            u32x4 ka[KS], va[KS];
+            ka[0] = ds_read128<0>(kbase + a_off[kt][0]);
+            ka[1] = ds_read128<0>(kbase + a_off[kt][1]);
+            ka[2] = ds_read128<0>(kbase + a_off[kt][2]);
+            ka[3] = ds_read128<0>(kbase + a_off[kt][3]);
+            va[0] = ds_read128<0>(vbase + a_off[kt][0]);
+            va[1] = ds_read128<0>(vbase + a_off[kt][1]);
+            va[2] = ds_read128<0>(vbase + a_off[kt][2]);
+            va[3] = ds_read128<0>(vbase + a_off[kt][3]);
+            lgkm_wait<0>();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) { settle(ka[ks]); settle(va[ks]); }
+            s[kt] = f32x16{};
+            dp[kt] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int off = tile_off<D>(32 * t + s_row, 2 * ks + h);
-                    s[t] = T::mfma32(lds_read16(kbuf, off), qf[ks], s[t]);
-                    dp[t] = T::mfma32(lds_read16(vbuf, off), dof[ks], dp[t]);
-                }
-            }
-            const bool need_mask = (CAUSAL && key0 + kDqBc - 1 > q0) || (key0 + kDqBc > N);
-            uint32_t dsw[2][8];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-#pragma unroll
-                for (int w = 0; w < 8; ++w) {
-                    float ds[2];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int i = 2 * w + e;
-                        float pv = fast_exp2(__builtin_fmaf(s[t][i], a.c, -lse2));
-                        if (need_mask) {
-                            const int kj = key0 + 32 * t + 16 * (i >> 3) + 8 * h + (i & 7);
-                            if ((CAUSAL && kj > qrow) || kj >= N) pv = 0.f;
-                        }
-                        ds[e] = pv * (dp[t][i] - Di);
-                    }
-                    dsw[t][w] = T::pack2(ds[0], ds[1]);
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u32x4 sb = {dsw[c >> 1][4 * (c & 1)], dsw[c >> 1][4 * (c & 1) + 1],
-                                  dsw[c >> 1][4 * (c & 1) + 2], dsw[c >> 1][4 * (c & 1) + 3]};
-                const int row = 16 * c + tr_row;
-#pragma unroll
-                for (int u = 0; u < DT; ++u) {
-                    const int col = 32 * u + tr_col;
-                    const u32x2 lo = lds_read_tr(kbuf, tile_off<D>(row, col >> 3) + tr_half);
-                    const u32x2 hi = lds_read_tr(kbuf, tile_off<D>(row + 4, col >> 3) + tr_half);
-                    dqa[u] = T::mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, sb, dqa[u]);
-                }
+                s[kt] = T::mfma32(ka[ks], qf[ks], s[kt]);
+                dp[kt] = T::mfma32(va[ks], dof[ks], dp[kt]);
             }
         }
-        if (kb + 1 < nkb) swrite(buf ^ 1);
-        __syncthreads();
+        // K^T operands of the whole block, issued before the elementwise work
+        u32x2 ktr[4][DT][2];
+#pragma unroll
+        for (int u = 0; u < DT; ++u)
+#pragma unroll
+            for (int hi = 0; hi < 2; ++hi) {
+                const uint32_t ad = kbase + tr_off[u][hi];
+                ktr[0][u][hi] = tr_read<0 * 16 * kRowB>(ad);
+                ktr[1][u][hi] = tr_read<1 * 16 * kRowB>(ad);
+                ktr[2][u][hi] = tr_read<2 * 16 * kRowB>(ad);
+                ktr[3][u][hi] = tr_read<3 * 16 * kRowB>(ad);
+            }
+        // ---- dS^T = P^T (dP^T - D), P^T = exp2(S^T c - lse2)
+        const bool need_mask = (CAUSAL && key0 + kQKeys - 1 > q0) || (key0 + kQKeys > N);
+        uint32_t dsw[2][8];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                float ds[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int i = 2 * w + e;
+                    float pv = fast_exp2(__builtin_fmaf(s[kt][i], a.c, -l2q));
+                    if (need_mask) {
+                        const int kj = key0 + 32 * kt + 16 * (i >> 3) + 8 * h + (i & 7);
+                        if ((CAUSAL && kj > qrow) || kj >= N) pv = 0.f;
+                    }
+                    ds[e] = pv * (dp[kt][i] - Dq);
+                }
+                dsw[kt][w] = T::pack2(ds[0], ds[1]);
+            }
+        }
+        lgkm_wait<0>();
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int u = 0; u < DT; ++u) { settle(ktr[c][u][0]); settle(ktr[c][u][1]); }
+        // ---- dQ^T (64 dims x 32 queries) += K^T dS^T over four 16-key chunks
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 sb = {dsw[c >> 1][4 * (c & 1)], dsw[c >> 1][4 * (c & 1) + 1],
+                              dsw[c >> 1][4 * (c & 1) + 2], dsw[c >> 1][4 * (c & 1) + 3]};
+#pragma unroll
+            for (int u = 0; u < DT; ++u) {
+                const u32x4 kA = {ktr[c][u][0][0], ktr[c][u][0][1], ktr[c][u][1][0], ktr[c][u][1][1]};
+                dqa[u] = T::mfma32(kA, sb, dqa[u]);
+            }
+        }
     }
 
     if (wave_active && qrow < N) {
@@ -460,9 +508,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int u = 0; u < DT; ++u) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int i = 4 * g;
-                *reinterpret_cast<u32x2*>(qp + 32 * u + 8 * g) =
+            for (int gg = 0; gg < 4; ++gg) {
+                const int i = 4 * gg;
+                *reinterpret_cast<u32x2*>(qp + 32 * u + 8 * gg) =
                     u32x2{T::pack2(dqa[u][i] * a.scale, dqa[u][i + 1] * a.scale),
                           T::pack2(dqa[u][i + 2] * a.scale, dqa[u][i + 3] * a.scale)};
             }
@@ -470,67 +518,69 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
     }
 }
 
-template <typename T, int D, bool C>
-hipError_t launch_all(BwdArgs a, int dq_mode, hipStream_t stream) {
-    const bool atomic = dq_mode == 1;
-    const int64_t rows = (int64_t)a.BH * a.N;
-    constexpr int RPB = kThreads / (D / 8);
-    const unsigned pre_grid = (unsigned)((rows + RPB - 1) / RPB);
-    if (atomic)
-        hipLaunchKernelGGL((bwd_pre_kernel<T, D, true>), dim3(pre_grid), dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((bwd_pre_kernel<T, D, false>), dim3(pre_grid), dim3(kThreads), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void bwd_fused_kernel(FusedArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+    int bh, blk;
+    bool is_q;
+    map_fused(blockIdx.x, a, CAUSAL, bh, is_q, blk);
+    if (is_q) q_body<T, CAUSAL>(a, bh, blk, smem);
+    else kv_body<T, CAUSAL>(a, bh, blk, smem);
+}
 
-    BwdArgs m = a;
-    m.nblk = (a.N + kBkv - 1) / kBkv;
-    if (atomic)
-        hipLaunchKernelGGL((bwd_main_kernel<T, D, C, true>), dim3(a.BH * m.nblk), dim3(kThreads), 0, stream, m);
+template <typename T>
+hipError_t launch_fused(FusedArgs a, bool causal, hipStream_t stream) {
+    a.nblk = (a.N + kKvKeys - 1) / kKvKeys;
+    static_assert(kKvKeys == kQRows, "both kinds of workgroup cover 128 rows");
+    a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+    const dim3 grid((unsigned)(a.BH * 2 * a.nblk));
+    if (causal)
+        hipLaunchKernelGGL((bwd_fused_kernel<T, true>), grid, dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((bwd_main_kernel<T, D, C, false>), dim3(a.BH * m.nblk), dim3(kThreads), 0, stream, m);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
-    if (atomic) {
-        const int64_t n8 = rows * D / 8;
-        hipLaunchKernelGGL((bwd_dq_convert_kernel<T>), dim3((unsigned)((n8 + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, stream, a.dq_acc, a.dq, n8, a.scale);
-    } else {
-        BwdArgs qarg = a;
-        qarg.nblk = (a.N + kDqBr - 1) / kDqBr;
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D, C>), dim3(a.BH * qarg.nblk), dim3(kThreads), 0, stream, qarg);
-    }
+        hipLaunchKernelGGL((bwd_fused_kernel<T, false>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t bwd_mfma(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                    const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-                    float scale, bool causal, int dtype, int dq_mode, float* delta, float* dq_acc,
-                    hipStream_t stream) {
-    (void)d;  // validated by the caller: 64
-    BwdArgs a;
+hipError_t bwd_prep(const void* o, const void* dout, const float* lse, int B, int H, int N, int dtype, float* delta,
+                    float* lse2, hipStream_t stream) {
+    PrepArgs p;
+    p.o = static_cast<const uint16_t*>(o);
+    p.dout = static_cast<const uint16_t*>(dout);
+    p.lse = lse;
+    p.delta = delta;
+    p.lse2 = lse2;
+    p.rows = (int64_t)B * H * N;
+    constexpr int RPB = kThreads / (D / 8);
+    const dim3 grid((unsigned)((p.rows + RPB - 1) / RPB));
+    if (dtype == 0)
+        hipLaunchKernelGGL((bwd_prep_kernel<Bf16>), grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_prep_kernel<F16>), grid, dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t bwd_fused(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                     const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale, bool causal,
+                     int dtype, hipStream_t stream) {
+    FusedArgs a;
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
-    a.o = static_cast<const uint16_t*>(o);
     a.dout = static_cast<const uint16_t*>(dout);
-    a.lse = lse;
+    a.lse2 = lse2;
+    a.delta = delta;
     a.dq = static_cast<uint16_t*>(dq);
     a.dk = static_cast<uint16_t*>(dk);
     a.dv = static_cast<uint16_t*>(dv);
-    a.delta = delta;
-    a.dq_acc = dq_acc;
     a.BH = B * H;
     a.N = N;
     a.nblk = 0;
-    a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+    a.heads_per_xcd = 0;
     a.c = scale * kLog2e;
     a.scale = scale;
-    if (dtype == 0) return causal ? launch_all<Bf16, 64, true>(a, dq_mode, stream) : launch_all<Bf16, 64, false>(a, dq_mode, stream);
-    return causal ? launch_all<F16, 64, true>(a, dq_mode, stream) : launch_all<F16, 64, false>(a, dq_mode, stream);
+    return dtype == 0 ? launch_fused<Bf16>(a, causal, stream) : launch_fused<F16>(a, causal, stream);
 }
 
 }  // namespace fa

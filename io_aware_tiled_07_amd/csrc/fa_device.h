@@ -142,6 +142,45 @@ __device__ __forceinline__ u32x2 tr_read(uint32_t addr) {
     return r;
 }
 
+// ---------------------------------------------------------------- LDS reads hidden from the wait pass
+// The compiler cannot tell an LDS read from the LDS-DMA writes still in
+// flight, so it puts a vmcnt(0) in front of the first use of every read it
+// sees, which drains the prefetch ring. Reads issued from inline asm are
+// invisible to that pass. Their results are NOT covered by any automatic
+// wait: call lgkm_wait<N>() and then settle() on each result before it is
+// used (settle() makes later uses depend on the wait, so the compiler cannot
+// move a use or a copy of the register above it).
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read128(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+template <int OFF>
+__device__ __forceinline__ f32x4 ds_read128f(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+    f32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+// s_waitcnt lgkmcnt(N): at most N LDS (or scalar-memory) operations of this
+// wave still outstanding; LDS operations complete in issue order.
+template <int N>
+__device__ __forceinline__ void lgkm_wait() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N) : "memory");
+}
+template <typename X>
+__device__ __forceinline__ void settle(X& x) {
+    asm volatile("" : "+v"(x));
+}
+
+// 4-byte LDS-DMA (global_load_lds_dword): lane l writes lds_base + 4 * l.
+__device__ __forceinline__ void dma4(const void* src, char* lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
 // LDS byte address of a pointer into __shared__ memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);

@@ -12,12 +12,21 @@ namespace fa {
 hipError_t fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                     int N, int d, float scale, bool causal, int dtype, hipStream_t stream);
 
-// 16-bit backward. dq_mode: 1 = fp32 atomics into dq_acc then convert, 2 = separate dQ kernel.
-// delta: [B,H,N] float scratch, dq_acc: [B,H,N,d] float scratch (atomic mode only).
-hipError_t bwd_mfma(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                    const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
-                    float scale, bool causal, int dtype, int dq_mode, float* delta, float* dq_acc,
-                    hipStream_t stream);
+// 16-bit backward, default strategy: D_i = dO_i . O_i and lse_i * log2(e)
+// into delta / lse2 ([B,H,N] float each), then one fused launch for dQ, dK, dV.
+hipError_t bwd_prep(const void* o, const void* dout, const float* lse, int B, int H, int N, int dtype, float* delta,
+                    float* lse2, hipStream_t stream);
+hipError_t bwd_fused(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                     const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale, bool causal,
+                     int dtype, hipStream_t stream);
+
+// 16-bit backward with fp32 atomics for dQ: the prologue computes delta and
+// zeroes dq_acc ([B,H,N,64] float); the main step adds into dq_acc and converts.
+hipError_t bwd_atomic_prep(const void* o, const void* dout, int B, int H, int N, int dtype, float* delta,
+                           float* dq_acc, hipStream_t stream);
+hipError_t bwd_atomic_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                           void* dq, void* dk, void* dv, int B, int H, int N, float scale, bool causal, int dtype,
+                           const float* delta, float* dq_acc, hipStream_t stream);
 
 // fp32 forward and backward, d = 64.
 hipError_t fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,

@@ -35,7 +35,8 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_workspace_size", "fa_status_string"}
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_prep", "fa_bwd_main",
+                          "fa_bwd_workspace_size", "fa_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -49,8 +50,9 @@ def test_status_strings(lib):
 def test_workspace_size(lib):
     def up(x):
         return (x + 255) // 256 * 256
-    assert fa.fa_bwd_workspace_size(8, 12, 1024, 64, fa.FA_BF16) == up(8 * 12 * 1024 * 4) + up(8 * 12 * 1024 * 64 * 4)
-    assert fa.fa_bwd_workspace_size(1, 1, 7, 64, fa.FA_FP32) == up(7 * 4)
+    rows = 8 * 12 * 1024
+    assert fa.fa_bwd_workspace_size(8, 12, 1024, 64, fa.FA_BF16) == 2 * up(rows * 4) + up(rows * 64 * 4)
+    assert fa.fa_bwd_workspace_size(1, 1, 7, 64, fa.FA_FP32) == 2 * up(7 * 4)
     assert fa.fa_bwd_workspace_size(0, 1, 7, 64, fa.FA_BF16) == 0
     assert fa.fa_bwd_workspace_size(1, 1, 7, 64, 9) == 0
 
@@ -106,6 +108,7 @@ def bwd(lib, B=2, H=3, N=100, d=64, scale=0.125, causal=0, dtype=0, strategy=0, 
     (dict(ws=0), fa.FA_ERR_WORKSPACE),
     (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE),
     (dict(ws=A + 9 * GAP + 4), fa.FA_ERR_WORKSPACE),  # misaligned workspace
+    (dict(ws=A + 9 * GAP + 128), fa.FA_ERR_WORKSPACE),  # workspace not 256-byte aligned
     (dict(dq=A + 2 * GAP), fa.FA_ERR_INVALID_ARG),    # dq aliases v
     (dict(dv=A + 6 * GAP), fa.FA_ERR_INVALID_ARG),    # dv aliases dq
     (dict(ws=A + 5 * GAP), fa.FA_ERR_INVALID_ARG),    # workspace overlaps lse
@@ -130,3 +133,53 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     with pytest.raises(RuntimeError, match="not built"):
         fa.load()
     importlib.reload(fa)
+
+
+def prep(lib, B=2, H=3, N=100, d=64, dtype=0, strategy=0, o=None, do=None, lse=None, ws=None, ws_bytes=None):
+    p = ptrs(3)
+    need = fa.fa_bwd_workspace_size(B, H, N, d, dtype) if dtype in (0, 1, 2) else 0
+    ws = A + 9 * GAP if ws is None else ws
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    args = [p[0] if o is None else o, p[1] if do is None else do, p[2] if lse is None else lse]
+    return lib.fa_bwd_prep(*[ctypes.c_void_p(x) for x in args], B, H, N, d, dtype, strategy, ctypes.c_void_p(ws),
+                           ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=A + 2 * GAP + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=5), fa.FA_ERR_UNSUPPORTED),
+    (dict(strategy=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=0), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=100), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + GAP), fa.FA_ERR_INVALID_ARG),         # workspace overlaps dout
+])
+def test_prep_rejects(lib, kw, code):
+    assert prep(lib, **kw) == code
+
+
+def test_prep_fp32_is_a_validated_no_op(lib):
+    """For fp32 the first stage only validates (the fp32 backward forms D itself):
+    with valid arguments it returns FA_OK without launching anything."""
+    assert prep(lib, dtype=fa.FA_FP32) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(strategy=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE),
+    (dict(dk=A + 6 * GAP), fa.FA_ERR_INVALID_ARG),    # dk aliases dq
+])
+def test_main_rejects(lib, kw, code):
+    names = ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"]
+    p = dict(zip(names, ptrs(9)))
+    p.update({k: v for k, v in kw.items() if k in names})
+    d = kw.get("d", 64)
+    need = fa.fa_bwd_workspace_size(2, 3, 100, d, 0)
+    ws_bytes = kw.get("ws_bytes", need)
+    st = lib.fa_bwd_main(*[ctypes.c_void_p(p[n]) for n in names], 2, 3, 100, d, ctypes.c_float(0.125), 0, 0,
+                         kw.get("strategy", 0), ctypes.c_void_p(A + 9 * GAP), ctypes.c_size_t(ws_bytes), None)
+    assert st == code

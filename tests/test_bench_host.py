@@ -1,0 +1,39 @@
+"""Host-side pieces of bench.py (no GPU): FLOP and byte accounting, pinned to the
+pages' worked number and to hand arithmetic, and the refusal of more than one GPU."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def test_score_grid_of_the_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "score_count.json")))
+    assert bench.score_entries(g["tokens"]) == g["score_entries"]
+
+
+def test_flop_rule():
+    w = bench.WORKLOADS["gpt2_small_causal"]
+    base = 8 * 12 * 1024 ** 2 * 64
+    assert bench.flops(w, "fwd") == 4 * base / 2
+    assert bench.flops(w, "step") == 10 * base / 2
+    assert bench.flops(bench.WORKLOADS["bert_large"], "fwd") == 4 * 8 * 16 * 512 ** 2 * 64
+
+
+def test_io_bytes():
+    w = bench.WORKLOADS["gpt2_small_causal"]
+    fa_b, std_b = bench.io_bytes(w)
+    heads, N, d = 8 * 12, 1024, 64
+    assert fa_b == heads * (4 * N * d * 2 + 4 * N)         # 50.7 MB
+    assert std_b == heads * (4 * N * d + 4 * N * N) * 2    # 856 MB
+    assert round(std_b / fa_b, 1) == 16.9
+
+
+def test_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr

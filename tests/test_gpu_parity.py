@@ -231,3 +231,22 @@ def test_peak_memory_grows_linearly():
     log(f"  peak bytes {peaks} ratios {ratios}")
     assert all(1.8 <= r <= 2.2 for r in ratios)
     assert peaks[-1] < 16 * 16384 * 16384 * 4 / 10  # far below one fp32 score matrix for all heads
+
+
+def test_staged_backward_matches_fa_bwd():
+    """fa_bwd_prep followed by fa_bwd_main on one stream gives exactly what fa_bwd gives."""
+    drawn = inputs(1003, (2, 3, 300, 64), "bf16")
+    q, k, v, do = to_dev(drawn)
+    o, lse = fa.fwd(q, k, v, causal=True)
+    ref = fa.bwd(q, k, v, o, do, lse, causal=True)
+    for strategy in (fa.FA_DQ_SEPARATE, fa.FA_DQ_ATOMIC):
+        ws = torch.empty(fa.fa_bwd_workspace_size(2, 3, 300, 64, fa.FA_BF16), dtype=torch.uint8, device="cuda")
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        fa.fa_bwd_prep(o, do, lse, ws, strategy)
+        fa.fa_bwd_main(q, k, v, o, do, lse, dq, dk, dv, ws, True, None, strategy)
+        torch.cuda.synchronize()
+        if strategy == fa.FA_DQ_SEPARATE:
+            assert torch.equal(dq, ref[0]) and torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
+        else:
+            assert torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
+            assert (dq.float() - ref[0].float()).abs().max().item() < 2e-2

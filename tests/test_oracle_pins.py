@@ -10,7 +10,9 @@ in the michaelc-yu summary ("What FlashAttention targets"). The backward is
 the chain rule through that definition ("Backward / recomputation" names it
 only).
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -95,36 +97,29 @@ def test_single_token():
     np.testing.assert_allclose(lse, 0.25 * np.einsum("bhnd,bhnd->bhn", q, k), rtol=0, atol=1e-14)
 
 
-def test_hand_worked_two_tokens():
-    """A 2-token, 1-dim head solved by hand.
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
-    q = [ln 3, 0], k = [1, 0], v = [4, 8], scale = 1, dO = [1, 0].
-    Scores: row 0 = [ln 3, 0], row 1 = [0, 0].
-    Non-causal: P_0 = [3/4, 1/4], P_1 = [1/2, 1/2]; O = [5, 6]; lse = [ln 4, ln 2].
-    Causal: P_0 = [1, 0], P_1 = [1/2, 1/2]; O = [4, 6]; lse = [ln 3, ln 2].
-    Backward of L = O_0 (non-causal): dV = P_0 = [3/4, 1/4]; dP_0 = [4, 8];
-    D_0 = 3 + 2 = 5 = dO_0 O_0; dS_0 = P_0 (dP_0 - 5) = [-3/4, 3/4];
-    dQ_0 = -3/4 * 1 + 3/4 * 0 = -3/4; dQ_1 = 0; dK = dS_0 * q_0 = [-3/4 ln 3, 3/4 ln 3].
-    Causal: only key 0 is visible to row 0, so dS_0 = 0 and dQ = dK = 0, dV = [1, 0].
-    """
-    L3 = math.log(3.0)
-    q = np.array([L3, 0.0]).reshape(1, 1, 2, 1)
-    k = np.array([1.0, 0.0]).reshape(1, 1, 2, 1)
-    v = np.array([4.0, 8.0]).reshape(1, 1, 2, 1)
-    do = np.array([1.0, 0.0]).reshape(1, 1, 2, 1)
-    r = oracle.bwd(q, k, v, do, 1.0, False)
-    np.testing.assert_allclose(r["o"].ravel(), [5.0, 6.0], atol=1e-15)
-    np.testing.assert_allclose(r["lse"].ravel(), [math.log(4.0), math.log(2.0)], atol=1e-15)
-    np.testing.assert_allclose(r["dv"].ravel(), [0.75, 0.25], atol=1e-15)
-    np.testing.assert_allclose(r["dq"].ravel(), [-0.75, 0.0], atol=1e-15)
-    np.testing.assert_allclose(r["dk"].ravel(), [-0.75 * L3, 0.75 * L3], atol=1e-15)
-    np.testing.assert_allclose(r["D_pdp"].ravel(), [5.0, 0.0], atol=1e-14)
-    rc = oracle.bwd(q, k, v, do, 1.0, True)
-    np.testing.assert_allclose(rc["o"].ravel(), [4.0, 6.0], atol=1e-15)
-    np.testing.assert_allclose(rc["lse"].ravel(), [L3, math.log(2.0)], atol=1e-15)
-    np.testing.assert_allclose(rc["dv"].ravel(), [1.0, 0.0], atol=1e-15)
-    np.testing.assert_allclose(rc["dq"].ravel(), [0.0, 0.0], atol=1e-15)
-    np.testing.assert_allclose(rc["dk"].ravel(), [0.0, 0.0], atol=1e-15)
+
+def _golden_value(x):
+    """Fixture numbers are floats or short expressions in ln2 / ln3 / ln4."""
+    if isinstance(x, (int, float)):
+        return float(x)
+    env = {"ln2": math.log(2.0), "ln3": math.log(3.0), "ln4": math.log(4.0)}
+    return float(eval(x, {"__builtins__": {}}, env))
+
+
+def test_hand_worked_two_tokens():
+    """A 2-token, 1-dim head solved by hand (tests/golden/two_token.json holds the derivation)."""
+    g = json.load(open(os.path.join(GOLDEN, "two_token.json")))
+    inp = {k: np.array([_golden_value(x) for x in v]).reshape(1, 1, 2, 1)
+           for k, v in g["inputs"].items() if k != "scale"}
+    for causal, exp in ((False, g["noncausal"]), (True, g["causal"])):
+        r = oracle.bwd(inp["q"], inp["k"], inp["v"], inp["dout"], g["inputs"]["scale"], causal)
+        for name in ("o", "lse", "dv", "dq", "dk"):
+            np.testing.assert_allclose(r[name].ravel(), [_golden_value(x) for x in exp[name]], atol=1e-14,
+                                       err_msg=f"{name} causal={causal}")
+        if "D" in exp:
+            np.testing.assert_allclose(r["D_pdp"].ravel(), [_golden_value(x) for x in exp["D"]], atol=1e-14)
 
 
 def test_lse_shift():
