@@ -49,6 +49,18 @@ def _compile(src: str, build_dir: str, extra: tuple) -> str:
     return obj
 
 
+def device_asm(src: str, extra_flags=()) -> str:
+    """gfx950 assembly of one source file, compiled with the library's flags."""
+    import tempfile
+    with tempfile.TemporaryDirectory() as tmp:
+        out = os.path.join(tmp, "k.s")
+        cmd = [hipcc()] + flags() + list(extra_flags) + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+        return open(out).read()
+
+
 def build(jobs: int = 4, extra_flags=(), lib_path: str = LIB) -> str:
     """Compile every source and link ``lib_path``. ``extra_flags`` (e.g. -D tuning
     macros) go to every hipcc compile; objects go to a build folder next to the library."""

@@ -43,34 +43,49 @@ namespace fa {
 
 namespace {
 
-constexpr int kThreads = 256;
+#ifndef FA_BWD_NG
+#define FA_BWD_NG 1
+#endif
+constexpr int NG = FA_BWD_NG;       // wave groups per workgroup (they split the long loop)
+constexpr int kWaves = 4 * NG;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPrepThreads = 256;
 constexpr int D = 64;          // head dim of the backward
 constexpr int KS = D / 16;     // k-steps over the head dim (32x32x16 MFMA)
 constexpr int DT = D / 32;     // 32-wide tiles of the head dim
 constexpr int CH = D / 8;      // 16-byte chunks per row
 constexpr int kRowB = 2 * D;   // bytes per tile row
+constexpr int kRingRounds = 3; // rounds of stages held by the ring
 
 // key workgroups
-constexpr int kKvKeys = 128;                 // keys per workgroup (32 per wave)
+constexpr int kKvKeys = 128;                 // keys per workgroup (32 per wave of a group)
 #ifndef FA_BWD_QH
 #define FA_BWD_QH 2
 #endif
 constexpr int QH = FA_BWD_QH;                // 32-query halves per ring stage
 constexpr int kKvQRows = 32 * QH;            // query rows per ring stage
 constexpr int kKvTileB = kKvQRows * kRowB;   // bytes of the Q (or dO) part of a stage
+constexpr int kKvTC = kKvTileB / 1024;       // 1 KiB chunks of that part
 constexpr int kKvStatB = 256;                // 64 floats of lse*log2e, then 64 of D
 constexpr int kKvStage = 2 * kKvTileB + 2 * kKvStatB;
-constexpr int kKvCpw = 2 * (kKvTileB / 1024) / 4;  // 16-byte DMA instructions per wave per stage
+constexpr int kKvRound = NG * kKvStage;      // one round: a stage per wave group
+constexpr int kKvCpw = NG * 2 * kKvTC / kWaves;  // 16-byte DMA instructions per wave per round
+static_assert(kKvCpw * kWaves == NG * 2 * kKvTC, "round must split evenly over the waves");
 
 // query workgroups
-constexpr int kQRows = 128;                  // queries per workgroup (32 per wave)
+constexpr int kQRows = 128;                  // queries per workgroup (32 per wave of a group)
 constexpr int kQKeys = 64;                   // keys per ring stage
 constexpr int kQTileB = kQKeys * kRowB;      // bytes of the K (or V) part of a stage
+constexpr int kQTC = kQTileB / 1024;
 constexpr int kQStage = 2 * kQTileB;
-constexpr int kQCpw = 2 * (kQTileB / 1024) / 4;
+constexpr int kQRound = NG * kQStage;
+constexpr int kQCpw = NG * 2 * kQTC / kWaves;
+static_assert(kQCpw * kWaves == NG * 2 * kQTC, "round must split evenly over the waves");
 
-constexpr int kStages = 3;
-constexpr int kSmem = kStages * (kKvStage > kQStage ? kKvStage : kQStage);
+constexpr int kRingB = kRingRounds * (kKvRound > kQRound ? kKvRound : kQRound);
+// after the loop the ring is reused to add group g > 0's accumulators into group 0's
+constexpr int kMergeB = (NG - 1) * 4 * 64 * 64 * 4;  // 4 waves x 64 floats x 64 lanes per extra group
+constexpr int kSmem = kRingB > kMergeB ? kRingB : kMergeB;
 
 struct FusedArgs {
     const uint16_t* q;
@@ -99,11 +114,11 @@ struct PrepArgs {
 };
 
 // ---------------------------------------------------------------- 1. prep
-// 8 lanes per row, 8 elements each; 32 rows per workgroup.
+// 8 lanes per row, 8 elements each; 32 rows per 256-thread workgroup.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(PrepArgs a) {
     constexpr int LPR = D / 8;
-    constexpr int RPB = kThreads / LPR;
+    constexpr int RPB = kPrepThreads / LPR;
     const int tid = threadIdx.x, part = tid % LPR;
     const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
     const int64_t r = row < a.rows ? row : a.rows - 1;
@@ -142,10 +157,13 @@ __device__ __forceinline__ void map_fused(int bid, const FusedArgs& a, bool caus
     blk = is_q ? (causal ? a.nblk - 1 - i : i) : i;
 }
 
-// Key workgroup: dK and dV of 128 keys.
+// Key workgroup: dK and dV of 128 keys. Wave group grp (waves 4 grp .. 4 grp + 3)
+// takes query stages g0 + grp, g0 + grp + NG, ...; every group's wave wl owns the
+// same 32 keys, and the groups' accumulators are added through LDS at the end.
 template <typename T, bool CAUSAL>
 __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = wave >> 2, wl = wave & 3;
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
     const int N = a.N;
     const size_t head = (size_t)bh * N * D;
@@ -154,33 +172,39 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     const float* __restrict__ lse2 = a.lse2 + (size_t)bh * N;
     const float* __restrict__ delta = a.delta + (size_t)bh * N;
 
-    const int kw0 = kb * kKvKeys + wave * 32;  // first key of this wave
+    const int kw0 = kb * kKvKeys + wl * 32;    // first key of this wave
     const int key = kw0 + l32;                 // key of this lane (and of lane ^ 32)
     f32x16 dk[DT], dv[DT];
 #pragma unroll
     for (int u = 0; u < DT; ++u) { dk[u] = f32x16{}; dv[u] = f32x16{}; }
 
-    const int ng = (N + kKvQRows - 1) / kKvQRows;          // query groups of kKvQRows rows
-    const int g0 = CAUSAL ? (kb * kKvKeys) / kKvQRows : 0;  // first group touching these keys
+    const int ng = (N + kKvQRows - 1) / kKvQRows;          // query stages of kKvQRows rows
+    const int g0 = CAUSAL ? (kb * kKvKeys) / kKvQRows : 0;  // first stage touching these keys
+    const int nr = (ng - g0 + NG - 1) / NG;                 // rounds (NG stages each)
 
-    // Ring stage layout: [Q rows][dO rows][lse2 x64][D x64]. Chunk j (1 KiB) of
-    // the Q/dO part is written by wave j % 4; lane l of it carries tile row
-    // 8 (j % (kKvTileB/1024)) + l / 8, stored chunk l % 8.
-    auto issue = [&](int g, int st) {
-        char* sb = smem + st * kKvStage;
-        const int r0 = g * kKvQRows;
+    // Ring: kRingRounds rounds of NG stages; stage j of round r holds query stage
+    // g0 + NG r + j (rows past the end clamp to the last row and are never used):
+    // [Q rows][dO rows][lse2 x64][D x64]. Chunk c (1 KiB) of a round's Q/dO parts
+    // is written by wave c % kWaves; lane l of it carries tile row
+    // 8 (c % kKvTC) + l / 8, stored chunk l % 8. Waves 0 .. 2 NG - 1 also copy the
+    // statistics (one 256-byte vector each).
+    auto issue = [&](int r, int slot) {
+        char* rb = smem + slot * kKvRound;
 #pragma unroll
         for (int u = 0; u < kKvCpw; ++u) {
-            const int chunk = u * 4 + wave;
-            constexpr int TC = kKvTileB / 1024;
-            const int p = (chunk % TC) * 64 + lane;
-            const int r = p / CH, c = (p % CH) ^ swz<D>(r);
-            const uint16_t* src = (chunk < TC ? Q : dO) + (size_t)min(r0 + r, N - 1) * D + c * 8;
-            dma16(src, sb + chunk * 1024);
+            const int chunk = u * kWaves + wave;
+            const int j = chunk / (2 * kKvTC), cj = chunk % (2 * kKvTC);
+            const int r0 = (g0 + NG * r + j) * kKvQRows;
+            const int p = (cj % kKvTC) * 64 + lane;
+            const int row = p / CH, c = (p % CH) ^ swz<D>(row);
+            const uint16_t* src = (cj < kKvTC ? Q : dO) + (size_t)min(r0 + row, N - 1) * D + c * 8;
+            dma16(src, rb + j * kKvStage + cj * 1024);
         }
-        if (wave < 2) {
-            const float* src = (wave == 0 ? lse2 : delta) + min(r0 + lane, N - 1);
-            dma4(src, sb + 2 * kKvTileB + wave * kKvStatB);
+        if (wave < 2 * NG) {
+            const int j = wave >> 1, kind = wave & 1;
+            const int r0 = (g0 + NG * r + j) * kKvQRows;
+            const float* src = (kind == 0 ? lse2 : delta) + min(r0 + lane, N - 1);
+            dma4(src, rb + j * kKvStage + 2 * kKvTileB + kind * kKvStatB);
         }
     };
 
@@ -201,8 +225,10 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     for (int ks = 0; ks < KS; ++ks) a_off[ks] = (uint32_t)tile_off<D>(s_row, 2 * ks + h);
     const uint32_t smem_addr = lds_addr(smem);
 
-    if (g0 < ng) issue(g0, 0);
-    if (g0 + 1 < ng) issue(g0 + 1, 1);
+    // rounds 0 and 1 in flight (round 1 even when it lies past the end, so
+    // that the wait counts below are exact)
+    issue(0, 0);
+    issue(1, 1);
     // K and V rows: B operands of S = Q K^T and dP = dO V^T (k = head dim).
     // Loaded after the first ring stages are requested so the latencies overlap;
     // the full wait then tells the compiler's wait pass that no load into a
@@ -218,17 +244,21 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     }
     wait_vmcnt<0>();
 
-    int st = 0;
-    for (int g = g0; g < ng; ++g) {
-        if (g + 1 < ng) {
-            if (wave < 2) wait_vmcnt<kKvCpw + 1>();
+    int slot = 0;
+    for (int r = 0; r < nr; ++r) {
+        // round r has landed (round r + 1 may be in flight); every wave is done
+        // with round r - 1, whose slot the next issue overwrites
+        if (r + 1 < nr || r == 0) {
+            if (wave < 2 * NG) wait_vmcnt<kKvCpw + 1>();
             else wait_vmcnt<kKvCpw>();
         } else {
             wait_vmcnt<0>();
         }
         barrier();
-        if (g + 2 < ng) issue(g + 2, st == 0 ? 2 : st - 1);
-        const uint32_t sbase = smem_addr + (uint32_t)(st * kKvStage);
+        if (r + 2 < nr) issue(r + 2, slot == 0 ? kRingRounds - 1 : slot - 1);
+        const int g = g0 + NG * r + grp;  // this group's query stage
+        const uint32_t sbase = smem_addr + (uint32_t)(slot * kKvRound + grp * kKvStage);
+        slot = slot == kRingRounds - 1 ? 0 : slot + 1;
 #pragma unroll
         for (int hh = 0; hh < QH; ++hh) {
             const int qt0 = g * kKvQRows + 32 * hh;
@@ -270,7 +300,7 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
 #pragma unroll
             for (int j = 0; j < 4; ++j) { settle(lv[j]); settle(dl[j]); }
             // transposed operands for dV^T += dO^T P and dK^T += Q^T dS, issued
-            // now so they land during the elementwise work
+            // now (query chunk 0 first) so they land during the elementwise work
             u32x2 dtr[2][DT][2], qtr[2][DT][2];
 #pragma unroll
             for (int c = 0; c < 2; ++c)
@@ -287,36 +317,36 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
                         }
                     }
             const bool need_mask = (CAUSAL && kw0 + 31 > qt0) || kw0 + 32 > N || qt0 + 32 > N;
-            uint32_t pw[8], dsw[8];
+            // per query chunk c (16 queries): P and dS, then its dV / dK MFMAs, which
+            // run while the next chunk's elementwise work is issued
 #pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                float p[2], ds[2];
+            for (int c = 0; c < 2; ++c) {
+                uint32_t pw[4], dsw[4];
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int i = 2 * w + e;
-                    const float l2 = lv[i >> 2][i & 3];
-                    float pv = fast_exp2(__builtin_fmaf(s[i], a.c, -l2));
-                    if (need_mask) {
-                        const int qi = qt0 + 16 * (i >> 3) + 8 * h + (i & 7);
-                        if ((CAUSAL && key > qi) || key >= N || qi >= N) pv = 0.f;
+                for (int w = 0; w < 4; ++w) {
+                    float p[2], ds[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int i = 8 * c + 2 * w + e;
+                        float pv = fast_exp2(__builtin_fmaf(s[i], a.c, -lv[i >> 2][i & 3]));
+                        if (need_mask) {
+                            const int qi = qt0 + 16 * (i >> 3) + 8 * h + (i & 7);
+                            if ((CAUSAL && key > qi) || key >= N || qi >= N) pv = 0.f;
+                        }
+                        p[e] = pv;
+                        ds[e] = pv * (dp[i] - dl[i >> 2][i & 3]);
                     }
-                    p[e] = pv;
-                    ds[e] = pv * (dp[i] - dl[i >> 2][i & 3]);
+                    pw[w] = T::pack2(p[0], p[1]);
+                    dsw[w] = T::pack2(ds[0], ds[1]);
                 }
-                pw[w] = T::pack2(p[0], p[1]);
-                dsw[w] = T::pack2(ds[0], ds[1]);
-            }
-            lgkm_wait<0>();
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
+                if (c == 0) lgkm_wait<8>();
+                else lgkm_wait<0>();
 #pragma unroll
                 for (int u = 0; u < DT; ++u)
 #pragma unroll
                     for (int hi = 0; hi < 2; ++hi) { settle(dtr[c][u][hi]); settle(qtr[c][u][hi]); }
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const u32x4 pc = {pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]};
-                const u32x4 sc = {dsw[4 * c], dsw[4 * c + 1], dsw[4 * c + 2], dsw[4 * c + 3]};
+                const u32x4 pc = {pw[0], pw[1], pw[2], pw[3]};
+                const u32x4 sc = {dsw[0], dsw[1], dsw[2], dsw[3]};
 #pragma unroll
                 for (int u = 0; u < DT; ++u) {
                     const u32x4 dA = {dtr[c][u][0][0], dtr[c][u][0][1], dtr[c][u][1][0], dtr[c][u][1][1]};
@@ -326,7 +356,36 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
                 }
             }
         }
-        st = st == 2 ? 0 : st + 1;
+    }
+
+    // add the other groups' dK, dV into group 0's (the ring is free: the last
+    // round waited for all of its data and every wave passes the barrier)
+    if constexpr (NG > 1) {
+        barrier();
+        float* mb = reinterpret_cast<float*>(smem);
+        if (grp > 0) {
+            float* w = mb + ((size_t)((grp - 1) * 4 + wl) * 64) * 64 + lane;
+#pragma unroll
+            for (int u = 0; u < DT; ++u)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    w[(16 * u + i) * 64] = dk[u][i];
+                    w[(32 + 16 * u + i) * 64] = dv[u][i];
+                }
+        }
+        __syncthreads();
+        if (grp > 0) return;
+#pragma unroll
+        for (int gg = 1; gg < NG; ++gg) {
+            const float* rsrc = mb + ((size_t)((gg - 1) * 4 + wl) * 64) * 64 + lane;
+#pragma unroll
+            for (int u = 0; u < DT; ++u)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    dk[u][i] += rsrc[(16 * u + i) * 64];
+                    dv[u][i] += rsrc[(32 + 16 * u + i) * 64];
+                }
+        }
     }
 
     if (key < N) {
@@ -347,39 +406,47 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     }
 }
 
-// Query workgroup: dQ of 128 queries.
+// Query workgroup: dQ of 128 queries. Wave group grp takes key blocks grp,
+// grp + NG, ...; every group's wave wl owns the same 32 queries, and the
+// groups' dQ accumulators are added through LDS at the end.
 template <typename T, bool CAUSAL>
 __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = wave >> 2, wl = wave & 3;
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
     const int N = a.N;
     const size_t head = (size_t)bh * N * D;
     const uint16_t* __restrict__ K = a.k + head;
     const uint16_t* __restrict__ V = a.v + head;
 
-    const int q0 = qb * kQRows + wave * 32;  // first query of this wave
+    const int q0 = qb * kQRows + wl * 32;    // first query of this wave
     const int qrow = q0 + l32;
     const bool wave_active = q0 < N;
     const int qload = min(qrow, N - 1);
 
     const int nkb_all = (N + kQKeys - 1) / kQKeys;
     const int nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * kQRows) - 1) / kQKeys + 1) : nkb_all;
+    const int nr = (nkb + NG - 1) / NG;  // rounds (NG key blocks each)
 
     f32x16 dqa[DT];
 #pragma unroll
     for (int u = 0; u < DT; ++u) dqa[u] = f32x16{};
 
-    // Ring stage layout: [K block][V block], each 64 rows in the swizzled layout.
-    auto issue = [&](int kb, int st) {
-        char* sb = smem + st * kQStage;
+    // Ring: kRingRounds rounds of NG stages; stage j of round r holds key block
+    // NG r + j (clamped to the last block past the end, never used): [K block]
+    // [V block], each 64 rows in the swizzled layout. Chunk c of a round is
+    // written by wave c % kWaves.
+    auto issue = [&](int r, int slot) {
+        char* rb = smem + slot * kQRound;
 #pragma unroll
         for (int u = 0; u < kQCpw; ++u) {
-            const int chunk = u * 4 + wave;
-            constexpr int TC = kQTileB / 1024;
-            const int p = (chunk % TC) * 64 + lane;
-            const int r = p / CH, c = (p % CH) ^ swz<D>(r);
-            const uint16_t* src = (chunk < TC ? K : V) + (size_t)min(kb * kQKeys + r, N - 1) * D + c * 8;
-            dma16(src, sb + chunk * 1024);
+            const int chunk = u * kWaves + wave;
+            const int j = chunk / (2 * kQTC), cj = chunk % (2 * kQTC);
+            const int blk = min(NG * r + j, nkb - 1);
+            const int p = (cj % kQTC) * 64 + lane;
+            const int row = p / CH, c = (p % CH) ^ swz<D>(row);
+            const uint16_t* src = (cj < kQTC ? K : V) + (size_t)min(blk * kQKeys + row, N - 1) * D + c * 8;
+            dma16(src, rb + j * kQStage + cj * 1024);
         }
     };
 
@@ -400,7 +467,7 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
     const uint32_t smem_addr = lds_addr(smem);
 
     issue(0, 0);
-    if (nkb > 1) issue(1, 1);
+    issue(1, 1);
     // Q and dO rows: B operands of S^T = K Q^T and dP^T = V dO^T (k = head dim);
     // loaded and waited for as in the key workgroups.
     u32x4 qf[KS], dof[KS];
@@ -416,17 +483,20 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
     const float Dq = a.delta[(size_t)bh * N + qload];
     wait_vmcnt<0>();
 
-    int st = 0;
-    for (int kb = 0; kb < nkb; ++kb) {
-        if (kb + 1 < nkb) wait_vmcnt<kQCpw>();
+    // blocks this wave computes: 0 .. nkw-1 (causal: up to the one holding its last row)
+    const int nkw = !wave_active ? 0 : (CAUSAL ? min(nkb, min(q0 + 31, N - 1) / kQKeys + 1) : nkb);
+    int slot = 0;
+    for (int r = 0; r < nr; ++r) {
+        if (r + 1 < nr || r == 0) wait_vmcnt<kQCpw>();
         else wait_vmcnt<0>();
         barrier();
-        if (kb + 2 < nkb) issue(kb + 2, st == 0 ? 2 : st - 1);
-        const uint32_t kbase = smem_addr + (uint32_t)(st * kQStage);
+        if (r + 2 < nr) issue(r + 2, slot == 0 ? kRingRounds - 1 : slot - 1);
+        const uint32_t kbase = smem_addr + (uint32_t)(slot * kQRound + grp * kQStage);
         const uint32_t vbase = kbase + (uint32_t)kQTileB;
-        st = st == 2 ? 0 : st + 1;
+        slot = slot == kRingRounds - 1 ? 0 : slot + 1;
+        const int kb = NG * r + grp;
         const int key0 = kb * kQKeys;
-        if (!wave_active || (CAUSAL && key0 > q0 + 31)) continue;
+        if (kb >= nkw) continue;
 
         // ---- S^T = K Q^T and dP^T = V dO^T (64 keys x 32 queries; lane = query)
         f32x16 s[2], dp[2];
@@ -458,17 +528,23 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
         for (int u = 0; u < DT; ++u)
 #pragma unroll
             for (int hi = 0; hi < 2; ++hi) {
-                const uint32_t ad = kbase + tr_off[u][hi];
-                ktr[0][u][hi] = tr_read<0 * 16 * kRowB>(ad);
-                ktr[1][u][hi] = tr_read<1 * 16 * kRowB>(ad);
-                ktr[2][u][hi] = tr_read<2 * 16 * kRowB>(ad);
-                ktr[3][u][hi] = tr_read<3 * 16 * kRowB>(ad);
+                ktr[0][u][hi] = tr_read<0 * 16 * kRowB>(kbase + tr_off[u][hi]);
+                ktr[1][u][hi] = tr_read<1 * 16 * kRowB>(kbase + tr_off[u][hi]);
             }
-        // ---- dS^T = P^T (dP^T - D), P^T = exp2(S^T c - lse2)
+#pragma unroll
+        for (int u = 0; u < DT; ++u)
+#pragma unroll
+            for (int hi = 0; hi < 2; ++hi) {
+                ktr[2][u][hi] = tr_read<2 * 16 * kRowB>(kbase + tr_off[u][hi]);
+                ktr[3][u][hi] = tr_read<3 * 16 * kRowB>(kbase + tr_off[u][hi]);
+            }
+        // ---- per key tile kt: dS^T = P^T (dP^T - D) with P^T = exp2(S^T c - lse2),
+        // then dQ^T (64 dims x 32 queries) += K^T dS^T over its two 16-key chunks;
+        // those MFMAs run while the next tile's elementwise work is issued
         const bool need_mask = (CAUSAL && key0 + kQKeys - 1 > q0) || (key0 + kQKeys > N);
-        uint32_t dsw[2][8];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
+            uint32_t dsw[8];
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
                 float ds[2];
@@ -482,24 +558,45 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
                     }
                     ds[e] = pv * (dp[kt][i] - Dq);
                 }
-                dsw[kt][w] = T::pack2(ds[0], ds[1]);
+                dsw[w] = T::pack2(ds[0], ds[1]);
+            }
+            if (kt == 0) lgkm_wait<8>();
+            else lgkm_wait<0>();
+#pragma unroll
+            for (int c = 2 * kt; c < 2 * kt + 2; ++c)
+#pragma unroll
+                for (int u = 0; u < DT; ++u) { settle(ktr[c][u][0]); settle(ktr[c][u][1]); }
+#pragma unroll
+            for (int c = 2 * kt; c < 2 * kt + 2; ++c) {
+                const u32x4 sb = {dsw[4 * (c & 1)], dsw[4 * (c & 1) + 1], dsw[4 * (c & 1) + 2], dsw[4 * (c & 1) + 3]};
+#pragma unroll
+                for (int u = 0; u < DT; ++u) {
+                    const u32x4 kA = {ktr[c][u][0][0], ktr[c][u][0][1], ktr[c][u][1][0], ktr[c][u][1][1]};
+                    dqa[u] = T::mfma32(kA, sb, dqa[u]);
+                }
             }
         }
-        lgkm_wait<0>();
+    }
+
+    if constexpr (NG > 1) {
+        barrier();
+        float* mb = reinterpret_cast<float*>(smem);
+        if (grp > 0) {
+            float* w = mb + ((size_t)((grp - 1) * 4 + wl) * 32) * 64 + lane;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+            for (int u = 0; u < DT; ++u)
 #pragma unroll
-            for (int u = 0; u < DT; ++u) { settle(ktr[c][u][0]); settle(ktr[c][u][1]); }
-        // ---- dQ^T (64 dims x 32 queries) += K^T dS^T over four 16-key chunks
+                for (int i = 0; i < 16; ++i) w[(16 * u + i) * 64] = dqa[u][i];
+        }
+        __syncthreads();
+        if (grp > 0) return;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const u32x4 sb = {dsw[c >> 1][4 * (c & 1)], dsw[c >> 1][4 * (c & 1) + 1],
-                              dsw[c >> 1][4 * (c & 1) + 2], dsw[c >> 1][4 * (c & 1) + 3]};
+        for (int gg = 1; gg < NG; ++gg) {
+            const float* rsrc = mb + ((size_t)((gg - 1) * 4 + wl) * 32) * 64 + lane;
 #pragma unroll
-            for (int u = 0; u < DT; ++u) {
-                const u32x4 kA = {ktr[c][u][0][0], ktr[c][u][0][1], ktr[c][u][1][0], ktr[c][u][1][1]};
-                dqa[u] = T::mfma32(kA, sb, dqa[u]);
-            }
+            for (int u = 0; u < DT; ++u)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) dqa[u][i] += rsrc[(16 * u + i) * 64];
         }
     }
 
@@ -519,7 +616,7 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
 }
 
 template <typename T, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void bwd_fused_kernel(FusedArgs a) {
+__global__ __launch_bounds__(kThreads) void bwd_fused_kernel(FusedArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[kSmem];
     int bh, blk;
     bool is_q;
@@ -552,12 +649,12 @@ hipError_t bwd_prep(const void* o, const void* dout, const float* lse, int B, in
     p.delta = delta;
     p.lse2 = lse2;
     p.rows = (int64_t)B * H * N;
-    constexpr int RPB = kThreads / (D / 8);
+    constexpr int RPB = kPrepThreads / (D / 8);
     const dim3 grid((unsigned)((p.rows + RPB - 1) / RPB));
     if (dtype == 0)
-        hipLaunchKernelGGL((bwd_prep_kernel<Bf16>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((bwd_prep_kernel<Bf16>), grid, dim3(kPrepThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((bwd_prep_kernel<F16>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((bwd_prep_kernel<F16>), grid, dim3(kPrepThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -584,3 +681,4 @@ hipError_t bwd_fused(const void* q, const void* k, const void* v, const void* do
 }
 
 }  // namespace fa
+

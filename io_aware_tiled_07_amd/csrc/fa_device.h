@@ -53,6 +53,10 @@ struct Bf16 {
     __device__ __forceinline__ static float to_f32(uint16_t x) {
         return __uint_as_float(((uint32_t)x) << 16);
     }
+    // acc + lo + hi of a packed pair (v_dot2c_f32_bf16 against (1, 1))
+    __device__ __forceinline__ static float sum2(uint32_t packed, float acc) {
+        return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(packed), bitcast<bf16x2>(0x3F803F80u), acc, false);
+    }
 };
 
 struct F16 {
@@ -69,6 +73,10 @@ struct F16 {
     }
     __device__ __forceinline__ static float to_f32(uint16_t x) {
         return (float)bitcast<_Float16>(x);
+    }
+    // acc + lo + hi of a packed pair (v_dot2c_f32_f16 against (1, 1))
+    __device__ __forceinline__ static float sum2(uint32_t packed, float acc) {
+        return __builtin_amdgcn_fdot2(bitcast<f16x2>(packed), bitcast<f16x2>(0x3C003C00u), acc, false);
     }
 };
 

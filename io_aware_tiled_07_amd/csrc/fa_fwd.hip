@@ -23,8 +23,12 @@
 //    MFMA: O^T += V^T P^T takes P straight from registers (rounded to the
 //    input type), and V^T comes from row-major LDS through the gfx950
 //    transposed read ds_read_b64_tr_b16.
-//  * Softmax runs in base 2 with scale*log2(e) folded into one FMA; O is
-//    rescaled only when some row maximum of the wave actually moved.
+//  * Softmax runs in base 2 with scale*log2(e) folded into one FMA. A row's
+//    reference maximum only moves when the block maximum exceeds it by more
+//    than 2^8 (weights then stay <= 256: exact in fp32, and bf16/fp16 keep
+//    their relative precision), so O is rarely rescaled. The row sum adds the
+//    rounded weights in pairs (v_dot2c_f32 against (1, 1)), so numerator and
+//    denominator use the same values.
 //  * Causal: key blocks above the diagonal are never loaded, whole waves skip
 //    blocks above their rows, and only blocks crossing the diagonal (or the
 //    ragged end of the sequence) are masked element by element.
@@ -100,14 +104,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     const int q0 = qb * BR + wave * ROWS;  // first query row of this wave
     const bool wave_active = q0 < N;
 
-    // Q fragments: B operand of S^T = K Q^T (column = query, k = head dim).
-    u32x4 qf[QT][KS];
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-        const uint16_t* qp = Q + (size_t)min(q0 + 32 * t + l32, N - 1) * D + 8 * h;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[t][ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
-    }
 
     const int nkb_all = (N + kBc - 1) / kBc;
     const int nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * BR) - 1) / kBc + 1) : nkb_all;
@@ -152,9 +148,25 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
                                         (L16 & 1) * 8);
     const uint32_t smem_addr = lds_addr(smem);
     const int s_row = perm32(l32);
+    uint32_t a_off[KS];  // K operand rows for S^T, k-step ks (the second key tile adds 32 rows)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a_off[ks] = (uint32_t)tile_off<D>(s_row, 2 * ks + h);
 
     issue(0, 0);
     if (STAGES == 3 && nkb > 1) issue(1, 1);
+
+    // Q fragments: B operand of S^T = K Q^T (column = query, k = head dim).
+    // Loaded after the first ring stages are requested so the latencies
+    // overlap; the full wait tells the compiler's wait pass that no load into a
+    // register is pending inside the loop (else it drains the ring there).
+    u32x4 qf[QT][KS];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+        const uint16_t* qp = Q + (size_t)min(q0 + 32 * t + l32, N - 1) * D + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[t][ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+    }
+    wait_vmcnt<0>();
 
     for (int kb = 0; kb < nkb; ++kb) {
         // this wave's share of block kb has landed; then every wave's has, and
@@ -167,18 +179,21 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
         } else {
             if (kb + 1 < nkb) issue(kb + 1, (kb + 1) & 1);
         }
-        const char* kbuf = smem + (kb % STAGES) * SB;
-        const char* vbuf = kbuf + TB;
         const int key0 = kb * kBc;
         if (!wave_active || (CAUSAL && key0 > q0 + ROWS - 1)) continue;
 
         // ---- S^T (64 keys x 32 queries per query tile): two 32x32 tiles each.
         // All K operand reads go out first so their LDS latency overlaps.
+        const uint32_t stage_addr = smem_addr + (uint32_t)((kb % STAGES) * SB);
         u32x4 ka[KS][2];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks) {
+            ka[ks][0] = ds_read128<0>(stage_addr + a_off[ks]);
+            ka[ks][1] = ds_read128<32 * 2 * D>(stage_addr + a_off[ks]);
+        }
+        lgkm_wait<0>();
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) ka[ks][kt] = lds_read16(kbuf, tile_off<D>(32 * kt + s_row, 2 * ks + h));
+        for (int ks = 0; ks < KS; ++ks) { settle(ka[ks][0]); settle(ka[ks][1]); }
         f32x16 s[QT][2];
 #pragma unroll
         for (int t = 0; t < QT; ++t) s[t][0] = s[t][1] = f32x16{};
@@ -190,17 +205,35 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
                 for (int t = 0; t < QT; ++t) s[t][kt] = T::mfma32(ka[ks][kt], qf[t][ks], s[t][kt]);
 
         // V^T operands for the whole block, issued before the softmax so they land meanwhile
-        u32x4 va[4][DT];
+        u32x2 vlo[4][DT], vhi[4][DT];
         {
+            // head dim 64: chunk by chunk, so that chunks 0 and 1 (the first 32
+            // keys) land first; head dim 128: dim tile by dim tile
             const uint32_t stage_addr = smem_addr + (uint32_t)((kb % STAGES) * SB);
+            if constexpr (DT == 2) {
 #pragma unroll
-            for (int u = 0; u < DT; ++u) {
-                const uint32_t a0 = stage_addr + tr_addr[u][0], a1 = stage_addr + tr_addr[u][1];
-                u32x2 lo, hi;
-                lo = tr_read<0 * 16 * 2 * D>(a0); hi = tr_read<0 * 16 * 2 * D>(a1); va[0][u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-                lo = tr_read<1 * 16 * 2 * D>(a0); hi = tr_read<1 * 16 * 2 * D>(a1); va[1][u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-                lo = tr_read<2 * 16 * 2 * D>(a0); hi = tr_read<2 * 16 * 2 * D>(a1); va[2][u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-                lo = tr_read<3 * 16 * 2 * D>(a0); hi = tr_read<3 * 16 * 2 * D>(a1); va[3][u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                for (int u = 0; u < DT; ++u) {
+                    vlo[0][u] = tr_read<0 * 16 * 2 * D>(stage_addr + tr_addr[u][0]);
+                    vhi[0][u] = tr_read<0 * 16 * 2 * D>(stage_addr + tr_addr[u][1]);
+                    vlo[1][u] = tr_read<1 * 16 * 2 * D>(stage_addr + tr_addr[u][0]);
+                    vhi[1][u] = tr_read<1 * 16 * 2 * D>(stage_addr + tr_addr[u][1]);
+                }
+#pragma unroll
+                for (int u = 0; u < DT; ++u) {
+                    vlo[2][u] = tr_read<2 * 16 * 2 * D>(stage_addr + tr_addr[u][0]);
+                    vhi[2][u] = tr_read<2 * 16 * 2 * D>(stage_addr + tr_addr[u][1]);
+                    vlo[3][u] = tr_read<3 * 16 * 2 * D>(stage_addr + tr_addr[u][0]);
+                    vhi[3][u] = tr_read<3 * 16 * 2 * D>(stage_addr + tr_addr[u][1]);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < DT; ++u) {
+                    const uint32_t a0 = stage_addr + tr_addr[u][0], a1 = stage_addr + tr_addr[u][1];
+                    vlo[0][u] = tr_read<0 * 16 * 2 * D>(a0); vhi[0][u] = tr_read<0 * 16 * 2 * D>(a1);
+                    vlo[1][u] = tr_read<1 * 16 * 2 * D>(a0); vhi[1][u] = tr_read<1 * 16 * 2 * D>(a1);
+                    vlo[2][u] = tr_read<2 * 16 * 2 * D>(a0); vhi[2][u] = tr_read<2 * 16 * 2 * D>(a1);
+                    vlo[3][u] = tr_read<3 * 16 * 2 * D>(a0); vhi[3][u] = tr_read<3 * 16 * 2 * D>(a1);
+                }
             }
         }
 
@@ -225,42 +258,68 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
             for (int i = 1; i < 16; i += 2) mx = max3(mx, s[t][0][i], s[t][0][i + 1]);
 #pragma unroll
             for (int i = 0; i < 16; i += 2) mx = max3(mx, s[t][1][i], s[t][1][i + 1]);
-            mx = pair_max(mx);
-            const float m_new = fmaxf(m_run[t], mx * a.c);
-            const float alpha = fast_exp2(m_run[t] - m_new);
-            float lsum = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-                for (int w = 0; w < 8; ++w) {
-                    const float p0 = fast_exp2(__builtin_fmaf(s[t][kt][2 * w], a.c, -m_new));
-                    const float p1 = fast_exp2(__builtin_fmaf(s[t][kt][2 * w + 1], a.c, -m_new));
-                    lsum += p0 + p1;
-                    pk[t][kt][w] = T::pack2(p0, p1);
-                }
-            }
-            l_run[t] = alpha * l_run[t] + lsum;
-            if (__ballot(alpha != 1.f)) {
+            mx = pair_max(mx) * a.c;
+            const bool grow = mx > m_run[t] + 8.f;
+            if (__ballot(grow)) {
+                const float m_new = grow ? mx : m_run[t];
+                const float alpha = fast_exp2(m_run[t] - m_new);
+                l_run[t] *= alpha;
 #pragma unroll
                 for (int u = 0; u < DT; ++u) oacc[t][u] *= alpha;
+                m_run[t] = m_new;
             }
-            m_run[t] = m_new;
         }
-        // ---- O^T (D x 32 queries) += V^T P^T over four 16-key chunks
+        // ---- weights of the first 32 keys, their O^T += V^T P^T MFMAs (which run
+        // while the weights of the other 32 keys are formed), then the rest. At
+        // head dim 128 the V^T operands already fill the registers, so there all
+        // weights are formed before the MFMAs.
+        constexpr bool kSplit = DT == 2;
+        float lsum[QT];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if constexpr (DT == 2) lds_wait_all(va[c][0], va[c][1]);
-            else lds_wait_all(va[c][0], va[c][1], va[c][2], va[c][3]);
+        for (int t = 0; t < QT; ++t) lsum[t] = 0.f;
+        auto weights = [&](int kt) {
 #pragma unroll
-            for (int u = 0; u < DT; ++u) {
+            for (int t = 0; t < QT; ++t)
 #pragma unroll
-                for (int t = 0; t < QT; ++t) {
-                    const u32x4 pb = {pk[t][c >> 1][4 * (c & 1) + 0], pk[t][c >> 1][4 * (c & 1) + 1],
-                                      pk[t][c >> 1][4 * (c & 1) + 2], pk[t][c >> 1][4 * (c & 1) + 3]};
-                    oacc[t][u] = T::mfma32(va[c][u], pb, oacc[t][u]);
+                for (int w = 0; w < 8; ++w) {
+                    const float p0 = fast_exp2(__builtin_fmaf(s[t][kt][2 * w], a.c, -m_run[t]));
+                    const float p1 = fast_exp2(__builtin_fmaf(s[t][kt][2 * w + 1], a.c, -m_run[t]));
+                    pk[t][kt][w] = T::pack2(p0, p1);
+                    lsum[t] = T::sum2(pk[t][kt][w], lsum[t]);
+                }
+        };
+        if constexpr (!kSplit) {
+            weights(0);
+            weights(1);
+            lgkm_wait<0>();
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            if constexpr (kSplit) {
+                weights(kt);
+                if (kt == 0) lgkm_wait<(kSplit ? 4 * DT : 0)>();
+                else lgkm_wait<0>();
+            }
+#pragma unroll
+            for (int c = 2 * kt; c < 2 * kt + 2; ++c)
+#pragma unroll
+                for (int u = 0; u < DT; ++u) { settle(vlo[c][u]); settle(vhi[c][u]); }
+#pragma unroll
+            for (int c = 2 * kt; c < 2 * kt + 2; ++c) {
+#pragma unroll
+                for (int u = 0; u < DT; ++u) {
+                    const u32x4 va = {vlo[c][u][0], vlo[c][u][1], vhi[c][u][0], vhi[c][u][1]};
+#pragma unroll
+                    for (int t = 0; t < QT; ++t) {
+                        const u32x4 pb = {pk[t][kt][4 * (c & 1) + 0], pk[t][kt][4 * (c & 1) + 1],
+                                          pk[t][kt][4 * (c & 1) + 2], pk[t][kt][4 * (c & 1) + 3]};
+                        oacc[t][u] = T::mfma32(va, pb, oacc[t][u]);
+                    }
                 }
             }
         }
+#pragma unroll
+        for (int t = 0; t < QT; ++t) l_run[t] += lsum[t];
     }
 
     // ---- epilogue: O = O_acc / l, lse = ln2 * (m + log2 l)

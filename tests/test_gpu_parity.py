@@ -177,8 +177,10 @@ def test_forward_is_deterministic():
 
 
 def test_backward_determinism():
-    """dK, dV (and dQ with the separate pass) repeat bitwise; atomic dQ may differ
-    in the last bits from run to run but stays within tolerance of the oracle."""
+    """The default backward (dQ in its own pass) repeats bitwise; the atomic strategy's
+    dK and dV repeat bitwise, its dQ may differ in the last bits from run to run. The
+    two strategies add partial sums in different orders, so across strategies the
+    results agree to the parity tolerance, not bitwise."""
     drawn = inputs(1002, (2, 4, 512, 64), "bf16")
     q, k, v, do = to_dev(drawn)
     o, lse = fa.fwd(q, k, v)
@@ -186,7 +188,10 @@ def test_backward_determinism():
     b = fa.bwd(q, k, v, o, do, lse, dq_strategy=fa.FA_DQ_SEPARATE)
     assert all(torch.equal(x, y) for x, y in zip(a, b))
     c = fa.bwd(q, k, v, o, do, lse, dq_strategy=fa.FA_DQ_ATOMIC)
-    assert torch.equal(a[1], c[1]) and torch.equal(a[2], c[2])
+    e = fa.bwd(q, k, v, o, do, lse, dq_strategy=fa.FA_DQ_ATOMIC)
+    assert torch.equal(c[1], e[1]) and torch.equal(c[2], e[2])
+    for x, y in zip(a, c):
+        assert (x.float() - y.float()).abs().max().item() <= 2e-2
 
 
 def test_backward_invariants():
@@ -247,6 +252,6 @@ def test_staged_backward_matches_fa_bwd():
         torch.cuda.synchronize()
         if strategy == fa.FA_DQ_SEPARATE:
             assert torch.equal(dq, ref[0]) and torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
-        else:
-            assert torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
-            assert (dq.float() - ref[0].float()).abs().max().item() < 2e-2
+        else:  # another strategy: other summation order
+            for x, y in zip((dq, dk, dv), ref):
+                assert (x.float() - y.float()).abs().max().item() < 2e-2
