@@ -17,11 +17,12 @@
 //  2. bwd_fused: one grid holding two kinds of workgroups, which share no
 //     data and run side by side:
 //     * key workgroups (128 keys, 32 per wave): K and V rows of the wave stay
-//       in VGPRs, dK^T and dV^T in fp32 accumulators. Query tiles (Q, dO and
-//       their statistics) stream HBM -> LDS through a 3-stage LDS-DMA ring; per
-//       32 queries a wave forms S = Q K^T and dP = dO V^T (lane = key), then
-//       P and dS in registers, then dV^T += dO^T P and dK^T += Q^T dS with the
-//       dO^T / Q^T operands read transposed from LDS (ds_read_b64_tr_b16).
+//       in VGPRs, dK^T and dV^T in fp32 accumulators. Query stages (64 rows of
+//       Q and dO and their statistics) stream HBM -> LDS through a 3-slot
+//       LDS-DMA ring; per 32 queries a wave forms S = Q K^T and dP = dO V^T
+//       (lane = key), then P and dS in registers, then dV^T += dO^T P and
+//       dK^T += Q^T dS with the dO^T / Q^T operands read transposed from LDS
+//       (ds_read_b64_tr_b16).
 //     * query workgroups (128 queries, 32 per wave): Q and dO rows stay in
 //       VGPRs, K and V blocks of 64 keys stream through the same kind of ring
 //       (the forward's layout); a wave forms S^T = K Q^T and dP^T = V dO^T
@@ -31,11 +32,16 @@
 //     workgroup of one (batch, head) goes to the same XCD so its tensors are
 //     reused from that XCD's L2.
 //  Causal: tiles wholly above the diagonal are skipped; only tiles crossing it
-//  (or the ragged end of the sequence) are masked element by element.
+//  (or the ragged end of the sequence) run the element-wise mask, on a code
+//  path of their own.
+//  The ring loop is unrolled over its three slots, so every LDS read is a
+//  loop-invariant base register plus an immediate offset.
 //
 // The dQ pass recomputes S and dP (7 matrix products in total instead of 5),
 // which on this chip costs less than fp32 atomics for dQ (measured; the atomic
 // strategy lives in fa_bwd_atomic.hip).
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -43,49 +49,38 @@ namespace fa {
 
 namespace {
 
-#ifndef FA_BWD_NG
-#define FA_BWD_NG 1
-#endif
-constexpr int NG = FA_BWD_NG;       // wave groups per workgroup (they split the long loop)
-constexpr int kWaves = 4 * NG;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kPrepThreads = 256;
+template <int V>
+using Int = std::integral_constant<int, V>;
+using Masked = std::true_type;
+using Unmasked = std::false_type;
+
+constexpr int kThreads = 256;
 constexpr int D = 64;          // head dim of the backward
 constexpr int KS = D / 16;     // k-steps over the head dim (32x32x16 MFMA)
 constexpr int DT = D / 32;     // 32-wide tiles of the head dim
 constexpr int CH = D / 8;      // 16-byte chunks per row
 constexpr int kRowB = 2 * D;   // bytes per tile row
-constexpr int kRingRounds = 3; // rounds of stages held by the ring
+constexpr int kSlots = 3;      // ring slots
 
 // key workgroups
-constexpr int kKvKeys = 128;                 // keys per workgroup (32 per wave of a group)
-#ifndef FA_BWD_QH
-#define FA_BWD_QH 2
-#endif
-constexpr int QH = FA_BWD_QH;                // 32-query halves per ring stage
-constexpr int kKvQRows = 32 * QH;            // query rows per ring stage
+constexpr int kKvKeys = 128;                 // keys per workgroup (32 per wave)
+constexpr int kKvQRows = 64;                 // query rows per ring stage
 constexpr int kKvTileB = kKvQRows * kRowB;   // bytes of the Q (or dO) part of a stage
 constexpr int kKvTC = kKvTileB / 1024;       // 1 KiB chunks of that part
 constexpr int kKvStatB = 256;                // 64 floats of lse*log2e, then 64 of D
 constexpr int kKvStage = 2 * kKvTileB + 2 * kKvStatB;
-constexpr int kKvRound = NG * kKvStage;      // one round: a stage per wave group
-constexpr int kKvCpw = NG * 2 * kKvTC / kWaves;  // 16-byte DMA instructions per wave per round
-static_assert(kKvCpw * kWaves == NG * 2 * kKvTC, "round must split evenly over the waves");
+constexpr int kKvCpw = 2 * kKvTC / 4;        // 16-byte DMA instructions per wave per stage
 
 // query workgroups
-constexpr int kQRows = 128;                  // queries per workgroup (32 per wave of a group)
+constexpr int kQRows = 128;                  // queries per workgroup (32 per wave)
 constexpr int kQKeys = 64;                   // keys per ring stage
 constexpr int kQTileB = kQKeys * kRowB;      // bytes of the K (or V) part of a stage
 constexpr int kQTC = kQTileB / 1024;
 constexpr int kQStage = 2 * kQTileB;
-constexpr int kQRound = NG * kQStage;
-constexpr int kQCpw = NG * 2 * kQTC / kWaves;
-static_assert(kQCpw * kWaves == NG * 2 * kQTC, "round must split evenly over the waves");
+constexpr int kQCpw = 2 * kQTC / 4;
 
-constexpr int kRingB = kRingRounds * (kKvRound > kQRound ? kKvRound : kQRound);
-// after the loop the ring is reused to add group g > 0's accumulators into group 0's
-constexpr int kMergeB = (NG - 1) * 4 * 64 * 64 * 4;  // 4 waves x 64 floats x 64 lanes per extra group
-constexpr int kSmem = kRingB > kMergeB ? kRingB : kMergeB;
+constexpr int kSmem = kSlots * (kKvStage > kQStage ? kKvStage : kQStage);
+static_assert(kSlots * kKvStage < 65536 && kSlots * kQStage < 65536, "LDS offsets must fit the immediate field");
 
 struct FusedArgs {
     const uint16_t* q;
@@ -114,11 +109,11 @@ struct PrepArgs {
 };
 
 // ---------------------------------------------------------------- 1. prep
-// 8 lanes per row, 8 elements each; 32 rows per 256-thread workgroup.
+// 8 lanes per row, 8 elements each; 32 rows per workgroup.
 template <typename T>
-__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(PrepArgs a) {
     constexpr int LPR = D / 8;
-    constexpr int RPB = kPrepThreads / LPR;
+    constexpr int RPB = kThreads / LPR;
     const int tid = threadIdx.x, part = tid % LPR;
     const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
     const int64_t r = row < a.rows ? row : a.rows - 1;
@@ -157,13 +152,21 @@ __device__ __forceinline__ void map_fused(int bid, const FusedArgs& a, bool caus
     blk = is_q ? (causal ? a.nblk - 1 - i : i) : i;
 }
 
-// Key workgroup: dK and dV of 128 keys. Wave group grp (waves 4 grp .. 4 grp + 3)
-// takes query stages g0 + grp, g0 + grp + NG, ...; every group's wave wl owns the
-// same 32 keys, and the groups' accumulators are added through LDS at the end.
+// Run body(Int<slot>{}, r) for r = 0 .. n-1 with slot = r % kSlots known at
+// compile time.
+template <typename F>
+__device__ __forceinline__ void for_rounds(int n, F&& body) {
+    for (int r = 0; r < n; r += kSlots) {
+        body(Int<0>{}, r);
+        if (r + 1 < n) body(Int<1>{}, r + 1);
+        if (r + 2 < n) body(Int<2>{}, r + 2);
+    }
+}
+
+// Key workgroup: dK and dV of 128 keys.
 template <typename T, bool CAUSAL>
 __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int grp = wave >> 2, wl = wave & 3;
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
     const int N = a.N;
     const size_t head = (size_t)bh * N * D;
@@ -172,61 +175,59 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     const float* __restrict__ lse2 = a.lse2 + (size_t)bh * N;
     const float* __restrict__ delta = a.delta + (size_t)bh * N;
 
-    const int kw0 = kb * kKvKeys + wl * 32;    // first key of this wave
+    const int kw0 = kb * kKvKeys + wave * 32;  // first key of this wave
     const int key = kw0 + l32;                 // key of this lane (and of lane ^ 32)
     f32x16 dk[DT], dv[DT];
 #pragma unroll
     for (int u = 0; u < DT; ++u) { dk[u] = f32x16{}; dv[u] = f32x16{}; }
 
-    const int ng = (N + kKvQRows - 1) / kKvQRows;          // query stages of kKvQRows rows
+    const int ng = (N + kKvQRows - 1) / kKvQRows;          // query stages
     const int g0 = CAUSAL ? (kb * kKvKeys) / kKvQRows : 0;  // first stage touching these keys
-    const int nr = (ng - g0 + NG - 1) / NG;                 // rounds (NG stages each)
+    const int nst = ng - g0;
 
-    // Ring: kRingRounds rounds of NG stages; stage j of round r holds query stage
-    // g0 + NG r + j (rows past the end clamp to the last row and are never used):
-    // [Q rows][dO rows][lse2 x64][D x64]. Chunk c (1 KiB) of a round's Q/dO parts
-    // is written by wave c % kWaves; lane l of it carries tile row
-    // 8 (c % kKvTC) + l / 8, stored chunk l % 8. Waves 0 .. 2 NG - 1 also copy the
-    // statistics (one 256-byte vector each).
-    auto issue = [&](int r, int slot) {
-        char* rb = smem + slot * kKvRound;
+    // Stage s (query stage g0 + s, rows past the end clamp to the last row and
+    // are never used) in slot s % 3: [Q rows][dO rows][lse2 x64][D x64]. Chunk
+    // c (1 KiB) of the Q/dO part is written by wave c % 4; lane l of it carries
+    // tile row 8 (c % kKvTC) + l / 8, stored chunk l % 8. Waves 0 and 1 also
+    // copy the statistics.
+    auto issue = [&](int s, int slot) {
+        char* sb = smem + slot * kKvStage;
+        const int r0 = (g0 + s) * kKvQRows;
 #pragma unroll
         for (int u = 0; u < kKvCpw; ++u) {
-            const int chunk = u * kWaves + wave;
-            const int j = chunk / (2 * kKvTC), cj = chunk % (2 * kKvTC);
-            const int r0 = (g0 + NG * r + j) * kKvQRows;
-            const int p = (cj % kKvTC) * 64 + lane;
+            const int chunk = u * 4 + wave;
+            const int p = (chunk % kKvTC) * 64 + lane;
             const int row = p / CH, c = (p % CH) ^ swz<D>(row);
-            const uint16_t* src = (cj < kKvTC ? Q : dO) + (size_t)min(r0 + row, N - 1) * D + c * 8;
-            dma16(src, rb + j * kKvStage + cj * 1024);
+            const uint16_t* src = (chunk < kKvTC ? Q : dO) + (size_t)min(r0 + row, N - 1) * D + c * 8;
+            dma16(src, sb + chunk * 1024);
         }
-        if (wave < 2 * NG) {
-            const int j = wave >> 1, kind = wave & 1;
-            const int r0 = (g0 + NG * r + j) * kKvQRows;
-            const float* src = (kind == 0 ? lse2 : delta) + min(r0 + lane, N - 1);
-            dma4(src, rb + j * kKvStage + 2 * kKvTileB + kind * kKvStatB);
+        if (wave < 2) {
+            const float* src = (wave == 0 ? lse2 : delta) + min(r0 + lane, N - 1);
+            dma4(src, sb + 2 * kKvTileB + wave * kKvStatB);
         }
     };
 
-    // Transposed-read addresses (relative to a stage): lane L of 16-lane group g
-    // reads row 8h + L/4 (+4 for the upper half of the operand), columns
-    // 32u + 16(g&1) + 4(L&3) of the Q or dO rows; query chunks add 16 rows.
-    uint32_t tr_off[DT][2];
+    // Loop-invariant LDS addresses; the slot, half and chunk parts are immediates.
+    const uint32_t smem_addr = lds_addr(smem);
+    const int s_row = perm32(l32);
+    uint32_t a_base[KS];  // Q / dO operand rows for S and dP, k-step ks
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a_base[ks] = smem_addr + (uint32_t)tile_off<D>(s_row, 2 * ks + h);
+    // Transposed reads: lane L of 16-lane group g reads row 8h + L/4 (+4 for the
+    // upper half of the operand), columns 32u + 16(g&1) + 4(L&3) of the Q or dO
+    // rows; query chunks add 16 rows.
+    uint32_t tr_base[DT][2];
 #pragma unroll
     for (int u = 0; u < DT; ++u)
 #pragma unroll
         for (int hi = 0; hi < 2; ++hi)
-            tr_off[u][hi] = (uint32_t)(tile_off<D>(8 * h + (L16 >> 2) + 4 * hi,
-                                                   (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
-                                       (L16 & 1) * 8);
-    const int s_row = perm32(l32);
-    uint32_t a_off[KS];  // Q / dO operand rows for S and dP, k-step ks
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a_off[ks] = (uint32_t)tile_off<D>(s_row, 2 * ks + h);
-    const uint32_t smem_addr = lds_addr(smem);
+            tr_base[u][hi] = smem_addr + (uint32_t)(tile_off<D>(8 * h + (L16 >> 2) + 4 * hi,
+                                                                (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
+                                                    (L16 & 1) * 8);
+    const uint32_t st_base = smem_addr + (uint32_t)(4 * 8 * h);
 
-    // rounds 0 and 1 in flight (round 1 even when it lies past the end, so
-    // that the wait counts below are exact)
+    // stages 0 and 1 in flight (stage 1 even when it lies past the end, so that
+    // the wait counts below are exact)
     issue(0, 0);
     issue(1, 1);
     // K and V rows: B operands of S = Q K^T and dP = dO V^T (k = head dim).
@@ -244,149 +245,144 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     }
     wait_vmcnt<0>();
 
-    int slot = 0;
-    for (int r = 0; r < nr; ++r) {
-        // round r has landed (round r + 1 may be in flight); every wave is done
-        // with round r - 1, whose slot the next issue overwrites
-        if (r + 1 < nr || r == 0) {
-            if (wave < 2 * NG) wait_vmcnt<kKvCpw + 1>();
-            else wait_vmcnt<kKvCpw>();
-        } else {
-            wait_vmcnt<0>();
+    // One unit: 32 queries (half HH of the stage in slot SLOT) against the
+    // wave's 32 keys.
+    auto unit = [&](auto slot_c, auto hh_c, bool need_mask, int qt0) {
+        constexpr int SO = decltype(slot_c)::value * kKvStage;
+        constexpr int QO = SO + decltype(hh_c)::value * 32 * kRowB;  // Q rows of the half
+        constexpr int DO = QO + kKvTileB;                            // dO rows of the half
+        constexpr int TO = SO + 2 * kKvTileB + 4 * 32 * decltype(hh_c)::value;
+        // ---- S = Q K^T, dP = dO V^T (32 queries x 32 keys; lane = key)
+        u32x4 qa[KS], da[KS];
+        qa[0] = ds_read128<QO>(a_base[0]);
+        qa[1] = ds_read128<QO>(a_base[1]);
+        qa[2] = ds_read128<QO>(a_base[2]);
+        qa[3] = ds_read128<QO>(a_base[3]);
+        da[0] = ds_read128<DO>(a_base[0]);
+        da[1] = ds_read128<DO>(a_base[1]);
+        da[2] = ds_read128<DO>(a_base[2]);
+        da[3] = ds_read128<DO>(a_base[3]);
+        // statistics of this lane's first 8 queries (8h + 0..7); those of the
+        // other 8 (16 + 8h + 0..7) are read when their chunk comes up
+        f32x4 lv[2], dl[2];
+        lv[0] = ds_read128f<TO>(st_base);
+        lv[1] = ds_read128f<TO + 16>(st_base);
+        dl[0] = ds_read128f<TO + kKvStatB>(st_base);
+        dl[1] = ds_read128f<TO + kKvStatB + 16>(st_base);
+        lgkm_wait<4>();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) { settle(qa[ks]); settle(da[ks]); }
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s = T::mfma32(qa[ks], kf[ks], s);
+            dp = T::mfma32(da[ks], vf[ks], dp);
         }
-        barrier();
-        if (r + 2 < nr) issue(r + 2, slot == 0 ? kRingRounds - 1 : slot - 1);
-        const int g = g0 + NG * r + grp;  // this group's query stage
-        const uint32_t sbase = smem_addr + (uint32_t)(slot * kKvRound + grp * kKvStage);
-        slot = slot == kRingRounds - 1 ? 0 : slot + 1;
+        lgkm_wait<0>();
 #pragma unroll
-        for (int hh = 0; hh < QH; ++hh) {
-            const int qt0 = g * kKvQRows + 32 * hh;
-            const bool active = kw0 < N && qt0 < N && (!CAUSAL || qt0 + 31 >= kw0);
-            if (!active) continue;
-            const uint32_t qb = sbase + (uint32_t)(hh * 32 * kRowB);
-            const uint32_t db = qb + (uint32_t)kKvTileB;
-            // ---- S = Q K^T, dP = dO V^T (32 queries x 32 keys; lane = key)
-            u32x4 qa[KS], da[KS];
-            qa[0] = ds_read128<0>(qb + a_off[0]);
-            qa[1] = ds_read128<0>(qb + a_off[1]);
-            qa[2] = ds_read128<0>(qb + a_off[2]);
-            qa[3] = ds_read128<0>(qb + a_off[3]);
-            da[0] = ds_read128<0>(db + a_off[0]);
-            da[1] = ds_read128<0>(db + a_off[1]);
-            da[2] = ds_read128<0>(db + a_off[2]);
-            da[3] = ds_read128<0>(db + a_off[3]);
-            // statistics of this lane's 16 queries: 8h + 0..7 and 16 + 8h + 0..7
-            const uint32_t stb = sbase + (uint32_t)(2 * kKvTileB + 4 * (32 * hh + 8 * h));
-            f32x4 lv[4], dl[4];
-            lv[0] = ds_read128f<0>(stb);
-            lv[1] = ds_read128f<16>(stb);
-            lv[2] = ds_read128f<64>(stb);
-            lv[3] = ds_read128f<80>(stb);
-            dl[0] = ds_read128f<kKvStatB>(stb);
-            dl[1] = ds_read128f<kKvStatB + 16>(stb);
-            dl[2] = ds_read128f<kKvStatB + 64>(stb);
-            dl[3] = ds_read128f<kKvStatB + 80>(stb);
-            lgkm_wait<8>();
+        for (int j = 0; j < 2; ++j) { settle(lv[j]); settle(dl[j]); }
+        // transposed operands for dV^T += dO^T P and dK^T += Q^T dS, query chunk
+        // 0 first, so they land during the element-wise work
+        u32x2 dtr[2][DT][2], qtr[2][DT][2];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) { settle(qa[ks]); settle(da[ks]); }
-            f32x16 s = f32x16{}, dp = f32x16{};
+        for (int u = 0; u < DT; ++u)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s = T::mfma32(qa[ks], kf[ks], s);
-                dp = T::mfma32(da[ks], vf[ks], dp);
+            for (int hi = 0; hi < 2; ++hi) {
+                dtr[0][u][hi] = tr_read<DO>(tr_base[u][hi]);
+                qtr[0][u][hi] = tr_read<QO>(tr_base[u][hi]);
             }
-            lgkm_wait<0>();
 #pragma unroll
-            for (int j = 0; j < 4; ++j) { settle(lv[j]); settle(dl[j]); }
-            // transposed operands for dV^T += dO^T P and dK^T += Q^T dS, issued
-            // now (query chunk 0 first) so they land during the elementwise work
-            u32x2 dtr[2][DT][2], qtr[2][DT][2];
+        for (int u = 0; u < DT; ++u)
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+            for (int hi = 0; hi < 2; ++hi) {
+                dtr[1][u][hi] = tr_read<DO + 16 * kRowB>(tr_base[u][hi]);
+                qtr[1][u][hi] = tr_read<QO + 16 * kRowB>(tr_base[u][hi]);
+            }
+        // per query chunk c (16 queries): P and dS, then its dV / dK MFMAs, which
+        // run while the next chunk's element-wise work is issued
 #pragma unroll
-                for (int u = 0; u < DT; ++u)
+        for (int c = 0; c < 2; ++c) {
+            if (c == 1) {  // the second chunk's statistics were requested after its operands
+                lgkm_wait<0>();
 #pragma unroll
-                    for (int hi = 0; hi < 2; ++hi) {
-                        if (c == 0) {
-                            dtr[c][u][hi] = tr_read<0>(db + tr_off[u][hi]);
-                            qtr[c][u][hi] = tr_read<0>(qb + tr_off[u][hi]);
-                        } else {
-                            dtr[c][u][hi] = tr_read<16 * kRowB>(db + tr_off[u][hi]);
-                            qtr[c][u][hi] = tr_read<16 * kRowB>(qb + tr_off[u][hi]);
-                        }
-                    }
-            const bool need_mask = (CAUSAL && kw0 + 31 > qt0) || kw0 + 32 > N || qt0 + 32 > N;
-            // per query chunk c (16 queries): P and dS, then its dV / dK MFMAs, which
-            // run while the next chunk's elementwise work is issued
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                uint32_t pw[4], dsw[4];
+                for (int j = 0; j < 2; ++j) { settle(lv[j]); settle(dl[j]); }
+            }
+            uint32_t pw[4], dsw[4];
+            // the element-wise block, with the mask only on tiles that need it
+            // (a branch around the whole block, so it is not turned into selects)
+            auto elementwise = [&](auto mask_c) {
+                // mask bounds relative to the lane's first query qt0 + 8h; keys past
+                // the end see no query
+                const int dlim = key - qt0 - 8 * h;
+                const int nlim = key < N ? N - qt0 - 8 * h : -1;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     float p[2], ds[2];
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         const int i = 8 * c + 2 * w + e;
-                        float pv = fast_exp2(__builtin_fmaf(s[i], a.c, -lv[i >> 2][i & 3]));
-                        if (need_mask) {
-                            const int qi = qt0 + 16 * (i >> 3) + 8 * h + (i & 7);
-                            if ((CAUSAL && key > qi) || key >= N || qi >= N) pv = 0.f;
+                        const int j = (i >> 2) & 1;
+                        float pv = fast_exp2(__builtin_fmaf(s[i], a.c, -lv[j][i & 3]));
+                        if constexpr (decltype(mask_c)::value) {
+                            // query qt0 + 8h + ci: visible iff ci >= dlim (causal) and ci < nlim
+                            const int ci = 16 * (i >> 3) + (i & 7);
+                            if ((CAUSAL && ci < dlim) || ci >= nlim) pv = 0.f;
                         }
                         p[e] = pv;
-                        ds[e] = pv * (dp[i] - dl[i >> 2][i & 3]);
+                        ds[e] = pv * (dp[i] - dl[j][i & 3]);
                     }
                     pw[w] = T::pack2(p[0], p[1]);
                     dsw[w] = T::pack2(ds[0], ds[1]);
                 }
-                if (c == 0) lgkm_wait<8>();
-                else lgkm_wait<0>();
+            };
+            if (need_mask) elementwise(Masked{});
+            else elementwise(Unmasked{});
+            if (c == 0) {
+                lv[0] = ds_read128f<TO + 64>(st_base);
+                lv[1] = ds_read128f<TO + 80>(st_base);
+                dl[0] = ds_read128f<TO + kKvStatB + 64>(st_base);
+                dl[1] = ds_read128f<TO + kKvStatB + 80>(st_base);
+                lgkm_wait<12>();  // chunk 0's transposed operands (issued first) have landed
+            }
 #pragma unroll
-                for (int u = 0; u < DT; ++u)
+            for (int u = 0; u < DT; ++u)
 #pragma unroll
-                    for (int hi = 0; hi < 2; ++hi) { settle(dtr[c][u][hi]); settle(qtr[c][u][hi]); }
-                const u32x4 pc = {pw[0], pw[1], pw[2], pw[3]};
-                const u32x4 sc = {dsw[0], dsw[1], dsw[2], dsw[3]};
+                for (int hi = 0; hi < 2; ++hi) { settle(dtr[c][u][hi]); settle(qtr[c][u][hi]); }
+            const u32x4 pc = {pw[0], pw[1], pw[2], pw[3]};
+            const u32x4 sc = {dsw[0], dsw[1], dsw[2], dsw[3]};
 #pragma unroll
-                for (int u = 0; u < DT; ++u) {
-                    const u32x4 dA = {dtr[c][u][0][0], dtr[c][u][0][1], dtr[c][u][1][0], dtr[c][u][1][1]};
-                    const u32x4 qA = {qtr[c][u][0][0], qtr[c][u][0][1], qtr[c][u][1][0], qtr[c][u][1][1]};
-                    dv[u] = T::mfma32(dA, pc, dv[u]);
-                    dk[u] = T::mfma32(qA, sc, dk[u]);
-                }
+            for (int u = 0; u < DT; ++u) {
+                const u32x4 dA = {dtr[c][u][0][0], dtr[c][u][0][1], dtr[c][u][1][0], dtr[c][u][1][1]};
+                const u32x4 qA = {qtr[c][u][0][0], qtr[c][u][0][1], qtr[c][u][1][0], qtr[c][u][1][1]};
+                dv[u] = T::mfma32(dA, pc, dv[u]);
+                dk[u] = T::mfma32(qA, sc, dk[u]);
             }
         }
-    }
+    };
 
-    // add the other groups' dK, dV into group 0's (the ring is free: the last
-    // round waited for all of its data and every wave passes the barrier)
-    if constexpr (NG > 1) {
+    for_rounds(nst, [&](auto slot_c, int s) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        // stage s has landed (stage s + 1 may still be in flight); every wave is
+        // done with stage s - 1, whose slot the next issue overwrites
+        if (s + 1 < nst || s == 0) {
+            if (wave < 2) wait_vmcnt<kKvCpw + 1>();
+            else wait_vmcnt<kKvCpw>();
+        } else {
+            wait_vmcnt<0>();
+        }
         barrier();
-        float* mb = reinterpret_cast<float*>(smem);
-        if (grp > 0) {
-            float* w = mb + ((size_t)((grp - 1) * 4 + wl) * 64) * 64 + lane;
-#pragma unroll
-            for (int u = 0; u < DT; ++u)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    w[(16 * u + i) * 64] = dk[u][i];
-                    w[(32 + 16 * u + i) * 64] = dv[u][i];
-                }
-        }
-        __syncthreads();
-        if (grp > 0) return;
-#pragma unroll
-        for (int gg = 1; gg < NG; ++gg) {
-            const float* rsrc = mb + ((size_t)((gg - 1) * 4 + wl) * 64) * 64 + lane;
-#pragma unroll
-            for (int u = 0; u < DT; ++u)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    dk[u][i] += rsrc[(16 * u + i) * 64];
-                    dv[u][i] += rsrc[(32 + 16 * u + i) * 64];
-                }
-        }
-    }
+        if (s + 2 < nst) issue(s + 2, (SLOT + 2) % kSlots);
+        const int g = g0 + s;
+        auto half = [&](auto hh_c) {
+            const int qt0 = g * kKvQRows + 32 * decltype(hh_c)::value;
+            const bool active = kw0 < N && qt0 < N && (!CAUSAL || qt0 + 31 >= kw0);
+            if (!active) return;
+            const bool need_mask = (CAUSAL && kw0 + 31 > qt0) || kw0 + 32 > N || qt0 + 32 > N;
+            unit(slot_c, hh_c, need_mask, qt0);
+        };
+        half(Int<0>{});
+        half(Int<1>{});
+    });
 
     if (key < N) {
         uint16_t* dkp = a.dk + head + (size_t)key * D + 4 * h;
@@ -406,65 +402,59 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     }
 }
 
-// Query workgroup: dQ of 128 queries. Wave group grp takes key blocks grp,
-// grp + NG, ...; every group's wave wl owns the same 32 queries, and the
-// groups' dQ accumulators are added through LDS at the end.
+// Query workgroup: dQ of 128 queries.
 template <typename T, bool CAUSAL>
 __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int grp = wave >> 2, wl = wave & 3;
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
     const int N = a.N;
     const size_t head = (size_t)bh * N * D;
     const uint16_t* __restrict__ K = a.k + head;
     const uint16_t* __restrict__ V = a.v + head;
 
-    const int q0 = qb * kQRows + wl * 32;    // first query of this wave
+    const int q0 = qb * kQRows + wave * 32;  // first query of this wave
     const int qrow = q0 + l32;
     const bool wave_active = q0 < N;
     const int qload = min(qrow, N - 1);
 
     const int nkb_all = (N + kQKeys - 1) / kQKeys;
     const int nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * kQRows) - 1) / kQKeys + 1) : nkb_all;
-    const int nr = (nkb + NG - 1) / NG;  // rounds (NG key blocks each)
+    // blocks this wave computes: 0 .. nkw-1 (causal: up to the one holding its last row)
+    const int nkw = !wave_active ? 0 : (CAUSAL ? min(nkb, min(q0 + 31, N - 1) / kQKeys + 1) : nkb);
 
     f32x16 dqa[DT];
 #pragma unroll
     for (int u = 0; u < DT; ++u) dqa[u] = f32x16{};
 
-    // Ring: kRingRounds rounds of NG stages; stage j of round r holds key block
-    // NG r + j (clamped to the last block past the end, never used): [K block]
-    // [V block], each 64 rows in the swizzled layout. Chunk c of a round is
-    // written by wave c % kWaves.
-    auto issue = [&](int r, int slot) {
-        char* rb = smem + slot * kQRound;
+    // Stage b (key block b, clamped to the last block past the end and then
+    // never used) in slot b % 3: [K block][V block], each 64 rows in the
+    // swizzled layout. Chunk c of a stage is written by wave c % 4.
+    auto issue = [&](int b, int slot) {
+        char* sb = smem + slot * kQStage;
+        const int blk = min(b, nkb - 1);
 #pragma unroll
         for (int u = 0; u < kQCpw; ++u) {
-            const int chunk = u * kWaves + wave;
-            const int j = chunk / (2 * kQTC), cj = chunk % (2 * kQTC);
-            const int blk = min(NG * r + j, nkb - 1);
-            const int p = (cj % kQTC) * 64 + lane;
+            const int chunk = u * 4 + wave;
+            const int p = (chunk % kQTC) * 64 + lane;
             const int row = p / CH, c = (p % CH) ^ swz<D>(row);
-            const uint16_t* src = (cj < kQTC ? K : V) + (size_t)min(blk * kQKeys + row, N - 1) * D + c * 8;
-            dma16(src, rb + j * kQStage + cj * 1024);
+            const uint16_t* src = (chunk < kQTC ? K : V) + (size_t)min(blk * kQKeys + row, N - 1) * D + c * 8;
+            dma16(src, sb + chunk * 1024);
         }
     };
 
+    const uint32_t smem_addr = lds_addr(smem);
     const int s_row = perm32(l32);
-    uint32_t a_off[2][KS];  // K / V operand rows for S^T and dP^T: key tile kt, k-step ks
+    uint32_t a_base[KS];  // K / V operand rows for S^T and dP^T, k-step ks (the second key tile adds 32 rows)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) a_off[kt][ks] = (uint32_t)tile_off<D>(32 * kt + s_row, 2 * ks + h);
-    uint32_t tr_off[DT][2];  // K^T operand for dQ^T += K^T dS^T; key chunks add 16 rows
+    for (int ks = 0; ks < KS; ++ks) a_base[ks] = smem_addr + (uint32_t)tile_off<D>(s_row, 2 * ks + h);
+    uint32_t tr_base[DT][2];  // K^T operand for dQ^T += K^T dS^T; key chunks add 16 rows
 #pragma unroll
     for (int u = 0; u < DT; ++u)
 #pragma unroll
         for (int hi = 0; hi < 2; ++hi)
-            tr_off[u][hi] = (uint32_t)(tile_off<D>(8 * h + (L16 >> 2) + 4 * hi,
-                                                   (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
-                                       (L16 & 1) * 8);
-    const uint32_t smem_addr = lds_addr(smem);
+            tr_base[u][hi] = smem_addr + (uint32_t)(tile_off<D>(8 * h + (L16 >> 2) + 4 * hi,
+                                                                (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
+                                                    (L16 & 1) * 8);
 
     issue(0, 0);
     issue(1, 1);
@@ -483,65 +473,74 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
     const float Dq = a.delta[(size_t)bh * N + qload];
     wait_vmcnt<0>();
 
-    // blocks this wave computes: 0 .. nkw-1 (causal: up to the one holding its last row)
-    const int nkw = !wave_active ? 0 : (CAUSAL ? min(nkb, min(q0 + 31, N - 1) / kQKeys + 1) : nkb);
-    int slot = 0;
-    for (int r = 0; r < nr; ++r) {
-        if (r + 1 < nr || r == 0) wait_vmcnt<kQCpw>();
-        else wait_vmcnt<0>();
-        barrier();
-        if (r + 2 < nr) issue(r + 2, slot == 0 ? kRingRounds - 1 : slot - 1);
-        const uint32_t kbase = smem_addr + (uint32_t)(slot * kQRound + grp * kQStage);
-        const uint32_t vbase = kbase + (uint32_t)kQTileB;
-        slot = slot == kRingRounds - 1 ? 0 : slot + 1;
-        const int kb = NG * r + grp;
-        const int key0 = kb * kQKeys;
-        if (kb >= nkw) continue;
-
+    auto block = [&](auto slot_c, auto mask_c, int key0) {
+        constexpr int KO = decltype(slot_c)::value * kQStage;  // K rows of the stage
+        constexpr int VO = KO + kQTileB;                        // V rows
+        constexpr bool MASK = decltype(mask_c)::value;
         // ---- S^T = K Q^T and dP^T = V dO^T (64 keys x 32 queries; lane = query)
         f32x16 s[2], dp[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        {
             u32x4 ka[KS], va[KS];
-            ka[0] = ds_read128<0>(kbase + a_off[kt][0]);
-            ka[1] = ds_read128<0>(kbase + a_off[kt][1]);
-            ka[2] = ds_read128<0>(kbase + a_off[kt][2]);
-            ka[3] = ds_read128<0>(kbase + a_off[kt][3]);
-            va[0] = ds_read128<0>(vbase + a_off[kt][0]);
-            va[1] = ds_read128<0>(vbase + a_off[kt][1]);
-            va[2] = ds_read128<0>(vbase + a_off[kt][2]);
-            va[3] = ds_read128<0>(vbase + a_off[kt][3]);
+            ka[0] = ds_read128<KO>(a_base[0]);
+            ka[1] = ds_read128<KO>(a_base[1]);
+            ka[2] = ds_read128<KO>(a_base[2]);
+            ka[3] = ds_read128<KO>(a_base[3]);
+            va[0] = ds_read128<VO>(a_base[0]);
+            va[1] = ds_read128<VO>(a_base[1]);
+            va[2] = ds_read128<VO>(a_base[2]);
+            va[3] = ds_read128<VO>(a_base[3]);
             lgkm_wait<0>();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) { settle(ka[ks]); settle(va[ks]); }
-            s[kt] = f32x16{};
-            dp[kt] = f32x16{};
+            s[0] = dp[0] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                s[kt] = T::mfma32(ka[ks], qf[ks], s[kt]);
-                dp[kt] = T::mfma32(va[ks], dof[ks], dp[kt]);
+                s[0] = T::mfma32(ka[ks], qf[ks], s[0]);
+                dp[0] = T::mfma32(va[ks], dof[ks], dp[0]);
             }
         }
-        // K^T operands of the whole block, issued before the elementwise work
+        {
+            u32x4 ka[KS], va[KS];
+            ka[0] = ds_read128<KO + 32 * kRowB>(a_base[0]);
+            ka[1] = ds_read128<KO + 32 * kRowB>(a_base[1]);
+            ka[2] = ds_read128<KO + 32 * kRowB>(a_base[2]);
+            ka[3] = ds_read128<KO + 32 * kRowB>(a_base[3]);
+            va[0] = ds_read128<VO + 32 * kRowB>(a_base[0]);
+            va[1] = ds_read128<VO + 32 * kRowB>(a_base[1]);
+            va[2] = ds_read128<VO + 32 * kRowB>(a_base[2]);
+            va[3] = ds_read128<VO + 32 * kRowB>(a_base[3]);
+            lgkm_wait<0>();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) { settle(ka[ks]); settle(va[ks]); }
+            s[1] = dp[1] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                s[1] = T::mfma32(ka[ks], qf[ks], s[1]);
+                dp[1] = T::mfma32(va[ks], dof[ks], dp[1]);
+            }
+        }
+        // K^T operands of the whole block (key chunks 0 and 1 first), issued
+        // before the element-wise work
         u32x2 ktr[4][DT][2];
 #pragma unroll
         for (int u = 0; u < DT; ++u)
 #pragma unroll
             for (int hi = 0; hi < 2; ++hi) {
-                ktr[0][u][hi] = tr_read<0 * 16 * kRowB>(kbase + tr_off[u][hi]);
-                ktr[1][u][hi] = tr_read<1 * 16 * kRowB>(kbase + tr_off[u][hi]);
+                ktr[0][u][hi] = tr_read<KO + 0 * 16 * kRowB>(tr_base[u][hi]);
+                ktr[1][u][hi] = tr_read<KO + 1 * 16 * kRowB>(tr_base[u][hi]);
             }
 #pragma unroll
         for (int u = 0; u < DT; ++u)
 #pragma unroll
             for (int hi = 0; hi < 2; ++hi) {
-                ktr[2][u][hi] = tr_read<2 * 16 * kRowB>(kbase + tr_off[u][hi]);
-                ktr[3][u][hi] = tr_read<3 * 16 * kRowB>(kbase + tr_off[u][hi]);
+                ktr[2][u][hi] = tr_read<KO + 2 * 16 * kRowB>(tr_base[u][hi]);
+                ktr[3][u][hi] = tr_read<KO + 3 * 16 * kRowB>(tr_base[u][hi]);
             }
+        const int qlim = qrow - key0 - 8 * h;  // mask bounds relative to key0 + 8h
+        const int nlim = N - key0 - 8 * h;
         // ---- per key tile kt: dS^T = P^T (dP^T - D) with P^T = exp2(S^T c - lse2),
         // then dQ^T (64 dims x 32 queries) += K^T dS^T over its two 16-key chunks;
-        // those MFMAs run while the next tile's elementwise work is issued
-        const bool need_mask = (CAUSAL && key0 + kQKeys - 1 > q0) || (key0 + kQKeys > N);
+        // those MFMAs run while the next tile's element-wise work is issued
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             uint32_t dsw[8];
@@ -552,9 +551,10 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
                 for (int e = 0; e < 2; ++e) {
                     const int i = 2 * w + e;
                     float pv = fast_exp2(__builtin_fmaf(s[kt][i], a.c, -l2q));
-                    if (need_mask) {
-                        const int kj = key0 + 32 * kt + 16 * (i >> 3) + 8 * h + (i & 7);
-                        if ((CAUSAL && kj > qrow) || kj >= N) pv = 0.f;
+                    if constexpr (MASK) {
+                        // key key0 + 8h + ci: visible iff ci <= qlim (causal) and ci < nlim
+                        const int ci = 32 * kt + 16 * (i >> 3) + (i & 7);
+                        if ((CAUSAL && ci > qlim) || ci >= nlim) pv = 0.f;
                     }
                     ds[e] = pv * (dp[kt][i] - Dq);
                 }
@@ -576,29 +576,20 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
                 }
             }
         }
-    }
+    };
 
-    if constexpr (NG > 1) {
+    for_rounds(nkb, [&](auto slot_c, int kb) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        if (kb + 1 < nkb || kb == 0) wait_vmcnt<kQCpw>();
+        else wait_vmcnt<0>();
         barrier();
-        float* mb = reinterpret_cast<float*>(smem);
-        if (grp > 0) {
-            float* w = mb + ((size_t)((grp - 1) * 4 + wl) * 32) * 64 + lane;
-#pragma unroll
-            for (int u = 0; u < DT; ++u)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) w[(16 * u + i) * 64] = dqa[u][i];
-        }
-        __syncthreads();
-        if (grp > 0) return;
-#pragma unroll
-        for (int gg = 1; gg < NG; ++gg) {
-            const float* rsrc = mb + ((size_t)((gg - 1) * 4 + wl) * 32) * 64 + lane;
-#pragma unroll
-            for (int u = 0; u < DT; ++u)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) dqa[u][i] += rsrc[(16 * u + i) * 64];
-        }
-    }
+        if (kb + 2 < nkb) issue(kb + 2, (SLOT + 2) % kSlots);
+        if (kb >= nkw) return;
+        const int key0 = kb * kQKeys;
+        const bool need_mask = (CAUSAL && key0 + kQKeys - 1 > q0) || (key0 + kQKeys > N);
+        if (need_mask) block(slot_c, Masked{}, key0);
+        else block(slot_c, Unmasked{}, key0);
+    });
 
     if (wave_active && qrow < N) {
         uint16_t* qp = a.dq + head + (size_t)qrow * D + 4 * h;
@@ -616,7 +607,7 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
 }
 
 template <typename T, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_fused_kernel(FusedArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_fused_kernel(FusedArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[kSmem];
     int bh, blk;
     bool is_q;
@@ -649,12 +640,12 @@ hipError_t bwd_prep(const void* o, const void* dout, const float* lse, int B, in
     p.delta = delta;
     p.lse2 = lse2;
     p.rows = (int64_t)B * H * N;
-    constexpr int RPB = kPrepThreads / (D / 8);
+    constexpr int RPB = kThreads / (D / 8);
     const dim3 grid((unsigned)((p.rows + RPB - 1) / RPB));
     if (dtype == 0)
-        hipLaunchKernelGGL((bwd_prep_kernel<Bf16>), grid, dim3(kPrepThreads), 0, stream, p);
+        hipLaunchKernelGGL((bwd_prep_kernel<Bf16>), grid, dim3(kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((bwd_prep_kernel<F16>), grid, dim3(kPrepThreads), 0, stream, p);
+        hipLaunchKernelGGL((bwd_prep_kernel<F16>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -681,4 +672,3 @@ hipError_t bwd_fused(const void* q, const void* k, const void* v, const void* do
 }
 
 }  // namespace fa
-
