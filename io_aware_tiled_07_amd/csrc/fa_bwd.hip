@@ -49,8 +49,6 @@ namespace fa {
 
 namespace {
 
-template <int V>
-using Int = std::integral_constant<int, V>;
 using Masked = std::true_type;
 using Unmasked = std::false_type;
 
@@ -150,17 +148,6 @@ __device__ __forceinline__ void map_fused(int bid, const FusedArgs& a, bool caus
     is_q = s & 1;
     const int i = s >> 1;
     blk = is_q ? (causal ? a.nblk - 1 - i : i) : i;
-}
-
-// Run body(Int<slot>{}, r) for r = 0 .. n-1 with slot = r % kSlots known at
-// compile time.
-template <typename F>
-__device__ __forceinline__ void for_rounds(int n, F&& body) {
-    for (int r = 0; r < n; r += kSlots) {
-        body(Int<0>{}, r);
-        if (r + 1 < n) body(Int<1>{}, r + 1);
-        if (r + 2 < n) body(Int<2>{}, r + 2);
-    }
 }
 
 // Key workgroup: dK and dV of 128 keys.
@@ -360,7 +347,7 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         }
     };
 
-    for_rounds(nst, [&](auto slot_c, int s) {
+    for_ring<kSlots>(nst, [&](auto slot_c, int s) {
         constexpr int SLOT = decltype(slot_c)::value;
         // stage s has landed (stage s + 1 may still be in flight); every wave is
         // done with stage s - 1, whose slot the next issue overwrites
@@ -578,7 +565,7 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
         }
     };
 
-    for_rounds(nkb, [&](auto slot_c, int kb) {
+    for_ring<kSlots>(nkb, [&](auto slot_c, int kb) {
         constexpr int SLOT = decltype(slot_c)::value;
         if (kb + 1 < nkb || kb == 0) wait_vmcnt<kQCpw>();
         else wait_vmcnt<0>();

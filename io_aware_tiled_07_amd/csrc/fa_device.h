@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -103,6 +105,45 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
 // Completion is tracked by the wave's vmcnt, not by lgkmcnt.
 __device__ __forceinline__ void dma16(const void* src, char* lds_base) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+template <int V>
+using Int = std::integral_constant<int, V>;
+
+// body(Int<r % S>{}, r) for r = 0 .. n-1 (S <= 3): the ring slot of round r is a
+// compile-time constant inside the body, so LDS offsets become immediates.
+template <int S, typename F>
+__device__ __forceinline__ void for_ring(int n, F&& body) {
+    static_assert(S >= 1 && S <= 3, "ring depth");
+    for (int r = 0; r < n; r += S) {
+        body(Int<0>{}, r);
+        if constexpr (S > 1) if (r + 1 < n) body(Int<1>{}, r + 1);
+        if constexpr (S > 2) if (r + 2 < n) body(Int<2>{}, r + 2);
+    }
+}
+
+// buffer_load_dwordx4 ... lds: the same 16-byte-per-lane copy, addressed as
+// a wave-uniform buffer resource plus a per-lane byte offset. A lane whose
+// offset lies at or past the resource's byte count reads zeros, so a block
+// that runs past the end of a tensor needs no clamping.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ void amdgcn_raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) void* lds, int size,
+                                           int voffset, int soffset, int offset,
+                                           int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Raw (unstrided) resource over [base, base + bytes); base and bytes must be
+// wave-uniform (they are read from the first lane).
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu));  // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;  // gfx9 buffer format word: 32-bit data, no swizzle
+    return r;
+}
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voffset, char* lds_base) {
+    amdgcn_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_base, 16, (int)voffset, 0, 0, 0);
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).

@@ -12,8 +12,12 @@
 // gfx950 mapping:
 //  * A workgroup is 4 waves and owns 128 query rows of one (batch, head); each
 //    wave owns 32 rows. The Q tile stays in VGPRs for the whole kernel.
-//  * K and V blocks of 64 keys are staged HBM -> VGPR -> LDS (16-byte coalesced
-//    loads, XOR-swizzled rows, double buffered, one barrier per block).
+//  * K and V blocks of 64 keys stream through a ring of LDS stages (three at
+//    head dim 64, two at 128) filled by buffer_load ... lds (16 bytes per lane,
+//    XOR-swizzled rows, one barrier per block). Rows past the end of the
+//    sequence read as zeros, so the ragged last block needs no clamping. The
+//    ring slot is a compile-time constant in the unrolled loop body, so every
+//    LDS read is a loop-invariant base register plus an immediate offset.
 //  * The scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16:
 //    each lane then holds 16 of the 64 scores of ONE query row (its partner
 //    lane l^32 holds 16 more per 32-key tile), so the row max needs a single
@@ -23,12 +27,16 @@
 //    MFMA: O^T += V^T P^T takes P straight from registers (rounded to the
 //    input type), and V^T comes from row-major LDS through the gfx950
 //    transposed read ds_read_b64_tr_b16.
-//  * Softmax runs in base 2 with scale*log2(e) folded into one FMA. A row's
-//    reference maximum only moves when the block maximum exceeds it by more
-//    than 2^8 (weights then stay <= 256: exact in fp32, and bf16/fp16 keep
-//    their relative precision), so O is rarely rescaled. The row sum adds the
-//    rounded weights in pairs (v_dot2c_f32 against (1, 1)), so numerator and
-//    denominator use the same values.
+//  * Softmax runs in base 2 with scale*log2(e) folded into one FMA. The
+//    weights of each 32-key tile are formed against the row's current
+//    reference maximum straight away; only when some lane's rounded weights
+//    sum to 2^8 or more is the reference moved to the tile's row maximum, O
+//    and l rescaled and the tile's weights formed again. Every weight kept is
+//    therefore below 2^8 (exact in fp32, and bf16/fp16 keep their relative
+//    precision), the row maximum is computed only when it is needed, and O is
+//    rarely rescaled. The row sum adds the rounded weights in pairs
+//    (v_dot2c_f32 against (1, 1)), so numerator and denominator use the same
+//    values.
 //  * Causal: key blocks above the diagonal are never loaded, whole waves skip
 //    blocks above their rows, and only blocks crossing the diagonal (or the
 //    ragged end of the sequence) are masked element by element.
@@ -44,13 +52,15 @@ namespace {
 
 constexpr int kBc = 64;  // keys per block
 
-// Tuning knobs (compile-time): query rows per wave = 32 * QT, waves per workgroup = NW.
-#ifndef FA_FWD_QT
-#define FA_FWD_QT 1
-#endif
+// Tuning knob (compile-time): waves per workgroup, 32 query rows each.
 #ifndef FA_FWD_NW
 #define FA_FWD_NW 4
 #endif
+
+// A wave re-centres its running maximum only when the rounded weights of a
+// 16-key slice sum to at least this much in one lane (so every weight it keeps
+// is below it: exact in fp32, and bf16/fp16 keep their relative precision).
+constexpr float kRecentre = 256.f;
 
 struct FwdArgs {
     const uint16_t* q;
@@ -76,7 +86,7 @@ __device__ __forceinline__ void map_block(int bid, const FwdArgs& a, int& bh, in
     }
 }
 
-template <typename T, int D, bool CAUSAL, int QT, int NW>
+template <typename T, int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     constexpr int KS = D / 16;           // k-steps of the score MFMA
     constexpr int DT = D / 32;           // 32-wide output tiles
@@ -85,270 +95,238 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     constexpr int TB = kBc * D * 2;      // bytes of one K or V block
     constexpr int SB = 2 * TB;           // one ring stage: K block, then V block
     constexpr int KCH = TB / 1024;       // 1 KiB DMA chunks per block
-    constexpr int CPW = 2 * KCH / NW;    // DMA instructions per wave per stage
-    constexpr int ROWS = 32 * QT;        // query rows per wave
-    constexpr int BR = ROWS * NW;        // query rows per workgroup
-    static_assert(CPW * NW == 2 * KCH, "stage must split evenly over the waves");
+    constexpr int HALF = KCH / NW;       // DMA instructions per wave per block
+    constexpr int BR = 32 * NW;          // query rows per workgroup
+    static_assert(HALF * NW == KCH, "block must split evenly over the waves");
+    static_assert((STAGES - 1) * SB + TB + 3 * 16 * 2 * D < 65536, "ds offsets must fit 16 bits");
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5, l32 = lane & 31;
     int bh, qb;
     map_block(blockIdx.x, a, bh, qb);
     const int N = a.N;
     const size_t head = (size_t)bh * N * D;
     const uint16_t* __restrict__ Q = a.q + head;
-    const uint16_t* __restrict__ K = a.k + head;
-    const uint16_t* __restrict__ V = a.v + head;
+    const char* __restrict__ K = reinterpret_cast<const char*>(a.k + head);
+    const char* __restrict__ V = reinterpret_cast<const char*>(a.v + head);
 
-    const int q0 = qb * BR + wave * ROWS;  // first query row of this wave
+    const int q0 = qb * BR + wave * 32;  // first query row of this wave
     const bool wave_active = q0 < N;
-
 
     const int nkb_all = (N + kBc - 1) / kBc;
     const int nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * BR) - 1) / kBc + 1) : nkb_all;
 
-    f32x16 oacc[QT][DT];
-    float m_run[QT], l_run[QT];
+    f32x16 oacc[DT];
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-        m_run[t] = kMaskFloor;
-        l_run[t] = 0.f;
-#pragma unroll
-        for (int u = 0; u < DT; ++u) oacc[t][u] = f32x16{};
-    }
+    for (int u = 0; u < DT; ++u) oacc[u] = f32x16{};
+    float m_run = kMaskFloor, l_run = 0.f;
 
     // Ring of STAGES key/value blocks filled by LDS-DMA. Chunk j (1 KiB) of a
-    // stage is written by wave j % NW; lane l of it carries granule 64*(j % KCH) + l
-    // of the K (j < KCH) or V block, i.e. row r, stored chunk sc, logical chunk
-    // sc ^ swz(r) of the block.
-    auto issue = [&](int kb, int st) {
-        char* sb = smem + st * SB;
+    // block is written by wave j % NW; lane l of it carries granule 64 j + l,
+    // i.e. row r, stored chunk sc, logical chunk sc ^ swz(r) of the block. The
+    // same lane offsets serve the K and the V block; rows past the end of the
+    // sequence read as zeros (and are masked).
+    uint32_t dma_off[HALF];  // byte offset of the lane's granule from the block's first row
 #pragma unroll
-        for (int u = 0; u < CPW; ++u) {
-            const int chunk = u * NW + wave;
-            const int p = (chunk % KCH) * 64 + lane;
-            const int r = p / CH, c = (p % CH) ^ swz<D>(r);
-            const uint16_t* src = (chunk < KCH ? K : V) + (size_t)min(kb * kBc + r, N - 1) * D + c * 8;
-            dma16(src, sb + chunk * 1024);
-        }
+    for (int j = 0; j < HALF; ++j) {
+        const int p = (j * NW + wave) * 64 + lane;
+        const int r = p / CH, c = (p % CH) ^ swz<D>(r);
+        dma_off[j] = (uint32_t)((r * D + c * 8) * 2);
+    }
+    auto issue = [&](int kb, auto slot_c) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        const int row0 = kb * kBc;
+        const uint32_t left = (uint32_t)(N - row0) * D * 2;
+        const i32x4 kr = buffer_rsrc(K + (size_t)row0 * D * 2, left);
+        const i32x4 vr = buffer_rsrc(V + (size_t)row0 * D * 2, left);
+        char* sb = smem + SLOT * SB + wave * 1024;
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) dma16(kr, dma_off[j], sb + j * NW * 1024);
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) dma16(vr, dma_off[j], sb + TB + j * NW * 1024);
     };
 
-    // Transposed V read: lane L of 16-lane group g addresses row 16c + 8h + L/4 (+4 for
-    // the second half of the operand), columns 32u + 16(g&1) + 4(L&3). The row
-    // swizzle depends only on row bits 1..3, so the 16c part is an immediate offset.
+    // Loop-invariant LDS addresses; slot, key tile and key chunk are immediates.
+    // K operand of S^T = K Q^T: row perm32(l32) (+32 for the second key tile),
+    // k-step ks. Transposed V read: lane L of 16-lane group g addresses row
+    // 16c + 8h + L/4 (+4 for the second half of the operand), columns
+    // 32u + 16(g&1) + 4(L&3); the row swizzle depends only on row bits 1..3, so
+    // the 16c part is an immediate offset.
+    const uint32_t smem_addr = lds_addr(smem);
     const int g16 = lane >> 4, L16 = lane & 15;
-    uint32_t tr_addr[DT][2];
+    uint32_t tr_base[DT][2];
 #pragma unroll
     for (int u = 0; u < DT; ++u)
 #pragma unroll
         for (int hi = 0; hi < 2; ++hi)
-            tr_addr[u][hi] = (uint32_t)(TB + tile_off<D>(8 * h + (L16 >> 2) + 4 * hi,
-                                                         (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
-                                        (L16 & 1) * 8);
-    const uint32_t smem_addr = lds_addr(smem);
+            tr_base[u][hi] = smem_addr + (uint32_t)(tile_off<D>(8 * h + (L16 >> 2) + 4 * hi,
+                                                                (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
+                                                    (L16 & 1) * 8);
     const int s_row = perm32(l32);
-    uint32_t a_off[KS];  // K operand rows for S^T, k-step ks (the second key tile adds 32 rows)
+    uint32_t a_base[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a_off[ks] = (uint32_t)tile_off<D>(s_row, 2 * ks + h);
+    for (int ks = 0; ks < KS; ++ks) a_base[ks] = smem_addr + (uint32_t)tile_off<D>(s_row, 2 * ks + h);
 
-    issue(0, 0);
-    if (STAGES == 3 && nkb > 1) issue(1, 1);
+    issue(0, Int<0>{});
+    if (STAGES == 3 && nkb > 1) issue(1, Int<1>{});
 
     // Q fragments: B operand of S^T = K Q^T (column = query, k = head dim).
     // Loaded after the first ring stages are requested so the latencies
     // overlap; the full wait tells the compiler's wait pass that no load into a
     // register is pending inside the loop (else it drains the ring there).
-    u32x4 qf[QT][KS];
+    u32x4 qf[KS];
+    {
+        const uint16_t* qp = Q + (size_t)min(q0 + l32, N - 1) * D + 8 * h;
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-        const uint16_t* qp = Q + (size_t)min(q0 + 32 * t + l32, N - 1) * D + 8 * h;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[t][ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
     }
     wait_vmcnt<0>();
 
-    for (int kb = 0; kb < nkb; ++kb) {
+    for_ring<STAGES>(nkb, [&](auto slot_c, int kb) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        constexpr int BASE = SLOT * SB;
         // this wave's share of block kb has landed; then every wave's has, and
         // every wave is done reading the stage the next issue overwrites
-        if (STAGES == 3 && kb + 1 < nkb) wait_vmcnt<CPW>();
+        if (STAGES == 3 && kb + 1 < nkb) wait_vmcnt<2 * HALF>();
         else wait_vmcnt<0>();
         barrier();
         if constexpr (STAGES == 3) {
-            if (kb + 2 < nkb) issue(kb + 2, (kb + 2) % 3);
+            if (kb + 2 < nkb) issue(kb + 2, Int<(SLOT + 2) % 3>{});
         } else {
-            if (kb + 1 < nkb) issue(kb + 1, (kb + 1) & 1);
+            if (kb + 1 < nkb) issue(kb + 1, Int<(SLOT + 1) % 2>{});
         }
         const int key0 = kb * kBc;
-        if (!wave_active || (CAUSAL && key0 > q0 + ROWS - 1)) continue;
+        if (!wave_active || (CAUSAL && key0 > q0 + 31)) return;
 
-        // ---- S^T (64 keys x 32 queries per query tile): two 32x32 tiles each.
-        // All K operand reads go out first so their LDS latency overlaps.
-        const uint32_t stage_addr = smem_addr + (uint32_t)((kb % STAGES) * SB);
+        // ---- S^T (64 keys x 32 queries): two 32x32 tiles. All K operand reads
+        // go out first so their LDS latency overlaps.
         u32x4 ka[KS][2];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            ka[ks][0] = ds_read128<0>(stage_addr + a_off[ks]);
-            ka[ks][1] = ds_read128<32 * 2 * D>(stage_addr + a_off[ks]);
+            ka[ks][0] = ds_read128<BASE>(a_base[ks]);
+            ka[ks][1] = ds_read128<BASE + 32 * 2 * D>(a_base[ks]);
         }
         lgkm_wait<0>();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) { settle(ka[ks][0]); settle(ka[ks][1]); }
-        f32x16 s[QT][2];
-#pragma unroll
-        for (int t = 0; t < QT; ++t) s[t][0] = s[t][1] = f32x16{};
+        f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
+            for (int kt = 0; kt < 2; ++kt) s[kt] = T::mfma32(ka[ks][kt], qf[ks], s[kt]);
+
+        // V^T operands for the whole block, issued now so they land during the
+        // softmax. Head dim 64: chunk by chunk, so that chunks 0 and 1 (the
+        // first 32 keys) land first; head dim 128: dim tile by dim tile.
+        u32x2 vlo[4][DT], vhi[4][DT];
+        auto vread = [&](auto c_c, int u) {
+            constexpr int C = decltype(c_c)::value;
+            vlo[C][u] = tr_read<BASE + TB + C * 16 * 2 * D>(tr_base[u][0]);
+            vhi[C][u] = tr_read<BASE + TB + C * 16 * 2 * D>(tr_base[u][1]);
+        };
+        if constexpr (DT == 2) {
+#pragma unroll
+            for (int u = 0; u < DT; ++u) { vread(Int<0>{}, u); vread(Int<1>{}, u); }
+#pragma unroll
+            for (int u = 0; u < DT; ++u) { vread(Int<2>{}, u); vread(Int<3>{}, u); }
+        } else {
+#pragma unroll
+            for (int u = 0; u < DT; ++u) {
+                vread(Int<0>{}, u); vread(Int<1>{}, u); vread(Int<2>{}, u); vread(Int<3>{}, u);
+            }
+        }
+
+        // ---- mask: causal diagonal block and ragged end of the sequence.
+        // Register i of key tile kt holds key key0 + 32 kt + 16 (i/8) + 8 h + i%8.
+        if ((CAUSAL && key0 + kBc - 1 > q0) || key0 + kBc > N) {
+            const int qrow = q0 + l32;
+            const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - key0 - 8 * h;  // last visible offset
+#pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int t = 0; t < QT; ++t) s[t][kt] = T::mfma32(ka[ks][kt], qf[t][ks], s[t][kt]);
-
-        // V^T operands for the whole block, issued before the softmax so they land meanwhile
-        u32x2 vlo[4][DT], vhi[4][DT];
-        {
-            // head dim 64: chunk by chunk, so that chunks 0 and 1 (the first 32
-            // keys) land first; head dim 128: dim tile by dim tile
-            const uint32_t stage_addr = smem_addr + (uint32_t)((kb % STAGES) * SB);
-            if constexpr (DT == 2) {
-#pragma unroll
-                for (int u = 0; u < DT; ++u) {
-                    vlo[0][u] = tr_read<0 * 16 * 2 * D>(stage_addr + tr_addr[u][0]);
-                    vhi[0][u] = tr_read<0 * 16 * 2 * D>(stage_addr + tr_addr[u][1]);
-                    vlo[1][u] = tr_read<1 * 16 * 2 * D>(stage_addr + tr_addr[u][0]);
-                    vhi[1][u] = tr_read<1 * 16 * 2 * D>(stage_addr + tr_addr[u][1]);
-                }
-#pragma unroll
-                for (int u = 0; u < DT; ++u) {
-                    vlo[2][u] = tr_read<2 * 16 * 2 * D>(stage_addr + tr_addr[u][0]);
-                    vhi[2][u] = tr_read<2 * 16 * 2 * D>(stage_addr + tr_addr[u][1]);
-                    vlo[3][u] = tr_read<3 * 16 * 2 * D>(stage_addr + tr_addr[u][0]);
-                    vhi[3][u] = tr_read<3 * 16 * 2 * D>(stage_addr + tr_addr[u][1]);
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < DT; ++u) {
-                    const uint32_t a0 = stage_addr + tr_addr[u][0], a1 = stage_addr + tr_addr[u][1];
-                    vlo[0][u] = tr_read<0 * 16 * 2 * D>(a0); vhi[0][u] = tr_read<0 * 16 * 2 * D>(a1);
-                    vlo[1][u] = tr_read<1 * 16 * 2 * D>(a0); vhi[1][u] = tr_read<1 * 16 * 2 * D>(a1);
-                    vlo[2][u] = tr_read<2 * 16 * 2 * D>(a0); vhi[2][u] = tr_read<2 * 16 * 2 * D>(a1);
-                    vlo[3][u] = tr_read<3 * 16 * 2 * D>(a0); vhi[3][u] = tr_read<3 * 16 * 2 * D>(a1);
-                }
-            }
+                for (int i = 0; i < 16; ++i)
+                    if (32 * kt + 16 * (i >> 3) + (i & 7) > lim) s[kt][i] = -INFINITY;
         }
 
-        uint32_t pk[QT][2][8];
-#pragma unroll
-        for (int t = 0; t < QT; ++t) {
-            // ---- mask: causal diagonal block and ragged end of the sequence.
-            // Register i of key tile kt holds key key0 + 32 kt + 16 (i/8) + 8 h + i%8.
-            const bool need_mask = (CAUSAL && key0 + kBc - 1 > q0 + 32 * t) || (key0 + kBc > N);
-            if (need_mask) {
-                const int qrow = q0 + 32 * t + l32;
-                const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - key0 - 8 * h;  // last visible offset
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (32 * kt + 16 * (i >> 3) + (i & 7) > lim) s[t][kt][i] = -INFINITY;
-            }
-            // ---- online softmax (base 2)
-            float mx = s[t][0][0];
-#pragma unroll
-            for (int i = 1; i < 16; i += 2) mx = max3(mx, s[t][0][i], s[t][0][i + 1]);
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) mx = max3(mx, s[t][1][i], s[t][1][i + 1]);
-            mx = pair_max(mx) * a.c;
-            const bool grow = mx > m_run[t] + 8.f;
-            if (__ballot(grow)) {
-                const float m_new = grow ? mx : m_run[t];
-                const float alpha = fast_exp2(m_run[t] - m_new);
-                l_run[t] *= alpha;
-#pragma unroll
-                for (int u = 0; u < DT; ++u) oacc[t][u] *= alpha;
-                m_run[t] = m_new;
-            }
-        }
-        // ---- weights of the first 32 keys, their O^T += V^T P^T MFMAs (which run
-        // while the weights of the other 32 keys are formed), then the rest. At
-        // head dim 128 the V^T operands already fill the registers, so there all
-        // weights are formed before the MFMAs.
-        constexpr bool kSplit = DT == 2;
-        float lsum[QT];
-#pragma unroll
-        for (int t = 0; t < QT; ++t) lsum[t] = 0.f;
+        // ---- online softmax (base 2), one 32-key tile at a time. The weights
+        // are formed against the current reference maximum first; only if some
+        // lane's rounded weights reach kRecentre is the maximum moved to the
+        // tile's row maximum, O and l rescaled and the weights formed again.
+        // The row sum adds the rounded weights in pairs (v_dot2c_f32 against
+        // (1, 1)), so numerator and denominator use the same values.
+        uint32_t pk[2][8];
         auto weights = [&](int kt) {
+            float sum = 0.f;
 #pragma unroll
-            for (int t = 0; t < QT; ++t)
-#pragma unroll
-                for (int w = 0; w < 8; ++w) {
-                    const float p0 = fast_exp2(__builtin_fmaf(s[t][kt][2 * w], a.c, -m_run[t]));
-                    const float p1 = fast_exp2(__builtin_fmaf(s[t][kt][2 * w + 1], a.c, -m_run[t]));
-                    pk[t][kt][w] = T::pack2(p0, p1);
-                    lsum[t] = T::sum2(pk[t][kt][w], lsum[t]);
-                }
+            for (int w = 0; w < 8; ++w) {
+                const float p0 = fast_exp2(__builtin_fmaf(s[kt][2 * w], a.c, -m_run));
+                const float p1 = fast_exp2(__builtin_fmaf(s[kt][2 * w + 1], a.c, -m_run));
+                pk[kt][w] = T::pack2(p0, p1);
+                sum = T::sum2(pk[kt][w], sum);
+            }
+            return sum;
         };
-        if constexpr (!kSplit) {
-            weights(0);
-            weights(1);
-            lgkm_wait<0>();
-        }
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-            if constexpr (kSplit) {
-                weights(kt);
-                if (kt == 0) lgkm_wait<(kSplit ? 4 * DT : 0)>();
-                else lgkm_wait<0>();
+            float sum = weights(kt);
+            if (__ballot(!(sum < kRecentre))) {
+                float mx = s[kt][0];
+#pragma unroll
+                for (int i = 1; i < 15; i += 2) mx = max3(mx, s[kt][i], s[kt][i + 1]);
+                mx = pair_max(max(mx, s[kt][15])) * a.c;
+                const float m_new = max(m_run, mx);
+                const float alpha = fast_exp2(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int u = 0; u < DT; ++u) oacc[u] *= alpha;
+                m_run = m_new;
+                sum = weights(kt);
             }
+            l_run += sum;
+            if (kt == 0) lgkm_wait<(DT == 2 ? 4 * DT : 0)>();
+            else lgkm_wait<0>();
+            // ---- O^T += V^T P^T over the tile's two 16-key chunks
 #pragma unroll
             for (int c = 2 * kt; c < 2 * kt + 2; ++c)
 #pragma unroll
                 for (int u = 0; u < DT; ++u) { settle(vlo[c][u]); settle(vhi[c][u]); }
 #pragma unroll
-            for (int c = 2 * kt; c < 2 * kt + 2; ++c) {
+            for (int c = 2 * kt; c < 2 * kt + 2; ++c)
 #pragma unroll
                 for (int u = 0; u < DT; ++u) {
                     const u32x4 va = {vlo[c][u][0], vlo[c][u][1], vhi[c][u][0], vhi[c][u][1]};
-#pragma unroll
-                    for (int t = 0; t < QT; ++t) {
-                        const u32x4 pb = {pk[t][kt][4 * (c & 1) + 0], pk[t][kt][4 * (c & 1) + 1],
-                                          pk[t][kt][4 * (c & 1) + 2], pk[t][kt][4 * (c & 1) + 3]};
-                        oacc[t][u] = T::mfma32(va, pb, oacc[t][u]);
-                    }
+                    const u32x4 pb = {pk[kt][4 * (c & 1) + 0], pk[kt][4 * (c & 1) + 1],
+                                      pk[kt][4 * (c & 1) + 2], pk[kt][4 * (c & 1) + 3]};
+                    oacc[u] = T::mfma32(va, pb, oacc[u]);
                 }
-            }
         }
-#pragma unroll
-        for (int t = 0; t < QT; ++t) l_run[t] += lsum[t];
-    }
+    });
 
     // ---- epilogue: O = O_acc / l, lse = ln2 * (m + log2 l)
+    const float l_tot = pair_sum(l_run);
+    const int qrow = q0 + l32;
+    if (wave_active && qrow < N) {
+        const float inv = 1.f / l_tot;
+        uint16_t* op = a.o + head + (size_t)qrow * D + 4 * h;
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-        const float l_tot = pair_sum(l_run[t]);
-        const int qrow = q0 + 32 * t + l32;
-        if (wave_active && qrow < N) {
-            const float inv = 1.f / l_tot;
-            uint16_t* op = a.o + head + (size_t)qrow * D + 4 * h;
+        for (int u = 0; u < DT; ++u) {
 #pragma unroll
-            for (int u = 0; u < DT; ++u) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const u32x2 w = {T::pack2(oacc[t][u][4 * g] * inv, oacc[t][u][4 * g + 1] * inv),
-                                     T::pack2(oacc[t][u][4 * g + 2] * inv, oacc[t][u][4 * g + 3] * inv)};
-                    *reinterpret_cast<u32x2*>(op + 32 * u + 8 * g) = w;
-                }
+            for (int g = 0; g < 4; ++g) {
+                const u32x2 w = {T::pack2(oacc[u][4 * g] * inv, oacc[u][4 * g + 1] * inv),
+                                 T::pack2(oacc[u][4 * g + 2] * inv, oacc[u][4 * g + 3] * inv)};
+                *reinterpret_cast<u32x2*>(op + 32 * u + 8 * g) = w;
             }
-            if (h == 0) a.lse[(size_t)bh * N + qrow] = (m_run[t] + __log2f(l_tot)) * kLn2;
         }
+        if (h == 0) a.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
     }
 }
 
 template <int D>
-struct FwdShape {  // rows per wave (as 32-row tiles) and waves per workgroup for head dim D
-    static constexpr int QT = D == 64 ? FA_FWD_QT : 1;
+struct FwdShape {  // waves per workgroup and query rows per workgroup
     static constexpr int NW = FA_FWD_NW;
-    static constexpr int BR = 32 * QT * NW;
+    static constexpr int BR = 32 * NW;
 };
 
 template <typename T, int D, bool C>
@@ -356,7 +334,7 @@ hipError_t launch(FwdArgs a, hipStream_t stream) {
     using S = FwdShape<D>;
     a.nqb = (a.N + S::BR - 1) / S::BR;
     a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
-    hipLaunchKernelGGL((fwd_kernel<T, D, C, S::QT, S::NW>), dim3(a.BH * a.nqb), dim3(64 * S::NW), 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<T, D, C, S::NW>), dim3(a.BH * a.nqb), dim3(64 * S::NW), 0, stream, a);
     return hipGetLastError();
 }
 
