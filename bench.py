@@ -10,9 +10,12 @@ FLOP counting: forward 4*B*H*N^2*d, forward+backward 10*B*H*N^2*d, both halved
 for causal. The backward alone is credited with its five matrix products,
 10*B*H*N^2*d (halved for causal), whatever the kernels recompute.
 
-Every launch of the timed region is bracketed by HIP events on the stream the
-library enqueues on, so each stage's average duration is measured live; the
-roofline entry is the dominant one. Prints one JSON line.
+The timed region is K whole steps between two HIP events on the stream the
+library enqueues on; inside it only the dominant kernel's launches are
+bracketed by events, which give its average launch duration for the roofline
+entry. The per-stage breakdown comes from a separate pass of K steps with
+events around every launch (each event adds a little to the step, so that
+pass does not set the step time). Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -101,6 +104,9 @@ def main():
     ap.add_argument("--workload", default="gpt2_small_causal", choices=sorted(WORKLOADS))
     ap.add_argument("--dq", default="default", choices=["default", "atomic", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB (a known-size "
+                         "reference for hardware byte counters under a profiler)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the kernels are measured on "
@@ -129,34 +135,52 @@ def main():
     strategy = {"default": fa.FA_DQ_DEFAULT, "atomic": fa.FA_DQ_ATOMIC, "separate": fa.FA_DQ_SEPARATE}[args.dq]
     stream = torch.cuda.current_stream()
 
+    stages = ("fwd", "prep", "main")
+
     def run(evs=None):
-        if evs: evs[0].record(stream)
-        fa.fa_fwd(q, k, v, o, lse, causal, scale, stream)
-        if evs: evs[1].record(stream)
-        fa.fa_bwd_prep(o, do, lse, ws, strategy, stream)
-        if evs: evs[2].record(stream)
-        fa.fa_bwd_main(q, k, v, o, do, lse, dq, dk, dv, ws, causal, scale, strategy, stream)
-        if evs: evs[3].record(stream)
+        """One step; evs maps a stage name to the (start, end) events recorded around it."""
+        evs = evs or {}
+        for name in stages:
+            if name in evs: evs[name][0].record(stream)
+            if name == "fwd":
+                fa.fa_fwd(q, k, v, o, lse, causal, scale, stream)
+            elif name == "prep":
+                fa.fa_bwd_prep(o, do, lse, ws, strategy, stream)
+            else:
+                fa.fa_bwd_main(q, k, v, o, do, lse, dq, dk, dv, ws, causal, scale, strategy, stream)
+            if name in evs: evs[name][1].record(stream)
+
+    def ev_pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # Stage breakdown: every launch bracketed by events (the events themselves
+    # add a few microseconds per step, so this pass does not set the step time).
+    brk = [{name: ev_pair() for name in stages} for _ in range(K)]
+    for i in range(K):
+        run(brk[i])
+    torch.cuda.synchronize()
+    stage_ms = {name: statistics.mean(e[name][0].elapsed_time(e[name][1]) for e in brk) for name in stages}
+    dom = "main" if stage_ms["main"] >= stage_ms["fwd"] else "fwd"
+
+    # Timed region: K whole steps; only the dominant kernel's launches carry
+    # events, which give its average launch duration for the roofline entry.
+    dom_ev = [{dom: ev_pair()} for _ in range(K)]
+    t_start, t_end = ev_pair()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(K):
-        run(ev[i])
+        run(dom_ev[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / K
-    stage_ms = {name: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in ev)
-                for j, name in enumerate(("fwd", "prep", "main"))}
+    dom_ms = statistics.mean(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev)
 
     tf_step = flops(w, "step") / (ms_step * 1e-3) / 1e12
     tf_fwd = flops(w, "fwd") / (stage_ms["fwd"] * 1e-3) / 1e12
@@ -166,17 +190,25 @@ def main():
     peak = PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
 
     # roofline of the dominant kernel: algorithmic FLOP per launch / its average duration
-    dom = "main" if stage_ms["main"] >= stage_ms["fwd"] else "fwd"
     dom_flop = flops(w, "bwd") if dom == "main" else flops(w, "fwd")
-    dom_tf = dom_flop / (stage_ms[dom] * 1e-3) / 1e12
+    dom_tf = dom_flop / (dom_ms * 1e-3) / 1e12
     single = not (dom == "main" and (args.dq == "atomic" or fp32))
     roofline = {
         "bound": "mfma", "achieved": round(dom_tf, 2), "peak": peak, "unit": "TFLOP/s",
         "frac": round(dom_tf / peak, 4), "traffic": None,
         "kernel": KERNELS[dom] if single else f"fa_bwd_main ({'atomic main + convert' if not fp32 else 'fp32'})",
-        "flop_per_launch": dom_flop, "avg_launch_ms": round(stage_ms[dom], 5),
+        "flop_per_launch": dom_flop, "avg_launch_ms": round(dom_ms, 5),
         "flop_rule": "fwd 4*B*H*N^2*d, bwd 10*B*H*N^2*d (five products), halved for causal",
     }
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, shape, scale, causal)
 
@@ -188,6 +220,7 @@ def main():
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w["dtype"], "data": "synthetic: seeded i.i.d. N(0,1) inputs of the workload's shape",
         "config": cfg,
+        "stage_breakdown": "per-stage means from a separate pass with events around every launch",
         "fwd": {"ms": round(stage_ms["fwd"], 5), "tflops": round(tf_fwd, 3), "frac_peak": round(tf_fwd / peak, 4)},
         "bwd": {"ms": round(bwd_ms, 5), "prep_ms": round(stage_ms["prep"], 5), "main_ms": round(stage_ms["main"], 5),
                 "tflops_10x": round(tf_bwd, 3)},

@@ -58,7 +58,10 @@ constexpr int KS = D / 16;     // k-steps over the head dim (32x32x16 MFMA)
 constexpr int DT = D / 32;     // 32-wide tiles of the head dim
 constexpr int CH = D / 8;      // 16-byte chunks per row
 constexpr int kRowB = 2 * D;   // bytes per tile row
-constexpr int kSlots = 3;      // ring slots
+#ifndef FA_BWD_SLOTS
+#define FA_BWD_SLOTS 4
+#endif
+constexpr int kSlots = FA_BWD_SLOTS;  // ring slots; stage s + kSlots - 1 is requested while stage s is used
 
 // key workgroups
 constexpr int kKvKeys = 128;                 // keys per workgroup (32 per wave)
@@ -66,6 +69,7 @@ constexpr int kKvQRows = 64;                 // query rows per ring stage
 constexpr int kKvTileB = kKvQRows * kRowB;   // bytes of the Q (or dO) part of a stage
 constexpr int kKvTC = kKvTileB / 1024;       // 1 KiB chunks of that part
 constexpr int kKvStatB = 256;                // 64 floats of lse*log2e, then 64 of D
+constexpr int kKvRowsOff = 2 * kKvStatB;     // the Q rows follow the statistics, then the dO rows
 constexpr int kKvStage = 2 * kKvTileB + 2 * kKvStatB;
 constexpr int kKvCpw = 2 * kKvTC / 4;        // 16-byte DMA instructions per wave per stage
 
@@ -78,7 +82,25 @@ constexpr int kQStage = 2 * kQTileB;
 constexpr int kQCpw = 2 * kQTC / 4;
 
 constexpr int kSmem = kSlots * (kKvStage > kQStage ? kKvStage : kQStage);
-static_assert(kSlots * kKvStage < 65536 && kSlots * kQStage < 65536, "LDS offsets must fit the immediate field");
+// largest immediate LDS offsets: the last slot's dO rows of the second half plus a
+// 16-row chunk (key workgroups; the row bases carry kKvRowsOff), and the last
+// slot's V rows plus 32 rows or three 16-row chunks (query workgroups)
+static_assert((kSlots - 1) * kKvStage + 32 * kRowB + kKvTileB + 16 * kRowB + 16 <= 65536 &&
+                  (kSlots - 1) * kQStage + kQTileB + 48 * kRowB + 16 <= 65536,
+              "LDS offsets must fit the immediate field");
+static_assert(kKvTC % 4 == 0 && kQTC % 4 == 0, "a stage splits evenly over the four waves");
+
+// s_waitcnt leaving `ahead` stages of PER loads each in flight (0 <= ahead <= MAX).
+template <int PER, int MAX>
+__device__ __forceinline__ void wait_stages(int ahead) {
+    if constexpr (MAX >= 2) {
+        if (ahead >= 2) { wait_vmcnt<2 * PER>(); return; }
+    }
+    if constexpr (MAX >= 1) {
+        if (ahead >= 1) { wait_vmcnt<PER>(); return; }
+    }
+    wait_vmcnt<0>();
+}
 
 struct FusedArgs {
     const uint16_t* q;
@@ -107,27 +129,41 @@ struct PrepArgs {
 };
 
 // ---------------------------------------------------------------- 1. prep
-// 8 lanes per row, 8 elements each; 32 rows per workgroup.
+// 8 lanes per row, 8 elements each; a workgroup covers kPrepRounds rounds of
+// 32 rows, every round's loads issued before any sum. One round per workgroup
+// measured fastest: more workgroups in flight beat more rows per lane.
+constexpr int kPrepRounds = 1;
+constexpr int kPrepRows = kPrepRounds * kThreads / (D / 8);
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(PrepArgs a) {
     constexpr int LPR = D / 8;
-    constexpr int RPB = kThreads / LPR;
+    constexpr int RPR = kThreads / LPR;  // rows per round
     const int tid = threadIdx.x, part = tid % LPR;
-    const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
-    const int64_t r = row < a.rows ? row : a.rows - 1;
-    const u32x4 ov = *reinterpret_cast<const u32x4*>(a.o + r * D + part * 8);
-    const u32x4 dv = *reinterpret_cast<const u32x4*>(a.dout + r * D + part * 8);
-    float acc = 0.f;
+    const int64_t row0 = (int64_t)blockIdx.x * kPrepRows + tid / LPR;
+    u32x4 ov[kPrepRounds], dv[kPrepRounds];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        acc = __builtin_fmaf(T::to_f32((uint16_t)(ov[w] & 0xFFFF)), T::to_f32((uint16_t)(dv[w] & 0xFFFF)), acc);
-        acc = __builtin_fmaf(T::to_f32((uint16_t)(ov[w] >> 16)), T::to_f32((uint16_t)(dv[w] >> 16)), acc);
+    for (int k = 0; k < kPrepRounds; ++k) {
+        const int64_t row = row0 + k * RPR;
+        const int64_t r = row < a.rows ? row : a.rows - 1;
+        ov[k] = *reinterpret_cast<const u32x4*>(a.o + r * D + part * 8);
+        dv[k] = *reinterpret_cast<const u32x4*>(a.dout + r * D + part * 8);
     }
 #pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (row < a.rows) {
-        if (part == 0) a.delta[row] = acc;
-        if (part == 1) a.lse2[row] = a.lse[row] * kLog2e;
+    for (int k = 0; k < kPrepRounds; ++k) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            acc = __builtin_fmaf(T::to_f32((uint16_t)(ov[k][w] & 0xFFFF)), T::to_f32((uint16_t)(dv[k][w] & 0xFFFF)), acc);
+            acc = __builtin_fmaf(T::to_f32((uint16_t)(ov[k][w] >> 16)), T::to_f32((uint16_t)(dv[k][w] >> 16)), acc);
+        }
+#pragma unroll
+        for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+        const int64_t row = row0 + k * RPR;
+        if (row < a.rows) {
+            if (part == 0) a.delta[row] = acc;
+            if (part == 1) a.lse2[row] = a.lse[row] * kLog2e;
+        }
     }
 }
 
@@ -153,7 +189,7 @@ __device__ __forceinline__ void map_fused(int bid, const FusedArgs& a, bool caus
 // Key workgroup: dK and dV of 128 keys.
 template <typename T, bool CAUSAL>
 __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char* smem) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
     const int N = a.N;
     const size_t head = (size_t)bh * N * D;
@@ -172,26 +208,29 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     const int g0 = CAUSAL ? (kb * kKvKeys) / kKvQRows : 0;  // first stage touching these keys
     const int nst = ng - g0;
 
-    // Stage s (query stage g0 + s, rows past the end clamp to the last row and
-    // are never used) in slot s % 3: [Q rows][dO rows][lse2 x64][D x64]. Chunk
-    // c (1 KiB) of the Q/dO part is written by wave c % 4; lane l of it carries
-    // tile row 8 (c % kKvTC) + l / 8, stored chunk l % 8. Waves 0 and 1 also
-    // copy the statistics.
-    auto issue = [&](int s, int slot) {
-        char* sb = smem + slot * kKvStage;
-        const int r0 = (g0 + s) * kKvQRows;
+    // Stage s (query stage g0 + s; rows past the end read as zeros and are
+    // masked) in slot s % kSlots: [lse2 x64][D x64][Q rows][dO rows]. Chunk c (1 KiB)
+    // of the Q/dO part is written by wave c % 4; lane l of it carries tile row
+    // 8 (c % kKvTC) + l / 8, stored chunk l % 8; the same lane offsets serve Q
+    // and dO. Waves 0 and 1 also copy the statistics.
+    uint32_t dma_off[kKvTC / 4];
 #pragma unroll
-        for (int u = 0; u < kKvCpw; ++u) {
-            const int chunk = u * 4 + wave;
-            const int p = (chunk % kKvTC) * 64 + lane;
-            const int row = p / CH, c = (p % CH) ^ swz<D>(row);
-            const uint16_t* src = (chunk < kKvTC ? Q : dO) + (size_t)min(r0 + row, N - 1) * D + c * 8;
-            dma16(src, sb + chunk * 1024);
-        }
-        if (wave < 2) {
-            const float* src = (wave == 0 ? lse2 : delta) + min(r0 + lane, N - 1);
-            dma4(src, sb + 2 * kKvTileB + wave * kKvStatB);
-        }
+    for (int j = 0; j < kKvTC / 4; ++j) {
+        const int p = (j * 4 + wave) * 64 + lane;
+        const int row = p / CH, c = (p % CH) ^ swz<D>(row);
+        dma_off[j] = (uint32_t)((row * D + c * 8) * 2);
+    }
+    auto issue = [&](int s, int slot) {
+        const int r0 = (g0 + s) * kKvQRows;
+        const i32x4 qr = rows_rsrc(Q, N, r0, kRowB), dr = rows_rsrc(dO, N, r0, kRowB);
+        char* sb = smem + slot * kKvStage + kKvRowsOff + wave * 1024;
+#pragma unroll
+        for (int j = 0; j < kKvTC / 4; ++j) dma16(qr, dma_off[j], sb + j * 4 * 1024);
+#pragma unroll
+        for (int j = 0; j < kKvTC / 4; ++j) dma16(dr, dma_off[j], sb + kKvTileB + j * 4 * 1024);
+        if (wave < 2)
+            dma4(rows_rsrc(wave == 0 ? lse2 : delta, N, r0, 4), (uint32_t)lane * 4,
+                 smem + slot * kKvStage + wave * kKvStatB);
     };
 
     // Loop-invariant LDS addresses; the slot, half and chunk parts are immediates.
@@ -199,7 +238,7 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     const int s_row = perm32(l32);
     uint32_t a_base[KS];  // Q / dO operand rows for S and dP, k-step ks
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a_base[ks] = smem_addr + (uint32_t)tile_off<D>(s_row, 2 * ks + h);
+    for (int ks = 0; ks < KS; ++ks) a_base[ks] = smem_addr + kKvRowsOff + (uint32_t)tile_off<D>(s_row, 2 * ks + h);
     // Transposed reads: lane L of 16-lane group g reads row 8h + L/4 (+4 for the
     // upper half of the operand), columns 32u + 16(g&1) + 4(L&3) of the Q or dO
     // rows; query chunks add 16 rows.
@@ -208,15 +247,16 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     for (int u = 0; u < DT; ++u)
 #pragma unroll
         for (int hi = 0; hi < 2; ++hi)
-            tr_base[u][hi] = smem_addr + (uint32_t)(tile_off<D>(8 * h + (L16 >> 2) + 4 * hi,
-                                                                (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
-                                                    (L16 & 1) * 8);
+            tr_base[u][hi] = smem_addr + kKvRowsOff +
+                             (uint32_t)(tile_off<D>(8 * h + (L16 >> 2) + 4 * hi,
+                                                    (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
+                                        (L16 & 1) * 8);
     const uint32_t st_base = smem_addr + (uint32_t)(4 * 8 * h);
 
-    // stages 0 and 1 in flight (stage 1 even when it lies past the end, so that
-    // the wait counts below are exact)
-    issue(0, 0);
-    issue(1, 1);
+    // the first kSlots - 1 stages (those that exist) in flight
+#pragma unroll
+    for (int i = 0; i < kSlots - 1; ++i)
+        if (i < nst) issue(i, i);
     // K and V rows: B operands of S = Q K^T and dP = dO V^T (k = head dim).
     // Loaded after the first ring stages are requested so the latencies overlap;
     // the full wait then tells the compiler's wait pass that no load into a
@@ -238,7 +278,7 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         constexpr int SO = decltype(slot_c)::value * kKvStage;
         constexpr int QO = SO + decltype(hh_c)::value * 32 * kRowB;  // Q rows of the half
         constexpr int DO = QO + kKvTileB;                            // dO rows of the half
-        constexpr int TO = SO + 2 * kKvTileB + 4 * 32 * decltype(hh_c)::value;
+        constexpr int TO = SO + 4 * 32 * decltype(hh_c)::value;
         // ---- S = Q K^T, dP = dO V^T (32 queries x 32 keys; lane = key)
         u32x4 qa[KS], da[KS];
         qa[0] = ds_read128<QO>(a_base[0]);
@@ -349,16 +389,13 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
 
     for_ring<kSlots>(nst, [&](auto slot_c, int s) {
         constexpr int SLOT = decltype(slot_c)::value;
-        // stage s has landed (stage s + 1 may still be in flight); every wave is
-        // done with stage s - 1, whose slot the next issue overwrites
-        if (s + 1 < nst || s == 0) {
-            if (wave < 2) wait_vmcnt<kKvCpw + 1>();
-            else wait_vmcnt<kKvCpw>();
-        } else {
-            wait_vmcnt<0>();
-        }
+        // stage s has landed (the stages after it may still be in flight); every
+        // wave is done with stage s - 1, whose slot the next issue overwrites
+        const int ahead = min(kSlots - 2, nst - 1 - s);  // stages requested after s
+        if (wave < 2) wait_stages<kKvCpw + 1, kSlots - 2>(ahead);
+        else wait_stages<kKvCpw, kSlots - 2>(ahead);
         barrier();
-        if (s + 2 < nst) issue(s + 2, (SLOT + 2) % kSlots);
+        if (s + kSlots - 1 < nst) issue(s + kSlots - 1, (SLOT + kSlots - 1) % kSlots);
         const int g = g0 + s;
         auto half = [&](auto hh_c) {
             const int qt0 = g * kKvQRows + 32 * decltype(hh_c)::value;
@@ -392,7 +429,7 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
 // Query workgroup: dQ of 128 queries.
 template <typename T, bool CAUSAL>
 __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char* smem) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
     const int N = a.N;
     const size_t head = (size_t)bh * N * D;
@@ -413,20 +450,25 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
 #pragma unroll
     for (int u = 0; u < DT; ++u) dqa[u] = f32x16{};
 
-    // Stage b (key block b, clamped to the last block past the end and then
-    // never used) in slot b % 3: [K block][V block], each 64 rows in the
-    // swizzled layout. Chunk c of a stage is written by wave c % 4.
-    auto issue = [&](int b, int slot) {
-        char* sb = smem + slot * kQStage;
-        const int blk = min(b, nkb - 1);
+    // Stage b (key block b; rows past the end read as zeros) in slot
+    // b % kSlots: [K block][V
+    // block], each 64 rows in the swizzled layout. Chunk c of a stage is written
+    // by wave c % 4; the same lane offsets serve K and V.
+    uint32_t dma_off[kQTC / 4];
 #pragma unroll
-        for (int u = 0; u < kQCpw; ++u) {
-            const int chunk = u * 4 + wave;
-            const int p = (chunk % kQTC) * 64 + lane;
-            const int row = p / CH, c = (p % CH) ^ swz<D>(row);
-            const uint16_t* src = (chunk < kQTC ? K : V) + (size_t)min(blk * kQKeys + row, N - 1) * D + c * 8;
-            dma16(src, sb + chunk * 1024);
-        }
+    for (int j = 0; j < kQTC / 4; ++j) {
+        const int p = (j * 4 + wave) * 64 + lane;
+        const int row = p / CH, c = (p % CH) ^ swz<D>(row);
+        dma_off[j] = (uint32_t)((row * D + c * 8) * 2);
+    }
+    auto issue = [&](int b, int slot) {
+        const int r0 = b * kQKeys;
+        const i32x4 kr = rows_rsrc(K, N, r0, kRowB), vr = rows_rsrc(V, N, r0, kRowB);
+        char* sb = smem + slot * kQStage + wave * 1024;
+#pragma unroll
+        for (int j = 0; j < kQTC / 4; ++j) dma16(kr, dma_off[j], sb + j * 4 * 1024);
+#pragma unroll
+        for (int j = 0; j < kQTC / 4; ++j) dma16(vr, dma_off[j], sb + kQTileB + j * 4 * 1024);
     };
 
     const uint32_t smem_addr = lds_addr(smem);
@@ -443,8 +485,9 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
                                                                 (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
                                                     (L16 & 1) * 8);
 
-    issue(0, 0);
-    issue(1, 1);
+#pragma unroll
+    for (int i = 0; i < kSlots - 1; ++i)
+        if (i < nkb) issue(i, i);
     // Q and dO rows: B operands of S^T = K Q^T and dP^T = V dO^T (k = head dim);
     // loaded and waited for as in the key workgroups.
     u32x4 qf[KS], dof[KS];
@@ -567,10 +610,9 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
 
     for_ring<kSlots>(nkb, [&](auto slot_c, int kb) {
         constexpr int SLOT = decltype(slot_c)::value;
-        if (kb + 1 < nkb || kb == 0) wait_vmcnt<kQCpw>();
-        else wait_vmcnt<0>();
+        wait_stages<kQCpw, kSlots - 2>(min(kSlots - 2, nkb - 1 - kb));
         barrier();
-        if (kb + 2 < nkb) issue(kb + 2, (SLOT + 2) % kSlots);
+        if (kb + kSlots - 1 < nkb) issue(kb + kSlots - 1, (SLOT + kSlots - 1) % kSlots);
         if (kb >= nkw) return;
         const int key0 = kb * kQKeys;
         const bool need_mask = (CAUSAL && key0 + kQKeys - 1 > q0) || (key0 + kQKeys > N);
@@ -627,8 +669,7 @@ hipError_t bwd_prep(const void* o, const void* dout, const float* lse, int B, in
     p.delta = delta;
     p.lse2 = lse2;
     p.rows = (int64_t)B * H * N;
-    constexpr int RPB = kThreads / (D / 8);
-    const dim3 grid((unsigned)((p.rows + RPB - 1) / RPB));
+    const dim3 grid((unsigned)((p.rows + kPrepRows - 1) / kPrepRows));
     if (dtype == 0)
         hipLaunchKernelGGL((bwd_prep_kernel<Bf16>), grid, dim3(kThreads), 0, stream, p);
     else

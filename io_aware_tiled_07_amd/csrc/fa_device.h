@@ -110,15 +110,16 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_base) {
 template <int V>
 using Int = std::integral_constant<int, V>;
 
-// body(Int<r % S>{}, r) for r = 0 .. n-1 (S <= 3): the ring slot of round r is a
+// body(Int<r % S>{}, r) for r = 0 .. n-1 (S <= 4): the ring slot of round r is a
 // compile-time constant inside the body, so LDS offsets become immediates.
 template <int S, typename F>
 __device__ __forceinline__ void for_ring(int n, F&& body) {
-    static_assert(S >= 1 && S <= 3, "ring depth");
+    static_assert(S >= 1 && S <= 4, "ring depth");
     for (int r = 0; r < n; r += S) {
         body(Int<0>{}, r);
         if constexpr (S > 1) if (r + 1 < n) body(Int<1>{}, r + 1);
         if constexpr (S > 2) if (r + 2 < n) body(Int<2>{}, r + 2);
+        if constexpr (S > 3) if (r + 3 < n) body(Int<3>{}, r + 3);
     }
 }
 
@@ -144,6 +145,18 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 }
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voffset, char* lds_base) {
     amdgcn_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_base, 16, (int)voffset, 0, 0, 0);
+}
+// 4-byte form (buffer_load_dword ... lds): lane l writes lds_base + 4 * l.
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voffset, char* lds_base) {
+    amdgcn_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_base, 4, (int)voffset, 0, 0, 0);
+}
+// Resource over rows r0 .. n-1 of a row-major array with row_bytes per row (no
+// rows at all when r0 >= n; the byte count saturates at 2^32 - 1, far beyond
+// the 64 rows a stage reads).
+__device__ __forceinline__ i32x4 rows_rsrc(const void* base, int n, int r0, int row_bytes) {
+    const int64_t left = (int64_t)(n - r0) * row_bytes;
+    const char* p = static_cast<const char*>(base) + (r0 < n ? (int64_t)r0 * row_bytes : 0);
+    return buffer_rsrc(p, left <= 0 ? 0u : (left > 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)left));
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).

@@ -137,10 +137,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     }
     auto issue = [&](int kb, auto slot_c) {
         constexpr int SLOT = decltype(slot_c)::value;
-        const int row0 = kb * kBc;
-        const uint32_t left = (uint32_t)(N - row0) * D * 2;
-        const i32x4 kr = buffer_rsrc(K + (size_t)row0 * D * 2, left);
-        const i32x4 vr = buffer_rsrc(V + (size_t)row0 * D * 2, left);
+        const i32x4 kr = rows_rsrc(K, N, kb * kBc, D * 2);
+        const i32x4 vr = rows_rsrc(V, N, kb * kBc, D * 2);
         char* sb = smem + SLOT * SB + wave * 1024;
 #pragma unroll
         for (int j = 0; j < HALF; ++j) dma16(kr, dma_off[j], sb + j * NW * 1024);
