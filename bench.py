@@ -42,6 +42,54 @@ WORKLOADS = {
 
 # kernel names as rocprofv3 reports them, per stage of the default strategy
 KERNELS = {"fwd": "fwd_kernel", "prep": "bwd_prep_kernel", "main": "bwd_fused_kernel"}
+# source files each stage's kernel is built from (a change to any of them makes
+# recorded hardware counters stale)
+KERNEL_SOURCES = {"fwd": ("fa_fwd.hip", "fa_device.h"), "prep": ("fa_bwd.hip", "fa_device.h"),
+                  "main": ("fa_bwd.hip", "fa_device.h")}
+
+# Beyond-L2 traffic per launch from rocprofv3 --pmc (FETCH_SIZE, then WRITE_SIZE,
+# KiB per dispatch, in runs of their own), for the default dQ strategy, with the
+# sha256 (first 16 hex digits) of the kernel's sources when they were taken.
+# Each counter is scaled by what it reads for a plain 256 MiB device-to-device
+# copy in the same runs (the runtime's copy kernel: FETCH_SIZE 131,092.7 KiB and
+# WRITE_SIZE 262,144 KiB for 262,144 KiB each way). The summaries and the
+# commands are in profiles/.
+COPY_PROBE_KIB = 262144
+COUNTERS = {
+    # workload: {stage: (FETCH_SIZE KiB, WRITE_SIZE KiB, copy FETCH_SIZE KiB, copy WRITE_SIZE KiB, sources sha)}
+    "gpt2_small_causal": {
+        "fwd": (18537.4, 12672.3, 131092.7, 262144.0, "478abb7ebd439ff4"),
+        "prep": (12493.4, 768.0, 131092.7, 262144.0, "eaba20073856b242"),
+        "main": (63242.5, 47139.9, 131092.7, 262144.0, "eaba20073856b242"),
+    },
+}
+
+
+def sources_sha(stage):
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[stage]:
+        with open(os.path.join(ROOT, "io_aware_tiled_07_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(workload, stage):
+    """Counter-derived bytes per launch, or None when none were recorded for this
+    kernel or its sources changed since."""
+    rec = COUNTERS.get(workload, {}).get(stage)
+    if rec is None or rec[4] != sources_sha(stage):
+        return None
+    fetch, write, copy_fetch, copy_write, _ = rec
+    return round((fetch * COPY_PROBE_KIB / copy_fetch + write * COPY_PROBE_KIB / copy_write) * 1024)
+
+
+def algorithmic_bytes(w, stage):
+    """Bytes a launch must move at least: every input read once, every output written once."""
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    elt = 4 if w["dtype"] == "fp32" else 2
+    t, r = B * H * N * d * elt, B * H * N * 4
+    return {"fwd": 3 * t + t + r, "prep": 2 * t + r + 2 * r, "main": 4 * t + 2 * r + 3 * t}[stage]
 
 
 def flops(w, which):
@@ -195,7 +243,9 @@ def main():
     single = not (dom == "main" and (args.dq == "atomic" or fp32))
     roofline = {
         "bound": "mfma", "achieved": round(dom_tf, 2), "peak": peak, "unit": "TFLOP/s",
-        "frac": round(dom_tf / peak, 4), "traffic": None,
+        "frac": round(dom_tf / peak, 4), "traffic": traffic_bytes(args.workload, dom) if args.dq == "default" else None,
+        "traffic_unit": "bytes per launch beyond L2 (copy-calibrated FETCH_SIZE + WRITE_SIZE)",
+        "algorithmic_bytes": algorithmic_bytes(w, dom),
         "kernel": KERNELS[dom] if single else f"fa_bwd_main ({'atomic main + convert' if not fp32 else 'fp32'})",
         "flop_per_launch": dom_flop, "avg_launch_ms": round(dom_ms, 5),
         "flop_rule": "fwd 4*B*H*N^2*d, bwd 10*B*H*N^2*d (five products), halved for causal",
