@@ -37,3 +37,21 @@ def test_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_algorithmic_bytes_by_hand():
+    w = dict(B=1, H=2, N=3, d=4, dtype="bf16")
+    t, r = 1 * 2 * 3 * 4 * 2, 1 * 2 * 3 * 4
+    assert bench.algorithmic_bytes(w, "fwd") == 4 * t + r          # read Q, K, V; write O, lse
+    assert bench.algorithmic_bytes(w, "prep") == 2 * t + 3 * r     # read O, dO, lse; write D, lse2
+    assert bench.algorithmic_bytes(w, "main") == 7 * t + 2 * r     # read Q, K, V, dO, lse2, D; write dQ, dK, dV
+
+
+def test_traffic_is_calibrated_and_goes_stale(monkeypatch):
+    monkeypatch.setitem(bench.COUNTERS, "toy", {"main": (100.0, 50.0, 131072.0, 262144.0, "abc")})
+    monkeypatch.setattr(bench, "sources_sha", lambda stage: "abc")
+    # FETCH_SIZE scaled by 262144 / 131072 = 2, WRITE_SIZE by 1; KiB -> bytes
+    assert bench.traffic_bytes("toy", "main") == (200 + 50) * 1024
+    monkeypatch.setattr(bench, "sources_sha", lambda stage: "changed")
+    assert bench.traffic_bytes("toy", "main") is None
+    assert bench.traffic_bytes("toy", "fwd") is None
