@@ -108,7 +108,7 @@ struct FusedArgs {
     const uint16_t* v;
     const uint16_t* dout;
     const float* lse2;   // lse * log2(e), [BH][N]
-    const float* delta;  // D, [BH][N]
+    const float* delta;  // -D (negated), [BH][N]
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
@@ -123,7 +123,7 @@ struct PrepArgs {
     const uint16_t* o;
     const uint16_t* dout;
     const float* lse;
-    float* delta;
+    float* delta;  // receives -D
     float* lse2;
     int64_t rows;
 };
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(PrepArgs a) {
         for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
         const int64_t row = row0 + k * RPR;
         if (row < a.rows) {
-            if (part == 0) a.delta[row] = acc;
+            if (part == 0) a.delta[row] = -acc;  // stored negated: the initial dP accumulator
             if (part == 1) a.lse2[row] = a.lse[row] * kLog2e;
         }
     }
@@ -289,17 +289,29 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         da[1] = ds_read128<DO>(a_base[1]);
         da[2] = ds_read128<DO>(a_base[2]);
         da[3] = ds_read128<DO>(a_base[3]);
-        // statistics of this lane's first 8 queries (8h + 0..7); those of the
-        // other 8 (16 + 8h + 0..7) are read when their chunk comes up
-        f32x4 lv[2], dl[2];
+        // -D of this lane's 16 queries in accumulator order (registers 0..7:
+        // queries 8h + 0..7, 8..15: 16 + 8h + 0..7) is the initial dP
+        // accumulator, so the MFMAs produce dP - D directly
+        f32x4 nd[4];
+        nd[0] = ds_read128f<TO + kKvStatB>(st_base);
+        nd[1] = ds_read128f<TO + kKvStatB + 16>(st_base);
+        nd[2] = ds_read128f<TO + kKvStatB + 64>(st_base);
+        nd[3] = ds_read128f<TO + kKvStatB + 80>(st_base);
+        // lse * log2(e) of the first 8 queries; the other 8 are read when their
+        // chunk comes up
+        f32x4 lv[2];
         lv[0] = ds_read128f<TO>(st_base);
         lv[1] = ds_read128f<TO + 16>(st_base);
-        dl[0] = ds_read128f<TO + kKvStatB>(st_base);
-        dl[1] = ds_read128f<TO + kKvStatB + 16>(st_base);
-        lgkm_wait<4>();
+        lgkm_wait<2>();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) { settle(qa[ks]); settle(da[ks]); }
-        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) settle(nd[j]);
+        f32x16 s = f32x16{}, dp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[4 * j + e] = nd[j][e];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             s = T::mfma32(qa[ks], kf[ks], s);
@@ -307,7 +319,7 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         }
         lgkm_wait<0>();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) { settle(lv[j]); settle(dl[j]); }
+        for (int j = 0; j < 2; ++j) settle(lv[j]);
         // transposed operands for dV^T += dO^T P and dK^T += Q^T dS, query chunk
         // 0 first, so they land during the element-wise work
         u32x2 dtr[2][DT][2], qtr[2][DT][2];
@@ -332,7 +344,7 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
             if (c == 1) {  // the second chunk's statistics were requested after its operands
                 lgkm_wait<0>();
 #pragma unroll
-                for (int j = 0; j < 2; ++j) { settle(lv[j]); settle(dl[j]); }
+                for (int j = 0; j < 2; ++j) settle(lv[j]);
             }
             uint32_t pw[4], dsw[4];
             // the element-wise block, with the mask only on tiles that need it
@@ -356,7 +368,7 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
                             if ((CAUSAL && ci < dlim) || ci >= nlim) pv = 0.f;
                         }
                         p[e] = pv;
-                        ds[e] = pv * (dp[i] - dl[j][i & 3]);
+                        ds[e] = pv * dp[i];
                     }
                     pw[w] = T::pack2(p[0], p[1]);
                     dsw[w] = T::pack2(ds[0], ds[1]);
@@ -367,9 +379,7 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
             if (c == 0) {
                 lv[0] = ds_read128f<TO + 64>(st_base);
                 lv[1] = ds_read128f<TO + 80>(st_base);
-                dl[0] = ds_read128f<TO + kKvStatB + 64>(st_base);
-                dl[1] = ds_read128f<TO + kKvStatB + 80>(st_base);
-                lgkm_wait<12>();  // chunk 0's transposed operands (issued first) have landed
+                lgkm_wait<10>();  // chunk 0's transposed operands (issued first) have landed
             }
 #pragma unroll
             for (int u = 0; u < DT; ++u)
@@ -500,7 +510,14 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
         }
     }
     const float l2q = a.lse2[(size_t)bh * N + qload];
-    const float Dq = a.delta[(size_t)bh * N + qload];
+    // -D of this lane's query, broadcast: the initial dP^T accumulator of every
+    // key tile, so the MFMAs produce dP - D directly
+    f32x16 nd_init;
+    {
+        const float nd = a.delta[(size_t)bh * N + qload];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) nd_init[i] = nd;
+    }
     wait_vmcnt<0>();
 
     auto block = [&](auto slot_c, auto mask_c, int key0) {
@@ -522,7 +539,8 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
             lgkm_wait<0>();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) { settle(ka[ks]); settle(va[ks]); }
-            s[0] = dp[0] = f32x16{};
+            s[0] = f32x16{};
+            dp[0] = nd_init;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 s[0] = T::mfma32(ka[ks], qf[ks], s[0]);
@@ -542,7 +560,8 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
             lgkm_wait<0>();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) { settle(ka[ks]); settle(va[ks]); }
-            s[1] = dp[1] = f32x16{};
+            s[1] = f32x16{};
+            dp[1] = nd_init;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 s[1] = T::mfma32(ka[ks], qf[ks], s[1]);
@@ -586,7 +605,7 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
                         const int ci = 32 * kt + 16 * (i >> 3) + (i & 7);
                         if ((CAUSAL && ci > qlim) || ci >= nlim) pv = 0.f;
                     }
-                    ds[e] = pv * (dp[kt][i] - Dq);
+                    ds[e] = pv * dp[kt][i];
                 }
                 dsw[w] = T::pack2(ds[0], ds[1]);
             }
