@@ -222,14 +222,14 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     }
     auto issue = [&](int s, int slot) {
         const int r0 = (g0 + s) * kKvQRows;
-        const i32x4 qr = rows_rsrc(Q, N, r0, kRowB), dr = rows_rsrc(dO, N, r0, kRowB);
+        const i32x4 qr = rows_rsrc<kRowB>(Q, N, r0), dr = rows_rsrc<kRowB>(dO, N, r0);
         char* sb = smem + slot * kKvStage + kKvRowsOff + wave * 1024;
 #pragma unroll
         for (int j = 0; j < kKvTC / 4; ++j) dma16(qr, dma_off[j], sb + j * 4 * 1024);
 #pragma unroll
         for (int j = 0; j < kKvTC / 4; ++j) dma16(dr, dma_off[j], sb + kKvTileB + j * 4 * 1024);
         if (wave < 2)
-            dma4(rows_rsrc(wave == 0 ? lse2 : delta, N, r0, 4), (uint32_t)lane * 4,
+            dma4(rows_rsrc<4>(wave == 0 ? lse2 : delta, N, r0), (uint32_t)lane * 4,
                  smem + slot * kKvStage + wave * kKvStatB);
     };
 
@@ -473,7 +473,7 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
     }
     auto issue = [&](int b, int slot) {
         const int r0 = b * kQKeys;
-        const i32x4 kr = rows_rsrc(K, N, r0, kRowB), vr = rows_rsrc(V, N, r0, kRowB);
+        const i32x4 kr = rows_rsrc<kRowB>(K, N, r0), vr = rows_rsrc<kRowB>(V, N, r0);
         char* sb = smem + slot * kQStage + wave * 1024;
 #pragma unroll
         for (int j = 0; j < kQTC / 4; ++j) dma16(kr, dma_off[j], sb + j * 4 * 1024);

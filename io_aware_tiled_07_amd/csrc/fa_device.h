@@ -150,13 +150,14 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voffset, char* lds_ba
 __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voffset, char* lds_base) {
     amdgcn_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_base, 4, (int)voffset, 0, 0, 0);
 }
-// Resource over rows r0 .. n-1 of a row-major array with row_bytes per row (no
-// rows at all when r0 >= n; the byte count saturates at 2^32 - 1, far beyond
-// the 64 rows a stage reads).
-__device__ __forceinline__ i32x4 rows_rsrc(const void* base, int n, int r0, int row_bytes) {
-    const int64_t left = (int64_t)(n - r0) * row_bytes;
-    const char* p = static_cast<const char*>(base) + (r0 < n ? (int64_t)r0 * row_bytes : 0);
-    return buffer_rsrc(p, left <= 0 ? 0u : (left > 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)left));
+// Resource over rows r0 .. n-1 (0 <= r0 < n) of a row-major array with RB bytes
+// per row; the byte count saturates below 2^32, far beyond the 64 rows a stage
+// reads.
+template <int RB>
+__device__ __forceinline__ i32x4 rows_rsrc(const void* base, int n, int r0) {
+    constexpr int kMaxRows = (int)(0xFFFFFFFFu / RB);
+    const uint32_t left = (uint32_t)min(n - r0, kMaxRows) * RB;
+    return buffer_rsrc(static_cast<const char*>(base) + (int64_t)r0 * RB, left);
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).

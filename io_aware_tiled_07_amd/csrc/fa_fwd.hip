@@ -137,8 +137,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     }
     auto issue = [&](int kb, auto slot_c) {
         constexpr int SLOT = decltype(slot_c)::value;
-        const i32x4 kr = rows_rsrc(K, N, kb * kBc, D * 2);
-        const i32x4 vr = rows_rsrc(V, N, kb * kBc, D * 2);
+        const i32x4 kr = rows_rsrc<D * 2>(K, N, kb * kBc);
+        const i32x4 vr = rows_rsrc<D * 2>(V, N, kb * kBc);
         char* sb = smem + SLOT * SB + wave * 1024;
 #pragma unroll
         for (int j = 0; j < HALF; ++j) dma16(kr, dma_off[j], sb + j * NW * 1024);
