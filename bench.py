@@ -115,6 +115,17 @@ def io_bytes(w):
     return fa_b, std_b
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, shape, scale, causal, min_seconds=10.0):
     """The fp64 oracle (as it stands) on the host cores: whole fwd+bwd passes over the
     same seeded inputs, repeated until at least ``min_seconds`` have elapsed, or over a
@@ -139,7 +150,7 @@ def cpu_baseline(w, shape, scale, causal, min_seconds=10.0):
         reps += 1
     credited = flops(dict(w, B=1, H=nh), "step") * reps
     return {"value": round(credited / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{reps} fwd+bwd pass(es) of the fp64 oracle over {nh} of {heads} (batch, head) pairs "
                       f"of the same workload, {t_total:.2f} s; credited with the 10*N^2*d rule"}
 
@@ -152,6 +163,9 @@ def main():
     ap.add_argument("--workload", default="gpt2_small_causal", choices=sorted(WORKLOADS))
     ap.add_argument("--dq", default="default", choices=["default", "atomic", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="also time K cold steps, each after writing a 512 MiB scratch buffer (evicts L2 and the "
+                         "256 MB Infinity Cache)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters under a profiler)")
@@ -251,6 +265,24 @@ def main():
         "flop_rule": "fwd 4*B*H*N^2*d, bwd 10*B*H*N^2*d (five products), halved for causal",
     }
 
+    cold = None
+    if args.flush_mall:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold_ms = []
+        for i in range(K):
+            scratch.fill_(i & 0xFF)
+            e0, e1 = ev_pair()
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold_ms.append(e0.elapsed_time(e1))
+        del scratch
+        cms = statistics.median(cold_ms)
+        cold = {"ms_per_step_median": round(cms, 5), "ms_min": round(min(cold_ms), 5), "ms_max": round(max(cold_ms), 5),
+                "tflops_10x": round(flops(w, "step") / (cms * 1e-3) / 1e12, 3),
+                "note": "each step after a 512 MiB scratch write; events around each step"}
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -279,6 +311,10 @@ def main():
         "io_fwd": {"flash_bytes": io_bytes(w)[0], "standard_bytes": io_bytes(w)[1],
                    "standard_over_flash": round(io_bytes(w)[1] / io_bytes(w)[0], 2)},
         "roofline": roofline, "cpu_baseline": cpu, "wall_s_timed": round(wall, 4),
+        "dominant_launch_ms": {"median": round(statistics.median(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev), 5),
+                               "min": round(min(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev), 5),
+                               "max": round(max(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev), 5)},
+        "cold": cold,
     }
     print(json.dumps(out), flush=True)
 

@@ -183,3 +183,22 @@ def test_main_rejects(lib, kw, code):
     st = lib.fa_bwd_main(*[ctypes.c_void_p(p[n]) for n in names], 2, 3, 100, d, ctypes.c_float(0.125), 0, 0,
                          kw.get("strategy", 0), ctypes.c_void_p(A + 9 * GAP), ctypes.c_size_t(ws_bytes), None)
     assert st == code
+
+
+def test_library_never_allocates():
+    """The library allocates no device or host memory of its own: no allocation or
+    free routine of the HIP runtime is among the symbols it imports."""
+    import shutil
+    import subprocess
+    if not os.path.exists(fa.library_path()):
+        pytest.skip("libfa.so not built")
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", fa.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    imported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert any(s.startswith("hip") for s in imported), "expected HIP runtime imports"
+    forbidden = sorted(s for s in imported if re.match(r"hip(Ext)?(Malloc|Free|HostMalloc|HostFree|MallocAsync|"
+                                                        r"FreeAsync|MallocManaged|HostAlloc|MemAlloc)", s))
+    assert forbidden == []
