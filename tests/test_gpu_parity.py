@@ -166,6 +166,34 @@ def test_custom_scale():
     check("lse", lse, lse_ref, "bf16")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_growing_scores_move_the_running_maximum(causal, d):
+    """Scores that keep rising along the keys (keys ramped along a direction the
+    queries share), so the forward's reference maximum has to move, and O and l
+    be rescaled, on most key tiles rather than only on the first. Forward only:
+    with keys that share a large common component, rounding dS to bf16 before
+    the dQ/dK products (as the method does) costs a few percent of dQ by itself
+    (emulated on the host: relRMS 3-4.5e-2), beyond the 16-bit tolerance."""
+    log(f"growing scores causal={causal} d={d}")
+    B, H, N = 1, 2, 700
+    drawn = inputs(6000 + d, (B, H, N, d), "bf16", with_do=False)
+    qn, kn, vn = (x.f64 for x in drawn)
+    u = np.ones(d)
+    ramp = np.linspace(0.0, 10.0, N)[None, None, :, None]
+    # round to bf16 (RNE) on the host; the oracle sees exactly the rounded values
+    as_bf16 = lambda a: torch.tensor(a).to(torch.bfloat16)
+    q, k, v = (as_bf16(a) for a in (u + 0.5 * qn, ramp * u + 0.5 * kn, vn))
+    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
+    sc = scale_for(d)
+    s_last = sc * float(qd[0, 0, -1] @ kd[0, 0, -1])
+    assert s_last > 40, s_last  # the running maximum climbs by far more than 2^8 in base 2
+    o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=sc)
+    o_ref, lse_ref = oracle.fwd(qd, kd, vd, sc, causal)
+    check("o", o, o_ref, "bf16")
+    check("lse", lse, lse_ref, "bf16")
+
+
 # ---------------------------------------------------------------- determinism and invariants
 
 def test_forward_is_deterministic():
