@@ -51,16 +51,16 @@ KERNEL_SOURCES = {"fwd": ("fa_fwd.hip", "fa_device.h"), "prep": ("fa_bwd.hip", "
 # KiB per dispatch, in runs of their own), for the default dQ strategy, with the
 # sha256 (first 16 hex digits) of the kernel's sources when they were taken.
 # Each counter is scaled by what it reads for a plain 256 MiB device-to-device
-# copy in the same runs (the runtime's copy kernel: FETCH_SIZE 131,092.7 KiB and
+# copy in the same runs (the runtime's copy kernel: FETCH_SIZE 131,092 KiB and
 # WRITE_SIZE 262,144 KiB for 262,144 KiB each way). The summaries and the
 # commands are in profiles/.
 COPY_PROBE_KIB = 262144
 COUNTERS = {
     # workload: {stage: (FETCH_SIZE KiB, WRITE_SIZE KiB, copy FETCH_SIZE KiB, copy WRITE_SIZE KiB, sources sha)}
     "gpt2_small_causal": {
-        "fwd": (18537.4, 12672.3, 131092.7, 262144.0, "478abb7ebd439ff4"),
-        "prep": (12493.4, 768.0, 131092.7, 262144.0, "eaba20073856b242"),
-        "main": (63242.5, 47139.9, 131092.7, 262144.0, "eaba20073856b242"),
+        "fwd": (18655.1, 12672.0, 131092.0, 262144.0, "766d855969262cda"),
+        "prep": (12493.3, 768.0, 131092.0, 262144.0, "c0c49f9eac170e64"),
+        "main": (61312.3, 46894.7, 131092.0, 262144.0, "c0c49f9eac170e64"),
     },
 }
 

@@ -215,9 +215,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) s[kt] = T::mfma32(ka[ks][kt], qf[ks], s[kt]);
 
-        // V^T operands for the whole block, issued now so they land during the
-        // softmax. Head dim 64: chunk by chunk, so that chunks 0 and 1 (the
-        // first 32 keys) land first; head dim 128: dim tile by dim tile.
+        // V^T operands, requested early so they land during the softmax. Head
+        // dim 64: the first 32 keys' chunks now, the other two once the first
+        // half's PV MFMAs are issued (fewer live registers); head dim 128: all
+        // four chunks now, dim tile by dim tile.
         u32x2 vlo[4][DT], vhi[4][DT];
         auto vread = [&](auto c_c, int u) {
             constexpr int C = decltype(c_c)::value;
@@ -227,8 +228,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
         if constexpr (DT == 2) {
 #pragma unroll
             for (int u = 0; u < DT; ++u) { vread(Int<0>{}, u); vread(Int<1>{}, u); }
-#pragma unroll
-            for (int u = 0; u < DT; ++u) { vread(Int<2>{}, u); vread(Int<3>{}, u); }
         } else {
 #pragma unroll
             for (int u = 0; u < DT; ++u) {
@@ -283,8 +282,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
                 sum = weights(kt);
             }
             l_run += sum;
-            if (kt == 0) lgkm_wait<(DT == 2 ? 4 * DT : 0)>();
-            else lgkm_wait<0>();
+            lgkm_wait<0>();
             // ---- O^T += V^T P^T over the tile's two 16-key chunks
 #pragma unroll
             for (int c = 2 * kt; c < 2 * kt + 2; ++c)
@@ -299,6 +297,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
                                       pk[kt][4 * (c & 1) + 2], pk[kt][4 * (c & 1) + 3]};
                     oacc[u] = T::mfma32(va, pb, oacc[u]);
                 }
+            if constexpr (DT == 2) {
+                if (kt == 0) {
+#pragma unroll
+                    for (int u = 0; u < DT; ++u) { vread(Int<2>{}, u); vread(Int<3>{}, u); }
+                }
+            }
         }
     });
 
