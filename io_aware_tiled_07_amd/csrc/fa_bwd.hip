@@ -93,6 +93,10 @@ static_assert(kKvTC % 4 == 0 && kQTC % 4 == 0, "a stage splits evenly over the f
 // s_waitcnt leaving `ahead` stages of PER loads each in flight (0 <= ahead <= MAX).
 template <int PER, int MAX>
 __device__ __forceinline__ void wait_stages(int ahead) {
+    static_assert(MAX <= 3 && 3 * PER < 64, "vmcnt range");
+    if constexpr (MAX >= 3) {
+        if (ahead >= 3) { wait_vmcnt<3 * PER>(); return; }
+    }
     if constexpr (MAX >= 2) {
         if (ahead >= 2) { wait_vmcnt<2 * PER>(); return; }
     }
@@ -253,14 +257,11 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
                                         (L16 & 1) * 8);
     const uint32_t st_base = smem_addr + (uint32_t)(4 * 8 * h);
 
-    // the first kSlots - 1 stages (those that exist) in flight
-#pragma unroll
-    for (int i = 0; i < kSlots - 1; ++i)
-        if (i < nst) issue(i, i);
-    // K and V rows: B operands of S = Q K^T and dP = dO V^T (k = head dim).
-    // Loaded after the first ring stages are requested so the latencies overlap;
-    // the full wait then tells the compiler's wait pass that no load into a
-    // register is pending inside the loop (else it drains the ring there).
+    // K and V rows (B operands of S = Q K^T and dP = dO V^T, k = head dim)
+    // first, then the first kSlots - 1 stages (those that exist); the wait
+    // leaves the stages in flight (the loop waits for each) and tells the
+    // compiler's wait pass that no load into a register is pending inside the
+    // loop (else it drains the ring there).
     u32x4 kf[KS], vf[KS];
     {
         const size_t kr = head + (size_t)min(key, N - 1) * D + 8 * h;
@@ -270,7 +271,11 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
             vf[ks] = *reinterpret_cast<const u32x4*>(a.v + kr + 16 * ks);
         }
     }
-    wait_vmcnt<0>();
+#pragma unroll
+    for (int i = 0; i < kSlots - 1; ++i)
+        if (i < nst) issue(i, i);
+    if (wave < 2) wait_stages<kKvCpw + 1, kSlots - 1>(min(kSlots - 1, nst));
+    else wait_stages<kKvCpw, kSlots - 1>(min(kSlots - 1, nst));
 
     // One unit: 32 queries (half HH of the stage in slot SLOT) against the
     // wave's 32 keys.
@@ -495,11 +500,9 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
                                                                 (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
                                                     (L16 & 1) * 8);
 
-#pragma unroll
-    for (int i = 0; i < kSlots - 1; ++i)
-        if (i < nkb) issue(i, i);
-    // Q and dO rows: B operands of S^T = K Q^T and dP^T = V dO^T (k = head dim);
-    // loaded and waited for as in the key workgroups.
+    // Q and dO rows (B operands of S^T = K Q^T and dP^T = V dO^T, k = head
+    // dim) and the row statistics first, then the first ring stages, waited
+    // for as in the key workgroups.
     u32x4 qf[KS], dof[KS];
     {
         const size_t off = head + (size_t)qload * D + 8 * h;
@@ -509,16 +512,18 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
             dof[ks] = *reinterpret_cast<const u32x4*>(a.dout + off + 16 * ks);
         }
     }
-    const float l2q = a.lse2[(size_t)bh * N + qload];
+    const float l2q_ld = a.lse2[(size_t)bh * N + qload];
+    const float nd_ld = a.delta[(size_t)bh * N + qload];
+#pragma unroll
+    for (int i = 0; i < kSlots - 1; ++i)
+        if (i < nkb) issue(i, i);
+    wait_stages<kQCpw, kSlots - 1>(min(kSlots - 1, nkb));
+    const float l2q = l2q_ld, nd = nd_ld;
     // -D of this lane's query, broadcast: the initial dP^T accumulator of every
     // key tile, so the MFMAs produce dP - D directly
     f32x16 nd_init;
-    {
-        const float nd = a.delta[(size_t)bh * N + qload];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) nd_init[i] = nd;
-    }
-    wait_vmcnt<0>();
+    for (int i = 0; i < 16; ++i) nd_init[i] = nd;
 
     auto block = [&](auto slot_c, auto mask_c, int key0) {
         constexpr int KO = decltype(slot_c)::value * kQStage;  // K rows of the stage

@@ -167,20 +167,25 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) a_base[ks] = smem_addr + (uint32_t)tile_off<D>(s_row, 2 * ks + h);
 
-    issue(0, Int<0>{});
-    if (STAGES == 3 && nkb > 1) issue(1, Int<1>{});
-
-    // Q fragments: B operand of S^T = K Q^T (column = query, k = head dim).
-    // Loaded after the first ring stages are requested so the latencies
-    // overlap; the full wait tells the compiler's wait pass that no load into a
-    // register is pending inside the loop (else it drains the ring there).
+    // Q fragments (B operand of S^T = K Q^T: column = query, k = head dim)
+    // first, then the first ring stages; the wait leaves the stages in flight
+    // (the loop waits for each) and tells the compiler's wait pass that no load
+    // into a register is pending inside the loop (else it drains the ring there).
     u32x4 qf[KS];
     {
         const uint16_t* qp = Q + (size_t)min(q0 + l32, N - 1) * D + 8 * h;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
     }
-    wait_vmcnt<0>();
+    issue(0, Int<0>{});
+    if (STAGES == 3 && nkb > 1) {
+        issue(1, Int<1>{});
+        wait_vmcnt<4 * HALF>();
+    } else {
+        wait_vmcnt<2 * HALF>();
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) settle(qf[ks]);
 
     for_ring<STAGES>(nkb, [&](auto slot_c, int kb) {
         constexpr int SLOT = decltype(slot_c)::value;
