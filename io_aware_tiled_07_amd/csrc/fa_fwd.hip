@@ -70,14 +70,27 @@ struct FwdArgs {
     float* lse;
     int BH, N, nqb;
     int heads_per_xcd;  // > 0: XCD-aware mapping (B*H multiple of 8)
+    int cu_rounds;      // > 0: every workgroup is resident at once, cu_rounds per CU (causal only)
     float c;            // scale * log2(e)
 };
+
+constexpr int kCusPerXcd = 32;  // MI350-series: 256 CUs in 8 XCDs
 
 __device__ __forceinline__ void map_block(int bid, const FwdArgs& a, int& bh, int& qb) {
     if (a.heads_per_xcd > 0) {
         // Workgroup ids are dealt to the 8 XCDs round robin; give XCD x the heads
         // h with h % 8 == x and hand them out last query block first.
-        const int xcd = bid & 7, slot = bid >> 3;
+        const int xcd = bid & 7;
+        int slot = bid >> 3;
+        if (a.cu_rounds > 0) {
+            // All workgroups of the XCD are resident together and its k-th is
+            // placed on CU k % 32 in round k / 32. Dealing the longest-first
+            // list to the CUs in a snake (round r runs backwards when r is odd)
+            // gives every CU a long, a middle and a short query block, so the
+            // CUs carry nearly equal causal work.
+            const int j = slot % kCusPerXcd, r = slot / kCusPerXcd;
+            slot = r * kCusPerXcd + ((r & 1) ? kCusPerXcd - 1 - j : j);
+        }
         qb = a.nqb - 1 - slot / a.heads_per_xcd;
         bh = (slot % a.heads_per_xcd) * 8 + xcd;
     } else {
@@ -341,6 +354,11 @@ hipError_t launch(FwdArgs a, hipStream_t stream) {
     using S = FwdShape<D>;
     a.nqb = (a.N + S::BR - 1) / S::BR;
     a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+    // resident workgroups per CU: 3 at head dim 64, 2 at 128 (registers and LDS)
+    constexpr int kResident = D == 64 ? 3 : 2;
+    const int per_xcd = a.heads_per_xcd * a.nqb;
+    a.cu_rounds = (C && a.heads_per_xcd > 0 && per_xcd % kCusPerXcd == 0 && per_xcd <= kResident * kCusPerXcd)
+                      ? per_xcd / kCusPerXcd : 0;
     hipLaunchKernelGGL((fwd_kernel<T, D, C, S::NW>), dim3(a.BH * a.nqb), dim3(64 * S::NW), 0, stream, a);
     return hipGetLastError();
 }
@@ -365,6 +383,7 @@ hipError_t fwd_mfma(const void* q, const void* k, const void* v, void* o, float*
     a.N = N;
     a.nqb = 0;
     a.heads_per_xcd = 0;
+    a.cu_rounds = 0;
     a.c = scale * kLog2e;
     return dtype == 0 ? dispatch_d<Bf16>(a, d, causal, stream) : dispatch_d<F16>(a, d, causal, stream);
 }
