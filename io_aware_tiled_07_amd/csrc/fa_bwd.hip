@@ -89,6 +89,7 @@ static_assert((kSlots - 1) * kKvStage + 32 * kRowB + kKvTileB + 16 * kRowB + 16 
                   (kSlots - 1) * kQStage + kQTileB + 48 * kRowB + 16 <= 65536,
               "LDS offsets must fit the immediate field");
 static_assert(kKvTC % 4 == 0 && kQTC % 4 == 0, "a stage splits evenly over the four waves");
+static_assert(4 * 2048 * DT <= kQStage && 4 * 2048 * DT <= kKvStage, "the epilogues' staging fits one ring slot");
 
 // s_waitcnt leaving `ahead` stages of PER loads each in flight (0 <= ahead <= MAX).
 template <int PER, int MAX>
@@ -423,21 +424,12 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         half(Int<1>{});
     });
 
-    if (key < N) {
-        uint16_t* dkp = a.dk + head + (size_t)key * D + 4 * h;
-        uint16_t* dvp = a.dv + head + (size_t)key * D + 4 * h;
-#pragma unroll
-        for (int u = 0; u < DT; ++u) {
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                const int i = 4 * gg;
-                *reinterpret_cast<u32x2*>(dkp + 32 * u + 8 * gg) =
-                    u32x2{T::pack2(dk[u][i] * a.scale, dk[u][i + 1] * a.scale),
-                          T::pack2(dk[u][i + 2] * a.scale, dk[u][i + 3] * a.scale)};
-                *reinterpret_cast<u32x2*>(dvp + 32 * u + 8 * gg) =
-                    u32x2{T::pack2(dv[u][i], dv[u][i + 1]), T::pack2(dv[u][i + 2], dv[u][i + 3])};
-            }
-        }
+    // dK, dV go out row by row through a ring slot no wave reads any more (the
+    // last stage's barrier retired every earlier stage; nothing is in flight)
+    {
+        char* stage = smem + (nst % kSlots) * kKvStage + wave * (2048 * DT);
+        store_rows<T, DT>(dk, a.scale, a.dk + head + (size_t)kw0 * D, D, N - kw0, stage);
+        store_rows<T, DT>(dv, 1.f, a.dv + head + (size_t)kw0 * D, D, N - kw0, stage);
     }
 }
 
@@ -644,18 +636,9 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
         else block(slot_c, Unmasked{}, key0);
     });
 
-    if (wave_active && qrow < N) {
-        uint16_t* qp = a.dq + head + (size_t)qrow * D + 4 * h;
-#pragma unroll
-        for (int u = 0; u < DT; ++u) {
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                const int i = 4 * gg;
-                *reinterpret_cast<u32x2*>(qp + 32 * u + 8 * gg) =
-                    u32x2{T::pack2(dqa[u][i] * a.scale, dqa[u][i + 1] * a.scale),
-                          T::pack2(dqa[u][i + 2] * a.scale, dqa[u][i + 3] * a.scale)};
-            }
-        }
+    if (wave_active) {
+        char* stage = smem + (nkb % kSlots) * kQStage + wave * (2048 * DT);
+        store_rows<T, DT>(dqa, a.scale, a.dq + head + (size_t)q0 * D, D, N - q0, stage);
     }
 }
 

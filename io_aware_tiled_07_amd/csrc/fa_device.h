@@ -160,6 +160,38 @@ __device__ __forceinline__ i32x4 rows_rsrc(const void* base, int n, int r0) {
     return buffer_rsrc(static_cast<const char*>(base) + (int64_t)r0 * RB, left);
 }
 
+// ---------------------------------------------------------------- row stores
+// A wave's 32 x (32 DT) block in MFMA accumulator order (lane l holds column
+// l % 32; register 4g + k of tile u holds element 32u + 8g + 4(l / 32) + k of
+// that column) is scaled by `mul` (per lane), rounded to T's element type and
+// written out as 32 rows of 32 DT elements: column r goes to dst + r * ld,
+// columns >= nrows are skipped. The block goes through `lds` (wave-private,
+// 2048 DT bytes, 16-byte chunks XOR-swizzled by row), so that each global store
+// writes 16 contiguous bytes and one store instruction covers whole rows.
+template <typename T, int DT>
+__device__ __forceinline__ void store_rows(const f32x16 (&acc)[DT], float mul, uint16_t* dst, int ld, int nrows,
+                                           char* lds) {
+    constexpr int RB = 64 * DT;    // bytes per row
+    constexpr int CPR = RB / 16;   // 16-byte chunks per row
+    constexpr int RPI = 1024 / RB; // rows per wave-wide 16-byte access
+    const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int u = 0; u < DT; ++u)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int c = 4 * u + g;  // chunk of elements 32u + 8g .. 32u + 8g + 7
+            const u32x2 w = {T::pack2(acc[u][4 * g] * mul, acc[u][4 * g + 1] * mul),
+                             T::pack2(acc[u][4 * g + 2] * mul, acc[u][4 * g + 3] * mul)};
+            *reinterpret_cast<u32x2*>(lds + r * RB + ((c ^ (r & (CPR - 1))) << 4) + 8 * h) = w;
+        }
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int rr = i * RPI + lane / CPR, cc = lane % CPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + rr * RB + ((cc ^ (rr & (CPR - 1))) << 4));
+        if (rr < nrows) *reinterpret_cast<u32x4*>(dst + (size_t)rr * ld + cc * 8) = v;
+    }
+}
+
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

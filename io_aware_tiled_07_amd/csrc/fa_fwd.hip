@@ -112,6 +112,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     constexpr int BR = 32 * NW;          // query rows per workgroup
     static_assert(HALF * NW == KCH, "block must split evenly over the waves");
     static_assert((STAGES - 1) * SB + TB + 3 * 16 * 2 * D < 65536, "ds offsets must fit 16 bits");
+    static_assert(NW * 2048 * DT <= SB, "the epilogue's staging fits one ring slot");
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
 
     const int lane = threadIdx.x & 63;
@@ -325,21 +326,15 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     });
 
     // ---- epilogue: O = O_acc / l, lse = ln2 * (m + log2 l)
+    // (O goes out row by row through a ring slot no wave reads any more: the
+    // last iteration's barrier retired every block but the last, and no copy
+    // into that slot is in flight)
     const float l_tot = pair_sum(l_run);
     const int qrow = q0 + l32;
-    if (wave_active && qrow < N) {
-        const float inv = 1.f / l_tot;
-        uint16_t* op = a.o + head + (size_t)qrow * D + 4 * h;
-#pragma unroll
-        for (int u = 0; u < DT; ++u) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const u32x2 w = {T::pack2(oacc[u][4 * g] * inv, oacc[u][4 * g + 1] * inv),
-                                 T::pack2(oacc[u][4 * g + 2] * inv, oacc[u][4 * g + 3] * inv)};
-                *reinterpret_cast<u32x2*>(op + 32 * u + 8 * g) = w;
-            }
-        }
-        if (h == 0) a.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    if (wave_active) {
+        char* stage = smem + (nkb % STAGES) * SB + wave * (2048 * DT);
+        store_rows<T, DT>(oacc, 1.f / l_tot, a.o + head + (size_t)q0 * D, D, N - q0, stage);
+        if (h == 0 && qrow < N) a.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
     }
 }
 
