@@ -58,9 +58,9 @@ COPY_PROBE_KIB = 262144
 COUNTERS = {
     # workload: {stage: (FETCH_SIZE KiB, WRITE_SIZE KiB, copy FETCH_SIZE KiB, copy WRITE_SIZE KiB, sources sha)}
     "gpt2_small_causal": {
-        "fwd": (18655.1, 12672.0, 131092.0, 262144.0, "766d855969262cda"),
-        "prep": (12493.3, 768.0, 131092.0, 262144.0, "c0c49f9eac170e64"),
-        "main": (61312.3, 46894.7, 131092.0, 262144.0, "c0c49f9eac170e64"),
+        "fwd": (18535.8, 12672.0, 131092.5, 262144.0, "a78f81a51783dda4"),
+        "prep": (12493.3, 768.0, 131092.5, 262144.0, "2ffc48677a793cae"),
+        "main": (64158.5, 36864.0, 131092.5, 262144.0, "2ffc48677a793cae"),
     },
 }
 
