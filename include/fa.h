@@ -49,7 +49,7 @@ typedef enum {
     FA_ERR_INVALID_ARG = 1,  /* null or misaligned pointer, B/H/N < 1, causal not 0/1,
                                 scale not finite and > 0, overlapping buffers, size overflow */
     FA_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}, unknown dtype, fp32 with d = 128,
-                                unknown dQ strategy */
+                                unknown dQ strategy, FA_DQ_ATOMIC with 16-bit d = 128 */
     FA_ERR_WORKSPACE = 3,    /* workspace null, not 256-byte aligned, or smaller than
                                 fa_bwd_workspace_size() */
     FA_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError after launch) */
@@ -93,15 +93,16 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype);
  *                     256-byte aligned; its contents on entry do not matter.
  * Reads only q, k, v, o, dout and lse; recomputes every score and probability tile
  * on chip from them (michaelc-yu summary of Dao et al., "Backward / recomputation").
- * 16-bit inputs need d = 64. Uses the default dQ strategy. Equivalent to
- * fa_bwd_prep() followed by fa_bwd_main(). Returns a fa_status.
+ * 16-bit inputs: d in {64, 128}; fp32: d = 64. Uses the default dQ strategy.
+ * Equivalent to fa_bwd_prep() followed by fa_bwd_main(). Returns a fa_status.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, float scale, int causal, int dtype,
            void* workspace, size_t workspace_bytes, void* stream);
 
-/* fa_bwd() with an explicit fa_dq_strategy (ignored for FA_FP32, which has one path). */
+/* fa_bwd() with an explicit fa_dq_strategy (ignored for FA_FP32, which has one path;
+ * FA_DQ_ATOMIC exists for d = 64 only and returns FA_ERR_UNSUPPORTED for 16-bit d = 128). */
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
               const float* lse, void* dq, void* dk, void* dv,
               int B, int H, int N, int d, float scale, int causal, int dtype, int dq_strategy,

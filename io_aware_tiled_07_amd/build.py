@@ -15,7 +15,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_atomic.hip", "fa_fp32.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd128.hip", "fa_bwd_atomic.hip", "fa_fp32.hip"]
+# MFMA results stay in arch VGPRs (the softmax reads them directly, no AGPR
+# copies) everywhere except the head-dim-128 backward, whose fp32 accumulators
+# need the AGPRs beside the 256 VGPRs.
+AGPR_SOURCES = {"fa_bwd128.hip"}
 ARCH = "gfx950"
 
 
@@ -26,23 +30,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libfa.so)")
 
 
-def flags() -> list[str]:
-    return [
+def flags(src: str = "") -> list[str]:
+    f = [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # no packed fp32 instructions anywhere in the device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-munsafe-fp-atomics",
         # inputs are finite: max/min need no NaN canonicalisation
         "-fno-honor-nans",
-        # MFMA results in arch VGPRs: the softmax reads them directly, no AGPR copies
-        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     ]
+    if src not in AGPR_SOURCES:
+        f += ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+    return f
 
 
 def _compile(src: str, build_dir: str, extra: tuple) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags() + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + flags(src) + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -54,7 +59,7 @@ def device_asm(src: str, extra_flags=()) -> str:
     import tempfile
     with tempfile.TemporaryDirectory() as tmp:
         out = os.path.join(tmp, "k.s")
-        cmd = [hipcc()] + flags() + list(extra_flags) + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+        cmd = [hipcc()] + flags(src) + list(extra_flags) + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")

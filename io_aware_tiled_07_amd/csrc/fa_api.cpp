@@ -31,14 +31,12 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 int elt_bytes(int dtype) { return dtype == FA_FP32 ? 4 : 2; }
 
 // Shape, dtype, head-dim and scalar checks shared by the forward and backward.
-int check_common(int B, int H, int N, int d, float scale, int causal, int dtype, bool backward) {
+int check_common(int B, int H, int N, int d, float scale, int causal, int dtype) {
     if (dtype != FA_BF16 && dtype != FA_FP16 && dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
     if (dtype == FA_FP32) {
-        if (d != 64) return FA_ERR_UNSUPPORTED;
-    } else if (backward) {
         if (d != 64) return FA_ERR_UNSUPPORTED;
     } else if (d != 64 && d != 128) {
         return FA_ERR_UNSUPPORTED;
@@ -51,6 +49,11 @@ int check_common(int B, int H, int N, int d, float scale, int causal, int dtype,
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
 bool known_strategy(int s) { return s == FA_DQ_DEFAULT || s == FA_DQ_ATOMIC || s == FA_DQ_SEPARATE; }
+
+// The atomic dQ strategy exists for d = 64 only.
+bool strategy_supported(int s, int d, int dtype) {
+    return known_strategy(s) && !(s == FA_DQ_ATOMIC && dtype != FA_FP32 && d != 64);
+}
 
 // Workspace of the backward: D ([B,H,N] float), lse * log2(e) ([B,H,N] float)
 // and, for 16-bit inputs, the fp32 dQ accumulator of the atomic strategy
@@ -72,9 +75,9 @@ Workspace layout(int B, int H, int N, int d, int dtype) {
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
               void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
               int dq_strategy, void* workspace, size_t workspace_bytes) {
-    int st = check_common(B, H, N, d, scale, causal, dtype, /*backward=*/true);
+    int st = check_common(B, H, N, d, scale, causal, dtype);
     if (st != FA_OK) return st;
-    if (!known_strategy(dq_strategy)) return FA_ERR_UNSUPPORTED;
+    if (!strategy_supported(dq_strategy, d, dtype)) return FA_ERR_UNSUPPORTED;
     const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
     for (const void* p : ptrs)
         if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
@@ -112,7 +115,7 @@ const char* fa_status_string(int status) {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
            float scale, int causal, int dtype, void* stream) {
-    int st = check_common(B, H, N, d, scale, causal, dtype, /*backward=*/false);
+    int st = check_common(B, H, N, d, scale, causal, dtype);
     if (st != FA_OK) return st;
     const void* ptrs[] = {q, k, v, o, lse};
     for (const void* p : ptrs)
@@ -145,9 +148,9 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
 
 int fa_bwd_prep(const void* o, const void* dout, const float* lse, int B, int H, int N, int d, int dtype,
                 int dq_strategy, void* workspace, size_t workspace_bytes, void* stream) {
-    int st = check_common(B, H, N, d, 1.f, 0, dtype, /*backward=*/true);
+    int st = check_common(B, H, N, d, 1.f, 0, dtype);
     if (st != FA_OK) return st;
-    if (!known_strategy(dq_strategy)) return FA_ERR_UNSUPPORTED;
+    if (!strategy_supported(dq_strategy, d, dtype)) return FA_ERR_UNSUPPORTED;
     const void* ptrs[] = {o, dout, lse};
     for (const void* p : ptrs)
         if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
@@ -168,7 +171,7 @@ int fa_bwd_prep(const void* o, const void* dout, const float* lse, int B, int H,
     if (dq_strategy == FA_DQ_ATOMIC)
         e = fa::bwd_atomic_prep(o, dout, B, H, N, dtype, delta, reinterpret_cast<float*>(base + w.dq_acc), s);
     else
-        e = fa::bwd_prep(o, dout, lse, B, H, N, dtype, delta, reinterpret_cast<float*>(base + w.lse2), s);
+        e = fa::bwd_prep(o, dout, lse, B, H, N, d, dtype, delta, reinterpret_cast<float*>(base + w.lse2), s);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -191,6 +194,9 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* o, cons
     } else if (dq_strategy == FA_DQ_ATOMIC) {
         e = fa::bwd_atomic_main(q, k, v, dout, lse, dq, dk, dv, B, H, N, scale, causal != 0, dtype, delta,
                                 reinterpret_cast<float*>(base + w.dq_acc), s);
+    } else if (d == 128) {
+        e = fa::bwd128_fused(q, k, v, dout, delta, reinterpret_cast<const float*>(base + w.lse2), dq, dk, dv, B, H,
+                             N, scale, causal != 0, dtype, s);
     } else {
         e = fa::bwd_fused(q, k, v, dout, delta, reinterpret_cast<const float*>(base + w.lse2), dq, dk, dv, B, H, N,
                           scale, causal != 0, dtype, s);

@@ -18,7 +18,7 @@
 //     data and run side by side:
 //     * key workgroups (128 keys, 32 per wave): K and V rows of the wave stay
 //       in VGPRs, dK^T and dV^T in fp32 accumulators. Query stages (64 rows of
-//       Q and dO and their statistics) stream HBM -> LDS through a 3-slot
+//       Q and dO and their statistics) stream HBM -> LDS through a 4-slot
 //       LDS-DMA ring; per 32 queries a wave forms S = Q K^T and dP = dO V^T
 //       (lane = key), then P and dS in registers, then dV^T += dO^T P and
 //       dK^T += Q^T dS with the dO^T / Q^T operands read transposed from LDS
@@ -34,7 +34,7 @@
 //  Causal: tiles wholly above the diagonal are skipped; only tiles crossing it
 //  (or the ragged end of the sequence) run the element-wise mask, on a code
 //  path of their own.
-//  The ring loop is unrolled over its three slots, so every LDS read is a
+//  The ring loop is unrolled over its four slots, so every LDS read is a
 //  loop-invariant base register plus an immediate offset.
 //
 // The dQ pass recomputes S and dP (7 matrix products in total instead of 5),
@@ -134,25 +134,27 @@ struct PrepArgs {
 };
 
 // ---------------------------------------------------------------- 1. prep
-// 8 lanes per row, 8 elements each; a workgroup covers kPrepRounds rounds of
-// 32 rows, every round's loads issued before any sum. One round per workgroup
-// measured fastest: more workgroups in flight beat more rows per lane.
+// PD / 8 lanes per row (head dim PD), 8 elements each; a workgroup covers
+// kPrepRounds rounds of rows, every round's loads issued before any sum. One
+// round per workgroup measured fastest: more workgroups in flight beat more
+// rows per lane.
 constexpr int kPrepRounds = 1;
-constexpr int kPrepRows = kPrepRounds * kThreads / (D / 8);
+template <int PD>
+constexpr int kPrepRows = kPrepRounds * kThreads / (PD / 8);
 
-template <typename T>
+template <typename T, int PD>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(PrepArgs a) {
-    constexpr int LPR = D / 8;
+    constexpr int LPR = PD / 8;
     constexpr int RPR = kThreads / LPR;  // rows per round
     const int tid = threadIdx.x, part = tid % LPR;
-    const int64_t row0 = (int64_t)blockIdx.x * kPrepRows + tid / LPR;
+    const int64_t row0 = (int64_t)blockIdx.x * kPrepRows<PD> + tid / LPR;
     u32x4 ov[kPrepRounds], dv[kPrepRounds];
 #pragma unroll
     for (int k = 0; k < kPrepRounds; ++k) {
         const int64_t row = row0 + k * RPR;
         const int64_t r = row < a.rows ? row : a.rows - 1;
-        ov[k] = *reinterpret_cast<const u32x4*>(a.o + r * D + part * 8);
-        dv[k] = *reinterpret_cast<const u32x4*>(a.dout + r * D + part * 8);
+        ov[k] = *reinterpret_cast<const u32x4*>(a.o + r * PD + part * 8);
+        dv[k] = *reinterpret_cast<const u32x4*>(a.dout + r * PD + part * 8);
     }
 #pragma unroll
     for (int k = 0; k < kPrepRounds; ++k) {
@@ -667,8 +669,8 @@ hipError_t launch_fused(FusedArgs a, bool causal, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t bwd_prep(const void* o, const void* dout, const float* lse, int B, int H, int N, int dtype, float* delta,
-                    float* lse2, hipStream_t stream) {
+hipError_t bwd_prep(const void* o, const void* dout, const float* lse, int B, int H, int N, int d, int dtype,
+                    float* delta, float* lse2, hipStream_t stream) {
     PrepArgs p;
     p.o = static_cast<const uint16_t*>(o);
     p.dout = static_cast<const uint16_t*>(dout);
@@ -676,11 +678,19 @@ hipError_t bwd_prep(const void* o, const void* dout, const float* lse, int B, in
     p.delta = delta;
     p.lse2 = lse2;
     p.rows = (int64_t)B * H * N;
-    const dim3 grid((unsigned)((p.rows + kPrepRows - 1) / kPrepRows));
-    if (dtype == 0)
-        hipLaunchKernelGGL((bwd_prep_kernel<Bf16>), grid, dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((bwd_prep_kernel<F16>), grid, dim3(kThreads), 0, stream, p);
+    if (d == 128) {
+        const dim3 grid((unsigned)((p.rows + kPrepRows<128> - 1) / kPrepRows<128>));
+        if (dtype == 0)
+            hipLaunchKernelGGL((bwd_prep_kernel<Bf16, 128>), grid, dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((bwd_prep_kernel<F16, 128>), grid, dim3(kThreads), 0, stream, p);
+    } else {
+        const dim3 grid((unsigned)((p.rows + kPrepRows<64> - 1) / kPrepRows<64>));
+        if (dtype == 0)
+            hipLaunchKernelGGL((bwd_prep_kernel<Bf16, 64>), grid, dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((bwd_prep_kernel<F16, 64>), grid, dim3(kThreads), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

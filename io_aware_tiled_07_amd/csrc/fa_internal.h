@@ -12,13 +12,17 @@ namespace fa {
 hipError_t fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                     int N, int d, float scale, bool causal, int dtype, hipStream_t stream);
 
-// 16-bit backward, default strategy: D_i = dO_i . O_i and lse_i * log2(e)
-// into delta / lse2 ([B,H,N] float each), then one fused launch for dQ, dK, dV.
-hipError_t bwd_prep(const void* o, const void* dout, const float* lse, int B, int H, int N, int dtype, float* delta,
-                    float* lse2, hipStream_t stream);
+// 16-bit backward, default strategy: -D_i = -dO_i . O_i and lse_i * log2(e)
+// into delta / lse2 ([B,H,N] float each; d in {64, 128}), then one fused
+// launch for dQ, dK, dV (bwd_fused: d = 64, bwd128_fused: d = 128).
+hipError_t bwd_prep(const void* o, const void* dout, const float* lse, int B, int H, int N, int d, int dtype,
+                    float* delta, float* lse2, hipStream_t stream);
 hipError_t bwd_fused(const void* q, const void* k, const void* v, const void* dout, const float* delta,
                      const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale, bool causal,
                      int dtype, hipStream_t stream);
+hipError_t bwd128_fused(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                        const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale, bool causal,
+                        int dtype, hipStream_t stream);
 
 // 16-bit backward with fp32 atomics for dQ: the prologue computes delta and
 // zeroes dq_acc ([B,H,N,64] float); the main step adds into dq_acc and converts.

@@ -102,7 +102,8 @@ def bwd(lib, B=2, H=3, N=100, d=64, scale=0.125, causal=0, dtype=0, strategy=0, 
 @pytest.mark.parametrize("kw,code", [
     (dict(do=0), fa.FA_ERR_INVALID_ARG),
     (dict(dk=A + 4 * GAP + 2), fa.FA_ERR_INVALID_ARG),
-    (dict(d=128), fa.FA_ERR_UNSUPPORTED),            # 16-bit backward is d = 64
+    (dict(d=128, strategy=fa.FA_DQ_ATOMIC), fa.FA_ERR_UNSUPPORTED),  # atomic dQ is d = 64 only
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),             # 16-bit backward: d in {64, 128}
     (dict(d=32), fa.FA_ERR_UNSUPPORTED),
     (dict(strategy=3), fa.FA_ERR_UNSUPPORTED),
     (dict(ws=0), fa.FA_ERR_WORKSPACE),
@@ -149,7 +150,8 @@ def prep(lib, B=2, H=3, N=100, d=64, dtype=0, strategy=0, o=None, do=None, lse=N
     (dict(o=0), fa.FA_ERR_INVALID_ARG),
     (dict(lse=A + 2 * GAP + 4), fa.FA_ERR_INVALID_ARG),
     (dict(N=0), fa.FA_ERR_INVALID_ARG),
-    (dict(d=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=128, strategy=fa.FA_DQ_ATOMIC), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=5), fa.FA_ERR_UNSUPPORTED),
     (dict(strategy=7), fa.FA_ERR_UNSUPPORTED),
     (dict(ws=0), fa.FA_ERR_WORKSPACE),
@@ -168,7 +170,8 @@ def test_prep_fp32_is_a_validated_no_op(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), fa.FA_ERR_INVALID_ARG),
-    (dict(d=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=128, strategy=fa.FA_DQ_ATOMIC), fa.FA_ERR_UNSUPPORTED),
     (dict(strategy=3), fa.FA_ERR_UNSUPPORTED),
     (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE),
     (dict(dk=A + 6 * GAP), fa.FA_ERR_INVALID_ARG),    # dk aliases dq

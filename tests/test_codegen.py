@@ -1,9 +1,12 @@
 """Properties of the generated gfx950 code, checked on the CPU from hipcc's assembly.
 
-* No kernel spills to scratch, and no kernel that reads LDS from inline asm
-  (and waits for the data explicitly) copies registers through AGPRs: a spill
-  or copy placed by the compiler between such a read and its wait would copy
-  data that has not arrived yet. (MFMA results live in arch VGPRs.)
+* No kernel spills to scratch.
+* No compiler-generated instruction touches a register that an inline-asm LDS
+  read is still filling (the kernels wait for those reads explicitly; a copy,
+  spill or use placed by the compiler before the wait would see data that has
+  not arrived). Checked by a dataflow walk over each kernel's control-flow graph.
+* Kernels that read LDS from inline asm and are compiled with MFMA results in
+  arch VGPRs use no AGPRs at all.
 * No packed fp32 instructions (v_pk_fma_f32, v_pk_mul_f32, v_pk_add_f32)
   anywhere in the device code.
 """
@@ -12,6 +15,7 @@ import shutil
 
 import pytest
 
+from _lds_hazards import asm_lds_reads, check_kernel
 from io_aware_tiled_07_amd import build as fabuild
 
 HIP_SOURCES = [s for s in fabuild.SOURCES if s.endswith(".hip")]
@@ -37,18 +41,72 @@ def kernels(text):
     return out
 
 
-def test_no_spills_or_agpr_copies(asm):
+def test_no_spills(asm):
     src, text = asm
     ks = kernels(text)
     assert ks, f"no kernels found in {src}"
     for name, body in ks:
-        asm_lds = re.search(r";;#ASMSTART\s*\n\s*ds_read", body) is not None
-        if asm_lds:
-            assert "v_accvgpr_write" not in body and "v_accvgpr_read" not in body, \
-                f"{src}: {name} copies through AGPRs"
         assert "scratch_" not in body and "buffer_store_dword" not in body, f"{src}: {name} spills to scratch"
+        if src not in fabuild.AGPR_SOURCES and asm_lds_reads(body):
+            assert "v_accvgpr" not in body, f"{src}: {name} uses AGPRs"
     for m in re.finditer(r"; ScratchSize: (\d+)", text):
         assert m.group(1) == "0", f"{src}: scratch in use"
+
+
+def test_asm_lds_reads_are_waited_for(asm):
+    src, text = asm
+    for name, body in kernels(text):
+        bad = check_kernel(body)
+        assert not bad, f"{src}: {name} touches in-flight LDS data: {bad[:4]}"
+
+
+def test_backward_kernels_read_lds_from_asm(asm):
+    """The hazard check above has something to check in the backward kernels."""
+    src, text = asm
+    if src not in ("fa_bwd.hip", "fa_bwd128.hip"):
+        pytest.skip("forward / other files")
+    for name, body in kernels(text):
+        if "fused" in name:
+            assert asm_lds_reads(body) > 50, name
+
+
+SYNTH = """
+_Zk:
+  s_load_dwordx2 s[0:1], s[4:5], 0x0
+  ;;#ASMSTART
+  ds_read_b128 v[4:7], v1 offset:16
+  ;;#ASMEND
+  ;;#ASMSTART
+  ds_read_b64_tr_b16 v[8:9], v1 offset:32
+  ;;#ASMEND
+  {early}
+  ;;#ASMSTART
+  s_waitcnt lgkmcnt(1)
+  ;;#ASMEND
+  v_mov_b32 v20, v5
+  {middle}
+  s_cbranch_scc0 .LBB0_2
+  ;;#ASMSTART
+  s_waitcnt lgkmcnt(0)
+  ;;#ASMEND
+.LBB0_2:
+  {late}
+  s_endpgm
+.Lfunc_end0:
+"""
+
+
+@pytest.mark.parametrize("early,middle,late,flagged", [
+    ("", "", "", 0),
+    ("v_accvgpr_write_b32 a0, v6", "", "", 1),   # copy of a read before any wait
+    ("", "v_add_f32_e32 v21, v8, v20", "", 1),   # second read not retired by lgkmcnt(1)
+    ("", "", "v_mov_b32 v22, v9", 1),            # waited on one path only
+    ("", "", "v_mov_b32 v22, v7", 0),            # first read retired on every path
+    ("", "v_mov_b32 v9, 0", "", 1),              # overwrite of an in-flight destination
+])
+def test_hazard_check_on_synthetic_code(early, middle, late, flagged):
+    body = SYNTH.format(early=early, middle=middle, late=late)
+    assert len(check_kernel(body)) == flagged
 
 
 def test_no_packed_fp32(asm):

@@ -151,6 +151,28 @@ def test_ragged_backward(N, causal, strategy):
     check_all(drawn, outs, "bf16", causal)
 
 
+@pytest.mark.parametrize("N", [1, 7, 129, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_backward_d128(N, causal):
+    """Head dim 128 backward on ragged lengths; B*H = 3 takes the plain
+    (not XCD-grouped) workgroup mapping."""
+    log(f"ragged bwd d=128 N={N} causal={causal}")
+    drawn, outs = run_fwd_bwd(3128 + N, (1, 3, N, 128), "bf16", causal)
+    check_all(drawn, outs, "bf16", causal)
+
+
+@pytest.mark.parametrize("dtype,causal", [("bf16", True), ("bf16", False), ("fp16", True)])
+def test_backward_d128(dtype, causal):
+    """Head dim 128 backward over 2 x 8 heads of 2048 (XCD-grouped mapping,
+    several rounds of the 4-slot ring per workgroup): two seeded heads checked
+    completely against the oracle."""
+    log(f"bwd d=128 2x8x2048 {dtype} causal={causal}")
+    shape = (2, 8, 2048, 128)
+    drawn, outs = run_fwd_bwd(1128, shape, dtype, causal)
+    h0, h1 = (int(x) for x in seedgen.choice_rows(1128, 7, 8, 2))
+    check_all(drawn, outs, dtype, causal, heads=[(0, h0), (1, h1)])
+
+
 @pytest.mark.parametrize("N", [1, 7, 129])
 def test_ragged_fp32(N):
     drawn, outs = run_fwd_bwd(4000 + N, (1, 2, N, 64), "fp32", True)
