@@ -59,6 +59,12 @@ def _load():
         lib.oracle_bwd.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_double, ctypes.c_int,
                                    _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        mask_args = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64]
+        lib.oracle_fwd_masked.argtypes = ([_dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_double, ctypes.c_int] + mask_args + [_dp, _dp])
+        lib.oracle_bwd_masked.argtypes = ([_dp, _dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_double, ctypes.c_int] + mask_args +
+                                          [_dp, _dp, _dp, _dp, _dp, _dp, _dp])
         _lib = lib
     return _lib
 
@@ -79,16 +85,37 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
-def fwd(q, k, v, scale: float, causal: bool):
-    """Standard attention forward: returns (O [B,H,N,d], lse [B,H,N])."""
+def _block_mask(block_mask, B, H, N, block):
+    """(mask array, nb, per-head stride in bytes) for the C side; block_mask is
+    [nb, nb] (one mask for every head) or [B, H, nb, nb], nonzero = kept."""
+    nb = (N + block - 1) // block
+    m = np.ascontiguousarray(block_mask, dtype=np.uint8)
+    if m.shape == (nb, nb):
+        return m, nb, 0
+    if m.shape == (B, H, nb, nb):
+        return m, nb, nb * nb
+    raise ValueError(f"block mask must be [{nb},{nb}] or [{B},{H},{nb},{nb}], got {m.shape}")
+
+
+def fwd(q, k, v, scale: float, causal: bool, block_mask=None, block: int = 128):
+    """Standard attention forward: returns (O [B,H,N,d], lse [B,H,N]).
+
+    With ``block_mask`` (block-sparse attention), pair (i, j) is kept only if
+    ``block_mask[i // block, j // block]`` is nonzero (per head if the mask is
+    [B, H, nb, nb]); rows with no kept key get O = 0 and lse = -inf."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = q.shape
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share one shape")
     o = np.empty_like(q)
     lse = np.empty((B, H, N), dtype=np.float64)
-    _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), int(bool(causal)),
-                       _ptr(o), _ptr(lse))
+    if block_mask is None:
+        _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), int(bool(causal)),
+                           _ptr(o), _ptr(lse))
+    else:
+        m, nb, stride = _block_mask(block_mask, B, H, N, block)
+        _load().oracle_fwd_masked(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), int(bool(causal)),
+                                  m.ctypes.data, nb, block, stride, _ptr(o), _ptr(lse))
     return o, lse
 
 
@@ -107,10 +134,11 @@ def fwd_rows(q, k, v, scale: float, causal: bool, rows):
     return o, lse
 
 
-def bwd(q, k, v, dout, scale: float, causal: bool) -> dict:
+def bwd(q, k, v, dout, scale: float, causal: bool, block_mask=None, block: int = 128) -> dict:
     """Forward plus analytic backward of ``L = sum(dout * O)``.
 
     Returns a dict with o, lse, dq, dk, dv, D_pdp (sum_j P_ij dP_ij) and D_odo (dO_i . O_i).
+    ``block_mask`` / ``block`` as in :func:`fwd`.
     """
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, H, N, d = q.shape
@@ -120,7 +148,12 @@ def bwd(q, k, v, dout, scale: float, causal: bool) -> dict:
     out = {name: np.empty_like(q) for name in ("o", "dq", "dk", "dv")}
     for name in ("lse", "D_pdp", "D_odo"):
         out[name] = np.empty((B, H, N), dtype=np.float64)
-    _load().oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d, float(scale),
-                       int(bool(causal)), _ptr(out["o"]), _ptr(out["lse"]), _ptr(out["dq"]),
-                       _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["D_pdp"]), _ptr(out["D_odo"]))
+    outs = [_ptr(out[n]) for n in ("o", "lse", "dq", "dk", "dv", "D_pdp", "D_odo")]
+    if block_mask is None:
+        _load().oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d, float(scale),
+                           int(bool(causal)), *outs)
+    else:
+        m, nb, stride = _block_mask(block_mask, B, H, N, block)
+        _load().oracle_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d, float(scale),
+                                  int(bool(causal)), m.ctypes.data, nb, block, stride, *outs)
     return out

@@ -34,6 +34,14 @@
  *
  * Masked pairs (causal, j > i) have P_ij = 0 exactly and contribute nothing.
  * All tensors are contiguous [B,H,N,d] (lse and D: [B,H,N]) fp64.
+ *
+ * Block-sparse attention (the michaelc-yu summary of Dao et al. names a
+ * block-sparse extension of the method without defining it): the plainest
+ * reading is the same definition with more pairs masked. A block mask M of
+ * nb x nb bytes per head splits queries and keys into blocks of bs rows;
+ * pair (i, j) is kept iff M[i / bs][j / bs] != 0 (and j <= i when causal).
+ * A query row with no kept pair has P_i = 0, O_i = 0, lse_i = -inf and no
+ * gradient (D_i = 0, dQ_i = 0, and it adds nothing to dK or dV).
  */
 #include <math.h>
 #include <stdint.h>
@@ -50,8 +58,20 @@ static double dot(const double* a, const double* b, int d)
     return s;
 }
 
-/* Number of keys query row i may attend to. */
-static int keys_allowed(int N, int causal, int i) { return causal ? i + 1 : N; }
+/* The keys a head may pair: causal flag and, for block-sparse attention, the
+ * head's block mask (NULL: every block). */
+typedef struct {
+    int causal;
+    const uint8_t* blocks; /* nb x nb, row = query block, column = key block */
+    int nb, bs;
+} Visibility;
+
+/* Is pair (query i, key j) kept? */
+static int visible(const Visibility* vis, int i, int j)
+{
+    if (vis->causal && j > i) return 0;
+    return vis->blocks == NULL || vis->blocks[(size_t)(i / vis->bs) * vis->nb + j / vis->bs] != 0;
+}
 
 /*
  * One query row of the forward: fills p[0..N) with the probabilities P_i.
@@ -59,30 +79,50 @@ static int keys_allowed(int N, int causal, int i) { return causal ? i + 1 : N; }
  * Q, K, V point at one head ([N,d] each).
  */
 static void forward_row(const double* Q, const double* K, const double* V, int N, int d,
-                        double scale, int causal, int i, double* p, double* o_i, double* lse_i)
+                        double scale, const Visibility* vis, int i, double* p, double* o_i, double* lse_i)
 {
-    const int nk = keys_allowed(N, causal, i);
     double m = -INFINITY;
-    for (int j = 0; j < nk; ++j) {
+    int kept = 0;
+    for (int j = 0; j < N; ++j) {
+        if (!visible(vis, i, j)) { p[j] = 0.0; continue; }
         p[j] = scale * dot(Q + (size_t)i * d, K + (size_t)j * d, d);
         if (p[j] > m) m = p[j];
+        ++kept;
+    }
+    for (int c = 0; c < d; ++c) o_i[c] = 0.0;
+    if (kept == 0) { /* no key to attend to */
+        *lse_i = -INFINITY;
+        return;
     }
     double l = 0.0;
-    for (int j = 0; j < nk; ++j) {
+    for (int j = 0; j < N; ++j) {
+        if (!visible(vis, i, j)) continue;
         p[j] = exp(p[j] - m);
         l += p[j];
     }
-    for (int j = 0; j < nk; ++j) p[j] /= l;
-    for (int j = nk; j < N; ++j) p[j] = 0.0;
-    for (int c = 0; c < d; ++c) o_i[c] = 0.0;
-    for (int j = 0; j < nk; ++j)
-        for (int c = 0; c < d; ++c) o_i[c] += p[j] * V[(size_t)j * d + c];
+    for (int j = 0; j < N; ++j) if (visible(vis, i, j)) p[j] /= l;
+    for (int j = 0; j < N; ++j)
+        if (visible(vis, i, j))
+            for (int c = 0; c < d; ++c) o_i[c] += p[j] * V[(size_t)j * d + c];
     *lse_i = m + log(l);
 }
 
-/* Forward for every row of every head. */
-void oracle_fwd(const double* q, const double* k, const double* v, int B, int H, int N, int d,
-                double scale, int causal, double* o, double* lse)
+/* Visibility of head bh: mask bytes of head bh start mask_stride * bh bytes after
+ * mask (stride 0: one mask for every head). */
+static Visibility head_visibility(int causal, const uint8_t* mask, int nb, int bs, int64_t mask_stride, int64_t bh)
+{
+    Visibility v;
+    v.causal = causal;
+    v.blocks = mask ? mask + mask_stride * bh : NULL;
+    v.nb = nb;
+    v.bs = bs;
+    return v;
+}
+
+/* Forward for every row of every head; mask NULL for dense attention. */
+void oracle_fwd_masked(const double* q, const double* k, const double* v, int B, int H, int N, int d,
+                       double scale, int causal, const uint8_t* mask, int nb, int bs, int64_t mask_stride,
+                       double* o, double* lse)
 {
     const int64_t rows = (int64_t)B * H * N;
 #pragma omp parallel
@@ -93,11 +133,18 @@ void oracle_fwd(const double* q, const double* k, const double* v, int B, int H,
             const int64_t bh = r / N;
             const int i = (int)(r % N);
             const size_t head = (size_t)bh * N * d;
-            forward_row(q + head, k + head, v + head, N, d, scale, causal, i, p,
+            const Visibility vis = head_visibility(causal, mask, nb, bs, mask_stride, bh);
+            forward_row(q + head, k + head, v + head, N, d, scale, &vis, i, p,
                         o + (size_t)r * d, lse + r);
         }
         free(p);
     }
+}
+
+void oracle_fwd(const double* q, const double* k, const double* v, int B, int H, int N, int d,
+                double scale, int causal, double* o, double* lse)
+{
+    oracle_fwd_masked(q, k, v, B, H, N, d, scale, causal, NULL, 0, 1, 0, o, lse);
 }
 
 /*
@@ -117,7 +164,8 @@ void oracle_fwd_rows(const double* q, const double* k, const double* v, int B, i
             const int64_t bh = rows[t] / N;
             const int i = (int)(rows[t] % N);
             const size_t head = (size_t)bh * N * d;
-            forward_row(q + head, k + head, v + head, N, d, scale, causal, i, p,
+            const Visibility vis = head_visibility(causal, NULL, 0, 1, 0, bh);
+            forward_row(q + head, k + head, v + head, N, d, scale, &vis, i, p,
                         o_rows + (size_t)t * d, lse_rows + t);
         }
         free(p);
@@ -134,10 +182,11 @@ void oracle_fwd_rows(const double* q, const double* k, const double* v, int B, i
  * column j of P, dP and dS (P_ij = exp(S_ij - lse_i), the same value as pass 1's
  * exp(S_ij - m_i) / l_i) and sums dV_j and dK_j.
  */
-void oracle_bwd(const double* q, const double* k, const double* v, const double* dout,
-                int B, int H, int N, int d, double scale, int causal,
-                double* o, double* lse, double* dq, double* dk, double* dv,
-                double* D_pdp, double* D_odo)
+void oracle_bwd_masked(const double* q, const double* k, const double* v, const double* dout,
+                       int B, int H, int N, int d, double scale, int causal,
+                       const uint8_t* mask, int nb, int bs, int64_t mask_stride,
+                       double* o, double* lse, double* dq, double* dk, double* dv,
+                       double* D_pdp, double* D_odo)
 {
     const int64_t rows = (int64_t)B * H * N;
 #pragma omp parallel
@@ -150,10 +199,11 @@ void oracle_bwd(const double* q, const double* k, const double* v, const double*
             const int i = (int)(r % N);
             const size_t head = (size_t)bh * N * d;
             const double *Q = q + head, *K = k + head, *V = v + head, *dO = dout + head;
-            const int nk = keys_allowed(N, causal, i);
-            forward_row(Q, K, V, N, d, scale, causal, i, p, o + (size_t)r * d, lse + r);
+            const Visibility vis = head_visibility(causal, mask, nb, bs, mask_stride, bh);
+            forward_row(Q, K, V, N, d, scale, &vis, i, p, o + (size_t)r * d, lse + r);
             double Dp = 0.0;
-            for (int j = 0; j < nk; ++j) {
+            for (int j = 0; j < N; ++j) {
+                if (!visible(&vis, i, j)) continue;
                 dp[j] = dot(dO + (size_t)i * d, V + (size_t)j * d, d);
                 Dp += p[j] * dp[j];
             }
@@ -161,7 +211,8 @@ void oracle_bwd(const double* q, const double* k, const double* v, const double*
             D_odo[r] = dot(dO + (size_t)i * d, o + (size_t)r * d, d);
             double* dq_i = dq + (size_t)r * d;
             for (int c = 0; c < d; ++c) dq_i[c] = 0.0;
-            for (int j = 0; j < nk; ++j) {
+            for (int j = 0; j < N; ++j) {
+                if (!visible(&vis, i, j)) continue;
                 const double ds = p[j] * (dp[j] - Dp);
                 for (int c = 0; c < d; ++c) dq_i[c] += ds * K[(size_t)j * d + c];
             }
@@ -182,8 +233,9 @@ void oracle_bwd(const double* q, const double* k, const double* v, const double*
         double* dk_j = dk + (size_t)r * d;
         double* dv_j = dv + (size_t)r * d;
         for (int c = 0; c < d; ++c) { dk_j[c] = 0.0; dv_j[c] = 0.0; }
-        const int i0 = causal ? j : 0;   /* queries that may attend to key j */
-        for (int i = i0; i < N; ++i) {
+        const Visibility vis = head_visibility(causal, mask, nb, bs, mask_stride, bh);
+        for (int i = 0; i < N; ++i) {
+            if (!visible(&vis, i, j)) continue;   /* query i does not attend to key j */
             const double pij = exp(scale * dot(Q + (size_t)i * d, K + (size_t)j * d, d) - lse_h[i]);
             const double dpij = dot(dO + (size_t)i * d, V + (size_t)j * d, d);
             const double ds = pij * (dpij - D_h[i]);
@@ -194,4 +246,12 @@ void oracle_bwd(const double* q, const double* k, const double* v, const double*
         }
         for (int c = 0; c < d; ++c) dk_j[c] *= scale;
     }
+}
+
+void oracle_bwd(const double* q, const double* k, const double* v, const double* dout,
+                int B, int H, int N, int d, double scale, int causal,
+                double* o, double* lse, double* dq, double* dk, double* dv,
+                double* D_pdp, double* D_odo)
+{
+    oracle_bwd_masked(q, k, v, dout, B, H, N, d, scale, causal, NULL, 0, 1, 0, o, lse, dq, dk, dv, D_pdp, D_odo);
 }

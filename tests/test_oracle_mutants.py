@@ -20,10 +20,10 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 MUTANTS = [
     ("fwd_scale_dropped", "p[j] = scale * dot(Q + (size_t)i * d, K + (size_t)j * d, d);",
      "p[j] = dot(Q + (size_t)i * d, K + (size_t)j * d, d);"),
-    ("causal_ignored", "return causal ? i + 1 : N;", "return N;"),
-    ("causal_off_by_one", "return causal ? i + 1 : N;", "return causal ? (i + 2 < N ? i + 2 : N) : N;"),
+    ("causal_ignored", "if (vis->causal && j > i) return 0;", "if (0) return 0;"),
+    ("causal_off_by_one", "if (vis->causal && j > i) return 0;", "if (vis->causal && j > i + 1) return 0;"),
     ("lse_max_dropped", "*lse_i = m + log(l);", "*lse_i = log(l);"),
-    ("normalisation_dropped", "for (int j = 0; j < nk; ++j) p[j] /= l;", ""),
+    ("normalisation_dropped", "for (int j = 0; j < N; ++j) if (visible(vis, i, j)) p[j] /= l;", ""),
     ("o_uses_k", "o_i[c] += p[j] * V[(size_t)j * d + c];", "o_i[c] += p[j] * K[(size_t)j * d + c];"),
     ("score_transposed_pass2",
      "exp(scale * dot(Q + (size_t)i * d, K + (size_t)j * d, d) - lse_h[i]);",
@@ -37,7 +37,17 @@ MUTANTS = [
     ("dk_uses_dO", "dk_j[c] += ds * Q[(size_t)i * d + c];", "dk_j[c] += ds * dO[(size_t)i * d + c];"),
     ("dk_scale_dropped", "for (int c = 0; c < d; ++c) dk_j[c] *= scale;", ""),
     ("dv_uses_q", "dv_j[c] += pij * dO[(size_t)i * d + c];", "dv_j[c] += pij * Q[(size_t)i * d + c];"),
-    ("column_causal_off_by_one", "const int i0 = causal ? j : 0;", "const int i0 = causal ? j + 1 : 0;"),
+    ("column_visibility_transposed", "if (!visible(&vis, i, j)) continue;   /*",
+     "if (!visible(&vis, j, i)) continue;   /*"),
+    # block-sparse attention
+    ("block_index_transposed", "vis->blocks[(size_t)(i / vis->bs) * vis->nb + j / vis->bs]",
+     "vis->blocks[(size_t)(j / vis->bs) * vis->nb + i / vis->bs]"),
+    ("block_edge_off_by_one", "vis->nb + j / vis->bs] != 0",
+     "vis->nb + (j > 0 ? j - 1 : 0) / vis->bs] != 0"),
+    ("empty_row_lse_zero", "*lse_i = -INFINITY;", "*lse_i = 0.0;"),
+    ("column_pass_ignores_blocks", "if (!visible(&vis, i, j)) continue;   /*",
+     "if (vis.causal && j > i) continue;   /*"),
+    ("head_stride_ignored", "v.blocks = mask ? mask + mask_stride * bh : NULL;", "v.blocks = mask;"),
     ("dS_uses_pass1_D_minus", "const double ds = pij * (dpij - D_h[i]);", "const double ds = pij * dpij;"),
 ]
 

@@ -288,3 +288,152 @@ def test_backward_causal_first_key_row():
     ratio = r["dv"][:, :, -1] / do[:, :, -1]
     np.testing.assert_allclose(ratio, ratio[..., :1] * np.ones_like(ratio), rtol=1e-13)
     assert np.all((ratio > 0) & (ratio <= 1))
+
+
+# ---------------------------------------------------------------- block-sparse attention
+# The michaelc-yu summary of Dao et al. names a block-sparse extension of the method
+# without defining it. Reading taken: the same attention with more pairs masked; pair
+# (i, j) is kept iff the block mask entry [i // block, j // block] is nonzero (and
+# j <= i when causal); a row with no kept pair has O = 0, lse = -inf and no gradient.
+
+def element_mask(bm, N, block, causal):
+    """[N, N] boolean mask of kept pairs, expanded from a block mask by brute force."""
+    keep = np.zeros((N, N), dtype=bool)
+    for i in range(N):
+        for j in range(N):
+            keep[i, j] = bm[i // block, j // block] != 0 and (not causal or j <= i)
+    return keep
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_full_block_mask_is_dense_attention(causal):
+    """Every block kept: exactly the dense oracle, forward and backward, bit for bit."""
+    q, k, v = qkv(31, 2, 2, 19, 8)
+    do = rnd(31, 3, q.shape)
+    nb = 5
+    r = oracle.bwd(q, k, v, do, 0.4, causal, block_mask=np.ones((nb, nb)), block=4)
+    ref = oracle.bwd(q, k, v, do, 0.4, causal)
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        np.testing.assert_array_equal(r[name], ref[name])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_diagonal_mask_is_attention_per_block(causal):
+    """Only diagonal blocks kept: each block of rows attends within itself, so the
+    result equals dense attention run on each block on its own."""
+    block, N = 5, 17
+    q, k, v = qkv(32, 1, 2, N, 6)
+    do = rnd(32, 3, q.shape)
+    nb = (N + block - 1) // block
+    r = oracle.bwd(q, k, v, do, 0.6, causal, block_mask=np.eye(nb), block=block)
+    for b0 in range(0, N, block):
+        sl = slice(b0, min(N, b0 + block))
+        ref = oracle.bwd(q[:, :, sl], k[:, :, sl], v[:, :, sl], do[:, :, sl], 0.6, causal)
+        for name in ("o", "lse", "dq", "dk", "dv"):
+            np.testing.assert_allclose(r[name][:, :, sl], ref[name], rtol=1e-13, atol=1e-13)
+
+
+MASK_A = np.array([[1, 0, 1, 0], [1, 1, 0, 0], [0, 1, 1, 1], [1, 0, 0, 1]], dtype=np.uint8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_mask_matches_torch_cpu_fp64(causal):
+    """torch's CPU float64 attention with the expanded boolean mask, and autograd
+    (independent implementation; the mask keeps at least one key in every row)."""
+    torch = pytest.importorskip("torch")
+    block, N, d, scale = 4, 15, 8, 0.35
+    q, k, v = qkv(33, 2, 2, N, d)
+    do = rnd(33, 3, q.shape)
+    keep = element_mask(MASK_A, N, block, causal)
+    assert keep.any(axis=1).all()
+    r = oracle.bwd(q, k, v, do, scale, causal, block_mask=MASK_A, block=block)
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.tensor(keep), scale=scale)
+    to.backward(torch.tensor(do))
+    np.testing.assert_allclose(r["o"], to.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(r["dq"], tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(r["dk"], tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(r["dv"], tv.grad.numpy(), atol=1e-12)
+    s = scale * torch.tensor(q) @ torch.tensor(k).transpose(-1, -2)
+    s = s.masked_fill(~torch.tensor(keep), float("-inf"))
+    np.testing.assert_allclose(r["lse"], torch.logsumexp(s, -1).numpy(), atol=1e-12)
+
+
+def test_block_mask_backward_matches_finite_differences():
+    """Central differences of L = sum(dO * O) under a block mask (step 1e-5)."""
+    block, N, d, scale, h = 3, 8, 3, 0.8, 1e-5
+    bm = np.array([[1, 0, 1], [0, 1, 0], [1, 1, 0]], dtype=np.uint8)
+    q, k, v = qkv(34, 1, 1, N, d)
+    do = rnd(34, 3, q.shape)
+    r = oracle.bwd(q, k, v, do, scale, False, block_mask=bm, block=block)
+
+    def loss(q_, k_, v_):
+        return float(np.sum(do * oracle.fwd(q_, k_, v_, scale, False, block_mask=bm, block=block)[0]))
+
+    for name, x, g in (("q", q, r["dq"]), ("k", k, r["dk"]), ("v", v, r["dv"])):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        err = np.linalg.norm(fd - g) / np.linalg.norm(g)
+        assert err <= 1e-7, f"d{name}: relative error {err}"
+
+
+def test_masked_out_keys_do_not_matter():
+    """Changing keys and values of a dropped block leaves the rows that drop it bitwise
+    unchanged, and changes a row that keeps it."""
+    block, N = 4, 16
+    q, k, v = qkv(35, 1, 1, N, 5)
+    o, lse = oracle.fwd(q, k, v, 0.5, False, block_mask=MASK_A, block=block)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, 4:8] += 3.0    # key block 1: dropped by query blocks 0 and 2
+    v2[:, :, 4:8] -= 2.0
+    o2, lse2 = oracle.fwd(q, k2, v2, 0.5, False, block_mask=MASK_A, block=block)
+    for qb in range(4):
+        rows = slice(4 * qb, 4 * qb + 4)
+        if MASK_A[qb, 1]:
+            assert np.abs(o2[:, :, rows] - o[:, :, rows]).max() > 1e-3
+        else:
+            np.testing.assert_array_equal(o2[:, :, rows], o[:, :, rows])
+            np.testing.assert_array_equal(lse2[:, :, rows], lse[:, :, rows])
+
+
+def test_rows_without_keys():
+    """A query block whose mask row keeps nothing (or, causal, only later blocks):
+    O = 0, lse = -inf, dQ = 0, and its dO does not reach dK or dV."""
+    block, N = 4, 12
+    bm = np.array([[1, 0, 0], [0, 0, 1], [1, 1, 1]], dtype=np.uint8)  # causal: row block 1 keeps nothing
+    q, k, v = qkv(36, 1, 2, N, 4)
+    do = rnd(36, 3, q.shape)
+    r = oracle.bwd(q, k, v, do, 0.5, True, block_mask=bm, block=block)
+    rows = slice(4, 8)
+    assert np.all(np.isneginf(r["lse"][:, :, rows]))
+    np.testing.assert_array_equal(r["o"][:, :, rows], 0.0)
+    np.testing.assert_array_equal(r["dq"][:, :, rows], 0.0)
+    do2 = do.copy()
+    do2[:, :, rows] = 7.0
+    r2 = oracle.bwd(q, k, v, do2, 0.5, True, block_mask=bm, block=block)
+    np.testing.assert_array_equal(r2["dk"], r["dk"])
+    np.testing.assert_array_equal(r2["dv"], r["dv"])
+    assert np.all(np.isfinite(r["lse"][:, :, :4])) and np.all(np.isfinite(r["lse"][:, :, 8:]))
+
+
+def test_per_head_masks():
+    """A [B, H, nb, nb] mask applies head by head: each head equals a run with that
+    head's mask shared."""
+    block, N = 4, 10
+    B, H = 2, 2
+    q, k, v = qkv(37, B, H, N, 4)
+    nb = 3
+    bms = np.stack([np.stack([np.roll(np.eye(nb), s, axis=1) + np.eye(nb) for s in range(b * H, b * H + H)])
+                    for b in range(B)]).clip(0, 1)
+    o, lse = oracle.fwd(q, k, v, 0.5, False, block_mask=bms, block=block)
+    for b in range(B):
+        for h in range(H):
+            o1, l1 = oracle.fwd(q, k, v, 0.5, False, block_mask=bms[b, h], block=block)
+            np.testing.assert_array_equal(o[b, h], o1[b, h])
+            np.testing.assert_array_equal(lse[b, h], l1[b, h])
