@@ -32,12 +32,17 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA, published
 PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector, published
+SPARSE_BLOCK = 128         # block size of block-sparse attention (fa.h FA_SPARSE_BLOCK)
 
 WORKLOADS = {
     "gpt2_small_causal": dict(B=8, H=12, N=1024, d=64, causal=True, dtype="bf16", seed=1003, mul=1.0),
     "bert_large": dict(B=8, H=16, N=512, d=64, causal=False, dtype="bf16", seed=1002, mul=1.0),
     "long_causal_16k": dict(B=1, H=16, N=16384, d=64, causal=True, dtype="bf16", seed=1004, mul=1.0),
     "tiny_fp32": dict(B=1, H=1, N=128, d=64, causal=False, dtype="fp32", seed=1001, mul=1.0),
+    # block-sparse attention: one seeded mask of 128 x 128 blocks shared by every head,
+    # each block kept with probability 1/4, the diagonal always kept
+    "blocksparse_16k": dict(B=1, H=16, N=16384, d=64, causal=False, dtype="bf16", seed=1006, mul=1.0,
+                            sparse=dict(density=0.25, mask_seed=1006)),
 }
 
 # kernel names as rocprofv3 reports them, per stage of the default strategy
@@ -51,16 +56,16 @@ KERNEL_SOURCES = {"fwd": ("fa_fwd.hip", "fa_device.h"), "prep": ("fa_bwd.hip", "
 # KiB per dispatch, in runs of their own), for the default dQ strategy, with the
 # sha256 (first 16 hex digits) of the kernel's sources when they were taken.
 # Each counter is scaled by what it reads for a plain 256 MiB device-to-device
-# copy in the same runs (the runtime's copy kernel: FETCH_SIZE 131,092 KiB and
+# copy in the same runs (the runtime's copy kernel: FETCH_SIZE 131,089 KiB and
 # WRITE_SIZE 262,144 KiB for 262,144 KiB each way). The summaries and the
 # commands are in profiles/.
 COPY_PROBE_KIB = 262144
 COUNTERS = {
     # workload: {stage: (FETCH_SIZE KiB, WRITE_SIZE KiB, copy FETCH_SIZE KiB, copy WRITE_SIZE KiB, sources sha)}
     "gpt2_small_causal": {
-        "fwd": (18535.8, 12672.0, 131092.5, 262144.0, "a78f81a51783dda4"),
-        "prep": (12493.3, 768.0, 131092.5, 262144.0, "2ffc48677a793cae"),
-        "main": (64158.5, 36864.0, 131092.5, 262144.0, "2ffc48677a793cae"),
+        "fwd": (18536.3, 12672.0, 131089.1, 262144.0, "523496d11c4bb23a"),
+        "prep": (12493.3, 768.0, 131089.1, 262144.0, "cbc3cdc1c4827d5b"),
+        "main": (64237.4, 36864.0, 131089.1, 262144.0, "cbc3cdc1c4827d5b"),
     },
 }
 
@@ -92,10 +97,45 @@ def algorithmic_bytes(w, stage):
     return {"fwd": 3 * t + t + r, "prep": 2 * t + r + 2 * r, "main": 4 * t + 2 * r + 3 * t}[stage]
 
 
+def block_mask(w):
+    """The workload's seeded block mask ([nb, nb] uint8, shared by every head), or None."""
+    sp = w.get("sparse")
+    if sp is None:
+        return None
+    import numpy as np
+    import seedgen
+    nb = (w["N"] + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    m = seedgen.block_mask(sp["mask_seed"], seedgen.TENSOR_MASK, (nb, nb), sp["density"])
+    m[np.arange(nb), np.arange(nb)] = 1
+    return m
+
+
+def kept_pairs(N, mask, causal):
+    """Query-key pairs one head keeps under a block mask (exact count)."""
+    import numpy as np
+    nb = mask.shape[0]
+    total = 0
+    for bi in range(nb):
+        r0, r1 = bi * SPARSE_BLOCK, min(N, (bi + 1) * SPARSE_BLOCK)
+        for bj in np.nonzero(mask[bi])[0].tolist():
+            c0, c1 = bj * SPARSE_BLOCK, min(N, (bj + 1) * SPARSE_BLOCK)
+            if not causal:
+                total += (r1 - r0) * (c1 - c0)
+            else:
+                i = np.arange(r0, r1)
+                total += int(np.clip(np.minimum(c1, i + 1) - c0, 0, None).sum())
+    return total
+
+
+def pairs_per_head(w):
+    """Score pairs credited per head: N^2 (halved for causal), or the kept pairs of a block mask."""
+    return w["pairs"] if "pairs" in w else w["N"] ** 2 * (0.5 if w["causal"] else 1.0)
+
+
 def flops(w, which):
-    base = w["B"] * w["H"] * w["N"] ** 2 * w["d"]
+    base = w["B"] * w["H"] * w["d"] * pairs_per_head(w)
     mult = {"fwd": 4, "bwd": 10, "step": 10, "step_alg": 14}[which]
-    return mult * base * (0.5 if w["causal"] else 1.0)
+    return mult * base
 
 
 def score_entries(N):
@@ -135,24 +175,25 @@ def cpu_baseline(w, shape, scale, causal, min_seconds=10.0):
     B, H, N, d = shape
     heads = B * H
     drawn = [seedgen.draw(w["seed"], t, shape, w["dtype"], mul=w["mul"]).f64.reshape(heads, N, d) for t in range(4)]
+    mask = block_mask(w)
     # time one head first to size the sample
     one = [x[:1].reshape(1, 1, N, d) for x in drawn]
     t0 = time.perf_counter()
-    oracle.bwd(*one, scale, causal)
+    oracle.bwd(*one, scale, causal, block_mask=mask, block=SPARSE_BLOCK)
     t_head = max(time.perf_counter() - t0, 1e-6)
     nh = max(1, min(heads, int(min_seconds / t_head)))
     sample = [x[:nh].reshape(1, nh, N, d) for x in drawn]
     reps, t_total = 0, 0.0
     while t_total < min_seconds and reps < 1000:
         t0 = time.perf_counter()
-        oracle.bwd(*sample, scale, causal)
+        oracle.bwd(*sample, scale, causal, block_mask=mask, block=SPARSE_BLOCK)
         t_total += time.perf_counter() - t0
         reps += 1
     credited = flops(dict(w, B=1, H=nh), "step") * reps
     return {"value": round(credited / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{reps} fwd+bwd pass(es) of the fp64 oracle over {nh} of {heads} (batch, head) pairs "
-                      f"of the same workload, {t_total:.2f} s; credited with the 10*N^2*d rule"}
+                      f"of the same workload, {t_total:.2f} s; credited with the same rule as the GPU"}
 
 
 def main():
@@ -181,8 +222,12 @@ def main():
     import io_aware_tiled_07_amd as fa
     import seedgen
 
-    w = WORKLOADS[args.workload]
+    w = dict(WORKLOADS[args.workload])
+    mask_np = block_mask(w)
+    sparse = mask_np is not None
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    if sparse:
+        w["pairs"] = kept_pairs(N, mask_np, w["causal"])
     shape = (B, H, N, d)
     scale = 1.0 / math.sqrt(d)
     causal = w["causal"]
@@ -197,14 +242,26 @@ def main():
     strategy = {"default": fa.FA_DQ_DEFAULT, "atomic": fa.FA_DQ_ATOMIC, "separate": fa.FA_DQ_SEPARATE}[args.dq]
     stream = torch.cuda.current_stream()
 
-    stages = ("fwd", "prep", "main")
+    if sparse:
+        # block-sparse: each stage is one entry point (mask packing + forward;
+        # mask packing + prep + fused backward)
+        stages = ("fwd", "main")
+        mask_dev = torch.from_numpy(mask_np).to(dev)
+        ws_f = torch.empty(fa.fa_fwd_sparse_workspace_size(B, H, N, 0), dtype=torch.uint8, device=dev)
+        ws_b = torch.empty(fa.fa_bwd_sparse_workspace_size(B, H, N, 0), dtype=torch.uint8, device=dev)
+    else:
+        stages = ("fwd", "prep", "main")
 
     def run(evs=None):
         """One step; evs maps a stage name to the (start, end) events recorded around it."""
         evs = evs or {}
         for name in stages:
             if name in evs: evs[name][0].record(stream)
-            if name == "fwd":
+            if sparse and name == "fwd":
+                fa.fa_fwd_sparse(q, k, v, o, lse, mask_dev, causal, scale, ws_f, stream)
+            elif sparse:
+                fa.fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, mask_dev, causal, scale, ws_b, stream)
+            elif name == "fwd":
                 fa.fa_fwd(q, k, v, o, lse, causal, scale, stream)
             elif name == "prep":
                 fa.fa_bwd_prep(o, do, lse, ws, strategy, stream)
@@ -246,7 +303,7 @@ def main():
 
     tf_step = flops(w, "step") / (ms_step * 1e-3) / 1e12
     tf_fwd = flops(w, "fwd") / (stage_ms["fwd"] * 1e-3) / 1e12
-    bwd_ms = stage_ms["prep"] + stage_ms["main"]
+    bwd_ms = stage_ms.get("prep", 0.0) + stage_ms["main"]
     tf_bwd = flops(w, "bwd") / (bwd_ms * 1e-3) / 1e12
     fp32 = w["dtype"] == "fp32"
     peak = PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
@@ -264,6 +321,13 @@ def main():
         "flop_per_launch": dom_flop, "avg_launch_ms": round(dom_ms, 5),
         "flop_rule": "fwd 4*B*H*N^2*d, bwd 10*B*H*N^2*d (five products), halved for causal",
     }
+    if sparse:
+        roofline.update({
+            "traffic": None, "algorithmic_bytes": None,
+            "kernel": ("fa_bwd_sparse: mask packing + bwd_prep_kernel + bwd_fused_kernel (sparse)" if dom == "main"
+                       else "fa_fwd_sparse: mask packing + fwd_kernel (sparse)"),
+            "flop_rule": "fwd 4*B*H*d, bwd 10*B*H*d, per query-key pair kept by the block mask",
+        })
 
     cold = None
     if args.flush_mall:
@@ -296,16 +360,21 @@ def main():
 
     cfg = {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "causal": causal, "dtype": w["dtype"],
            "scale": scale, "dq_strategy": args.dq}
+    if sparse:
+        cfg.update({"block": SPARSE_BLOCK, "density": w["sparse"]["density"], "mask_seed": w["sparse"]["mask_seed"],
+                    "kept_blocks": int(mask_np.sum()), "blocks": int(mask_np.size),
+                    "kept_pairs_per_head": w["pairs"]})
     out = {
-        "metric": "attention TFLOP/s fwd+bwd (10*B*H*N^2*d, halved for causal)",
+        "metric": ("attention TFLOP/s fwd+bwd (10*B*H*d per kept query-key pair)" if sparse else
+                   "attention TFLOP/s fwd+bwd (10*B*H*N^2*d, halved for causal)"),
         "value": round(tf_step, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w["dtype"], "data": "synthetic: seeded i.i.d. N(0,1) inputs of the workload's shape",
         "config": cfg,
         "stage_breakdown": "per-stage means from a separate pass with events around every launch",
         "fwd": {"ms": round(stage_ms["fwd"], 5), "tflops": round(tf_fwd, 3), "frac_peak": round(tf_fwd / peak, 4)},
-        "bwd": {"ms": round(bwd_ms, 5), "prep_ms": round(stage_ms["prep"], 5), "main_ms": round(stage_ms["main"], 5),
-                "tflops_10x": round(tf_bwd, 3)},
+        "bwd": {"ms": round(bwd_ms, 5), "prep_ms": round(stage_ms.get("prep", 0.0), 5),
+                "main_ms": round(stage_ms["main"], 5), "tflops_10x": round(tf_bwd, 3)},
         "fwd_bwd": {"tflops_10x": round(tf_step, 3), "frac_peak": round(tf_step / peak, 4),
                     "tflops_14x_algorithmic": round(flops(w, "step_alg") / (ms_step * 1e-3) / 1e12, 3)},
         "io_fwd": {"flash_bytes": io_bytes(w)[0], "standard_bytes": io_bytes(w)[1],

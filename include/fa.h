@@ -130,6 +130,44 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* o, cons
                 int B, int H, int N, int d, float scale, int causal, int dtype, int dq_strategy,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Block-sparse attention (the block-sparse extension of the method that the
+ * michaelc-yu summary of Dao et al. names in its abstract without defining it;
+ * reading: exact attention with whole blocks of the score matrix dropped).
+ * The score matrix of a head is cut into FA_SPARSE_BLOCK x FA_SPARSE_BLOCK
+ * blocks, nb = ceil(N / FA_SPARSE_BLOCK) per side. block_mask holds, per
+ * mask, nb x nb bytes in row-major order (row = query block, column = key
+ * block): a nonzero byte keeps the block, zero drops it (its pairs are masked
+ * like the causal upper triangle, and its tiles are never loaded or computed).
+ * Causal masking applies on top. A query row that keeps no key gets O = 0,
+ * lse = -inf, and no gradient.
+ *   block_mask        : device memory, read only; head (b, h) uses the mask that
+ *                       starts mask_head_stride * (b * H + h) bytes in.
+ *   mask_head_stride  : 0 (one mask for every head) or >= nb * nb.
+ *   workspace         : caller-owned device memory, 256-byte aligned, at least
+ *                       fa_fwd_sparse_workspace_size() / fa_bwd_sparse_workspace_size()
+ *                       bytes; its contents on entry do not matter.
+ * bf16/fp16 only (FA_FP32 -> FA_ERR_UNSUPPORTED), d in {64, 128}. Other arguments,
+ * errors and semantics as fa_fwd / fa_bwd (overlaps with the mask or the
+ * workspace -> FA_ERR_INVALID_ARG; mask_head_stride invalid or mask NULL ->
+ * FA_ERR_INVALID_ARG). Returns a fa_status.
+ */
+#define FA_SPARSE_BLOCK 128
+
+size_t fa_fwd_sparse_workspace_size(int B, int H, int N, long long mask_head_stride);
+size_t fa_bwd_sparse_workspace_size(int B, int H, int N, long long mask_head_stride);
+
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int N, int d, float scale, int causal, int dtype,
+                  const void* block_mask, long long mask_head_stride,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv,
+                  int B, int H, int N, int d, float scale, int causal, int dtype,
+                  const void* block_mask, long long mask_head_stride,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a fa_status value. Never NULL. */
 const char* fa_status_string(int status);
 

@@ -6,8 +6,10 @@ the current stream. There is no fallback: if ``libfa.so`` is missing or a call
 fails, an exception is raised.
 
 The raw entry points keep the C names (``fa_fwd``, ``fa_bwd``, ``fa_bwd_dq``,
-``fa_bwd_prep``, ``fa_bwd_main``, ``fa_bwd_workspace_size``, ``fa_status_string``)
-and take caller-allocated torch tensors; ``fwd`` and ``bwd`` allocate their outputs.
+``fa_bwd_prep``, ``fa_bwd_main``, ``fa_bwd_workspace_size``, ``fa_status_string``,
+and for block-sparse attention ``fa_fwd_sparse``, ``fa_bwd_sparse`` and their
+workspace sizes) and take caller-allocated torch tensors; ``fwd``, ``bwd``,
+``fwd_sparse`` and ``bwd_sparse`` allocate their outputs.
 """
 from __future__ import annotations
 
@@ -20,17 +22,20 @@ __all__ = [
     "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_DQ_DEFAULT", "FA_DQ_ATOMIC", "FA_DQ_SEPARATE",
     "FaError", "library_path", "load", "fa_status_string", "fa_bwd_workspace_size",
     "fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_prep", "fa_bwd_main", "fwd", "bwd", "dtype_code",
+    "FA_SPARSE_BLOCK", "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size", "fa_fwd_sparse",
+    "fa_bwd_sparse", "fwd_sparse", "bwd_sparse",
 ]
 
 FA_BF16, FA_FP16, FA_FP32 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
 FA_DQ_DEFAULT, FA_DQ_ATOMIC, FA_DQ_SEPARATE = 0, 1, 2
+FA_SPARSE_BLOCK = 128
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfa.so")
 _lib = None
 
-_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_vp, _i, _f, _sz, _ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_longlong
 
 
 class FaError(RuntimeError):
@@ -66,6 +71,13 @@ def load():
         lib.fa_bwd_main.restype = _i
         lib.fa_bwd_prep.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]
         lib.fa_bwd_prep.restype = _i
+        for name in ("fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size"):
+            getattr(lib, name).argtypes = [_i, _i, _i, _ll]
+            getattr(lib, name).restype = _sz
+        lib.fa_fwd_sparse.argtypes = [_vp] * 5 + [_i, _i, _i, _i, _f, _i, _i, _vp, _ll, _vp, _sz, _vp]
+        lib.fa_fwd_sparse.restype = _i
+        lib.fa_bwd_sparse.argtypes = [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _i, _vp, _ll, _vp, _sz, _vp]
+        lib.fa_bwd_sparse.restype = _i
         _lib = lib
     return _lib
 
@@ -201,4 +213,89 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale=None, dq_strategy: int 
     import torch
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     fa_bwd_dq(q, k, v, o, do, lse, dq, dk, dv, causal, scale, dq_strategy, workspace, stream)
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------- block-sparse attention
+
+def fa_fwd_sparse_workspace_size(B: int, H: int, N: int, mask_head_stride: int) -> int:
+    return int(load().fa_fwd_sparse_workspace_size(B, H, N, mask_head_stride))
+
+
+def fa_bwd_sparse_workspace_size(B: int, H: int, N: int, mask_head_stride: int) -> int:
+    return int(load().fa_bwd_sparse_workspace_size(B, H, N, mask_head_stride))
+
+
+def _mask_args(block_mask, B, H, N):
+    """(pointer, per-head stride in bytes) of a uint8 device block mask that is
+    [nb, nb] (one mask for every head) or [B, H, nb, nb]."""
+    import torch
+    nb = (N + FA_SPARSE_BLOCK - 1) // FA_SPARSE_BLOCK
+    _check_bhnd("block_mask", block_mask, dtype=torch.uint8)
+    if tuple(block_mask.shape) == (nb, nb):
+        return block_mask.data_ptr(), 0
+    if tuple(block_mask.shape) == (B, H, nb, nb):
+        return block_mask.data_ptr(), nb * nb
+    raise ValueError(f"block_mask must be [{nb},{nb}] or [{B},{H},{nb},{nb}], got {tuple(block_mask.shape)}")
+
+
+def _workspace(q, need, workspace):
+    import torch
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_bhnd("workspace", workspace)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def fa_fwd_sparse(q, k, v, o, lse, block_mask, causal: bool = False, scale=None, workspace=None,
+                  stream=None) -> None:
+    """Block-sparse forward into caller-allocated ``o`` and ``lse``: 128 x 128 blocks of the
+    score matrix whose ``block_mask`` byte is zero are skipped (see ``fa_fwd_sparse`` in fa.h)."""
+    import torch
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_bhnd(name, t, q.shape, q.dtype)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    mp, stride = _mask_args(block_mask, B, H, N)
+    workspace, nbytes = _workspace(q, fa_fwd_sparse_workspace_size(B, H, N, stride), workspace)
+    st = load().fa_fwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                              B, H, N, d, _scale(scale, d), int(bool(causal)), dtype_code(q), mp, stride,
+                              workspace.data_ptr(), nbytes, _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_sparse")
+
+
+def fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, block_mask, causal: bool = False, scale=None,
+                  workspace=None, stream=None) -> None:
+    """Block-sparse backward into caller-allocated ``dq``, ``dk``, ``dv``."""
+    import torch
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_bhnd(name, t, q.shape, q.dtype)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    mp, stride = _mask_args(block_mask, B, H, N)
+    workspace, nbytes = _workspace(q, fa_bwd_sparse_workspace_size(B, H, N, stride), workspace)
+    st = load().fa_bwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                              lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                              _scale(scale, d), int(bool(causal)), dtype_code(q), mp, stride,
+                              workspace.data_ptr(), nbytes, _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_sparse")
+
+
+def fwd_sparse(q, k, v, block_mask, causal: bool = False, scale=None, stream=None):
+    """Allocate O and lse and run the block-sparse forward. Returns (o, lse)."""
+    import torch
+    B, H, N, _ = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd_sparse(q, k, v, o, lse, block_mask, causal, scale, None, stream)
+    return o, lse
+
+
+def bwd_sparse(q, k, v, o, do, lse, block_mask, causal: bool = False, scale=None, stream=None):
+    """Allocate dQ, dK, dV and run the block-sparse backward. Returns (dq, dk, dv)."""
+    import torch
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, block_mask, causal, scale, None, stream)
     return dq, dk, dv

@@ -98,6 +98,54 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
     return FA_OK;
 }
 
+// ---------------------------------------------------------------- block-sparse attention
+constexpr int kSparseBlock = 128;
+
+// Workspace of the block-sparse entry points: (backward only) -D and
+// lse * log2(e) as in the dense backward, then the packed mask bit rows and
+// bit columns ([nm][nb][W] words each); each part 256-byte aligned.
+struct SparseLayout {
+    size_t delta, lse2, rows, cols, bytes;
+    int nb, W, nm;
+    int64_t head_words;
+};
+SparseLayout sparse_layout(int B, int H, int N, long long head_stride, bool backward) {
+    const size_t nrows = (size_t)B * H * N;
+    SparseLayout s;
+    s.nb = (N + kSparseBlock - 1) / kSparseBlock;
+    s.W = (s.nb + 63) / 64;
+    s.nm = head_stride == 0 ? 1 : B * H;
+    s.head_words = head_stride == 0 ? 0 : (int64_t)s.nb * s.W;
+    size_t off = 0;
+    s.delta = s.lse2 = 0;
+    if (backward) {
+        s.lse2 = round_up(nrows * sizeof(float), 256);
+        off = s.lse2 + round_up(nrows * sizeof(float), 256);
+    }
+    const size_t bits = round_up((size_t)s.nm * s.nb * s.W * sizeof(uint64_t), 256);
+    s.rows = off;
+    s.cols = off + bits;
+    s.bytes = off + 2 * bits;
+    return s;
+}
+
+// Byte range of the caller's block mask(s).
+Range mask_range(const void* mask, int B, int H, int N, long long head_stride) {
+    const long long nb = (N + kSparseBlock - 1) / kSparseBlock;
+    const long long nm = head_stride == 0 ? 1 : (long long)B * H;
+    return range(mask, (size_t)((nm - 1) * head_stride + nb * nb));
+}
+
+// Checks shared by the block-sparse entry points (after check_common).
+int check_sparse(int dtype, const void* mask, int N, long long head_stride, const void* workspace,
+                 size_t workspace_bytes, size_t need) {
+    if (dtype == FA_FP32) return FA_ERR_UNSUPPORTED;
+    const long long nb = (N + kSparseBlock - 1) / kSparseBlock;
+    if (mask == nullptr || head_stride < 0 || (head_stride != 0 && head_stride < nb * nb)) return FA_ERR_INVALID_ARG;
+    if (workspace == nullptr || !aligned256(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -221,6 +269,97 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* workspace, size_t workspace_bytes, void* stream) {
     return fa_bwd_dq(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, FA_DQ_DEFAULT,
                      workspace, workspace_bytes, stream);
+}
+
+size_t fa_fwd_sparse_workspace_size(int B, int H, int N, long long mask_head_stride) {
+    if (B < 1 || H < 1 || N < 1 || mask_head_stride < 0) return 0;
+    return sparse_layout(B, H, N, mask_head_stride, false).bytes;
+}
+
+size_t fa_bwd_sparse_workspace_size(int B, int H, int N, long long mask_head_stride) {
+    if (B < 1 || H < 1 || N < 1 || mask_head_stride < 0) return 0;
+    return sparse_layout(B, H, N, mask_head_stride, true).bytes;
+}
+
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                  float scale, int causal, int dtype, const void* block_mask, long long mask_head_stride,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_common(B, H, N, d, scale, causal, dtype);
+    if (st != FA_OK) return st;
+    const void* ptrs[] = {q, k, v, o, lse};
+    for (const void* p : ptrs)
+        if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
+    const SparseLayout L = sparse_layout(B, H, N, mask_head_stride, false);
+    st = check_sparse(dtype, block_mask, N, mask_head_stride, workspace, workspace_bytes, L.bytes);
+    if (st != FA_OK) return st;
+    const size_t tbytes = (size_t)B * H * N * d * elt_bytes(dtype);
+    const size_t lbytes = (size_t)B * H * N * sizeof(float);
+    const Range outs[] = {range(o, tbytes), range(lse, lbytes), range(workspace, L.bytes)};
+    const Range ins[] = {range(q, tbytes), range(k, tbytes), range(v, tbytes),
+                         mask_range(block_mask, B, H, N, mask_head_stride)};
+    for (int i = 0; i < 3; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return FA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* base = static_cast<char*>(workspace);
+    uint64_t* rows = reinterpret_cast<uint64_t*>(base + L.rows);
+    uint64_t* cols = reinterpret_cast<uint64_t*>(base + L.cols);
+    (void)hipGetLastError();
+    hipError_t e = fa::sparse_mask_bits(static_cast<const uint8_t*>(block_mask), mask_head_stride, L.nm, L.nb, rows,
+                                        cols, s);
+    if (e == hipSuccess)
+        e = fa::fwd_sparse(q, k, v, o, lse, B, H, N, d, scale, causal != 0, dtype, rows, L.W, L.head_words, s);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype,
+                  const void* block_mask, long long mask_head_stride, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    int st = check_common(B, H, N, d, scale, causal, dtype);
+    if (st != FA_OK) return st;
+    const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+    for (const void* p : ptrs)
+        if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
+    const SparseLayout L = sparse_layout(B, H, N, mask_head_stride, true);
+    st = check_sparse(dtype, block_mask, N, mask_head_stride, workspace, workspace_bytes, L.bytes);
+    if (st != FA_OK) return st;
+    const size_t tbytes = (size_t)B * H * N * d * elt_bytes(dtype);
+    const size_t lbytes = (size_t)B * H * N * sizeof(float);
+    const Range outs[] = {range(dq, tbytes), range(dk, tbytes), range(dv, tbytes), range(workspace, L.bytes)};
+    const Range ins[] = {range(q, tbytes),    range(k, tbytes),     range(v, tbytes),
+                         range(o, tbytes),    range(dout, tbytes), range(lse, lbytes),
+                         mask_range(block_mask, B, H, N, mask_head_stride)};
+    for (int i = 0; i < 4; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return FA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* base = static_cast<char*>(workspace);
+    float* delta = reinterpret_cast<float*>(base + L.delta);
+    float* lse2 = reinterpret_cast<float*>(base + L.lse2);
+    uint64_t* rows = reinterpret_cast<uint64_t*>(base + L.rows);
+    uint64_t* cols = reinterpret_cast<uint64_t*>(base + L.cols);
+    (void)hipGetLastError();
+    hipError_t e = fa::sparse_mask_bits(static_cast<const uint8_t*>(block_mask), mask_head_stride, L.nm, L.nb, rows,
+                                        cols, s);
+    if (e == hipSuccess) e = fa::bwd_prep(o, dout, lse, B, H, N, d, dtype, delta, lse2, s);
+    if (e == hipSuccess) {
+        if (d == 128)
+            e = fa::bwd128_fused_sparse(q, k, v, dout, delta, lse2, dq, dk, dv, B, H, N, scale, causal != 0, dtype,
+                                        rows, cols, L.W, L.head_words, s);
+        else
+            e = fa::bwd_fused_sparse(q, k, v, dout, delta, lse2, dq, dk, dv, B, H, N, scale, causal != 0, dtype, rows,
+                                     cols, L.W, L.head_words, s);
+    }
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -122,6 +122,12 @@ struct FusedArgs {
     int heads_per_xcd;  // > 0: XCD-aware mapping
     float c;            // scale * log2(e)
     float scale;
+    // block-sparse attention: packed block-mask rows and columns (W words each,
+    // nb per mask); head bh uses the mask at bh * head_words (0: one for all)
+    const uint64_t* mask_rows;
+    const uint64_t* mask_cols;
+    int W, nb;
+    int64_t head_words;
 };
 
 struct PrepArgs {
@@ -194,7 +200,7 @@ __device__ __forceinline__ void map_fused(int bid, const FusedArgs& a, bool caus
 }
 
 // Key workgroup: dK and dV of 128 keys.
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, bool SPARSE>
 __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
@@ -213,7 +219,17 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
 
     const int ng = (N + kKvQRows - 1) / kKvQRows;          // query stages
     const int g0 = CAUSAL ? (kb * kKvKeys) / kKvQRows : 0;  // first stage touching these keys
-    const int nst = ng - g0;
+    // block-sparse: the 64-row halves of the kept query blocks of mask column kb
+    static_assert(!SPARSE || kKvKeys == kSparseBlock, "a key workgroup covers one block column of the mask");
+    BlockWalk walk;
+    int nst;
+    if constexpr (SPARSE) {
+        walk.init(a.mask_cols + (size_t)bh * a.head_words + (size_t)kb * a.W, CAUSAL ? kb : 0, ng);
+        nst = walk.count(CAUSAL ? kb : 0, a.nb - 1);
+    } else {
+        nst = ng - g0;
+    }
+    int slot_unit[kSlots];  // query stage (64 rows) held by each ring slot
 
     // Stage s (query stage g0 + s; rows past the end read as zeros and are
     // masked) in slot s % kSlots: [lse2 x64][D x64][Q rows][dO rows]. Chunk c (1 KiB)
@@ -228,7 +244,9 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         dma_off[j] = (uint32_t)((row * D + c * 8) * 2);
     }
     auto issue = [&](int s, int slot) {
-        const int r0 = (g0 + s) * kKvQRows;
+        const int g = SPARSE ? walk.next() : g0 + s;
+        slot_unit[slot] = g;
+        const int r0 = g * kKvQRows;
         const i32x4 qr = rows_rsrc<kRowB>(Q, N, r0), dr = rows_rsrc<kRowB>(dO, N, r0);
         char* sb = smem + slot * kKvStage + kKvRowsOff + wave * 1024;
 #pragma unroll
@@ -414,7 +432,7 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         else wait_stages<kKvCpw, kSlots - 2>(ahead);
         barrier();
         if (s + kSlots - 1 < nst) issue(s + kSlots - 1, (SLOT + kSlots - 1) % kSlots);
-        const int g = g0 + s;
+        const int g = SPARSE ? slot_unit[SLOT] : g0 + s;
         auto half = [&](auto hh_c) {
             const int qt0 = g * kKvQRows + 32 * decltype(hh_c)::value;
             const bool active = kw0 < N && qt0 < N && (!CAUSAL || qt0 + 31 >= kw0);
@@ -436,7 +454,7 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
 }
 
 // Query workgroup: dQ of 128 queries.
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, bool SPARSE>
 __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
@@ -451,9 +469,19 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
     const int qload = min(qrow, N - 1);
 
     const int nkb_all = (N + kQKeys - 1) / kQKeys;
-    const int nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * kQRows) - 1) / kQKeys + 1) : nkb_all;
+    // block-sparse: the 64-key halves of the kept key blocks of mask row qb
+    static_assert(!SPARSE || kQRows == kSparseBlock, "a query workgroup covers one block row of the mask");
+    BlockWalk walk;
+    int nkb;
+    if constexpr (SPARSE) {
+        walk.init(a.mask_rows + (size_t)bh * a.head_words + (size_t)qb * a.W, 0, nkb_all);
+        nkb = walk.count(0, CAUSAL ? qb : a.nb - 1);
+    } else {
+        nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * kQRows) - 1) / kQKeys + 1) : nkb_all;
+    }
     // blocks this wave computes: 0 .. nkw-1 (causal: up to the one holding its last row)
     const int nkw = !wave_active ? 0 : (CAUSAL ? min(nkb, min(q0 + 31, N - 1) / kQKeys + 1) : nkb);
+    int slot_unit[kSlots];  // key block (64 keys) held by each ring slot
 
     f32x16 dqa[DT];
 #pragma unroll
@@ -471,6 +499,8 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
         dma_off[j] = (uint32_t)((row * D + c * 8) * 2);
     }
     auto issue = [&](int b, int slot) {
+        if constexpr (SPARSE) b = walk.next();
+        slot_unit[slot] = b;
         const int r0 = b * kQKeys;
         const i32x4 kr = rows_rsrc<kRowB>(K, N, r0), vr = rows_rsrc<kRowB>(V, N, r0);
         char* sb = smem + slot * kQStage + wave * 1024;
@@ -631,8 +661,12 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
         wait_stages<kQCpw, kSlots - 2>(min(kSlots - 2, nkb - 1 - kb));
         barrier();
         if (kb + kSlots - 1 < nkb) issue(kb + kSlots - 1, (SLOT + kSlots - 1) % kSlots);
-        if (kb >= nkw) return;
-        const int key0 = kb * kQKeys;
+        const int key0 = (SPARSE ? slot_unit[SLOT] : kb) * kQKeys;
+        if constexpr (SPARSE) {
+            if (!wave_active || (CAUSAL && key0 > q0 + 31)) return;
+        } else {
+            if (kb >= nkw) return;
+        }
         const bool need_mask = (CAUSAL && key0 + kQKeys - 1 > q0) || (key0 + kQKeys > N);
         if (need_mask) block(slot_c, Masked{}, key0);
         else block(slot_c, Unmasked{}, key0);
@@ -644,26 +678,26 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
     }
 }
 
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 2) void bwd_fused_kernel(FusedArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[kSmem];
     int bh, blk;
     bool is_q;
     map_fused(blockIdx.x, a, CAUSAL, bh, is_q, blk);
-    if (is_q) q_body<T, CAUSAL>(a, bh, blk, smem);
-    else kv_body<T, CAUSAL>(a, bh, blk, smem);
+    if (is_q) q_body<T, CAUSAL, SPARSE>(a, bh, blk, smem);
+    else kv_body<T, CAUSAL, SPARSE>(a, bh, blk, smem);
 }
 
-template <typename T>
+template <typename T, bool SPARSE>
 hipError_t launch_fused(FusedArgs a, bool causal, hipStream_t stream) {
     a.nblk = (a.N + kKvKeys - 1) / kKvKeys;
     static_assert(kKvKeys == kQRows, "both kinds of workgroup cover 128 rows");
     a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
     const dim3 grid((unsigned)(a.BH * 2 * a.nblk));
     if (causal)
-        hipLaunchKernelGGL((bwd_fused_kernel<T, true>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((bwd_fused_kernel<T, true, SPARSE>), grid, dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((bwd_fused_kernel<T, false>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((bwd_fused_kernel<T, false, SPARSE>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -713,7 +747,38 @@ hipError_t bwd_fused(const void* q, const void* k, const void* v, const void* do
     a.heads_per_xcd = 0;
     a.c = scale * kLog2e;
     a.scale = scale;
-    return dtype == 0 ? launch_fused<Bf16>(a, causal, stream) : launch_fused<F16>(a, causal, stream);
+    a.mask_rows = a.mask_cols = nullptr;
+    a.W = a.nb = 0;
+    a.head_words = 0;
+    return dtype == 0 ? launch_fused<Bf16, false>(a, causal, stream) : launch_fused<F16, false>(a, causal, stream);
+}
+
+hipError_t bwd_fused_sparse(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                            const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale,
+                            bool causal, int dtype, const uint64_t* mask_rows, const uint64_t* mask_cols, int W,
+                            int64_t head_words, hipStream_t stream) {
+    FusedArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.dout = static_cast<const uint16_t*>(dout);
+    a.lse2 = lse2;
+    a.delta = delta;
+    a.dq = static_cast<uint16_t*>(dq);
+    a.dk = static_cast<uint16_t*>(dk);
+    a.dv = static_cast<uint16_t*>(dv);
+    a.BH = B * H;
+    a.N = N;
+    a.nblk = 0;
+    a.heads_per_xcd = 0;
+    a.c = scale * kLog2e;
+    a.scale = scale;
+    a.mask_rows = mask_rows;
+    a.mask_cols = mask_cols;
+    a.W = W;
+    a.nb = (N + kSparseBlock - 1) / kSparseBlock;
+    a.head_words = head_words;
+    return dtype == 0 ? launch_fused<Bf16, true>(a, causal, stream) : launch_fused<F16, true>(a, causal, stream);
 }
 
 }  // namespace fa

@@ -112,6 +112,12 @@ struct Args {
     int heads_per_xcd;  // > 0: XCD-aware mapping
     float c;            // scale * log2(e)
     float scale;
+    // block-sparse attention: packed block-mask rows and columns (W words each,
+    // nb per mask); head bh uses the mask at bh * head_words (0: one for all)
+    const uint64_t* mask_rows;
+    const uint64_t* mask_cols;
+    int W, nb;
+    int64_t head_words;
 };
 
 // Workgroup -> (head, kind, block): slot s of a head alternates key and query
@@ -144,7 +150,7 @@ __device__ __forceinline__ void stage_offsets(uint32_t (&off)[TC / 4], int wave,
 }
 
 // Key workgroup: dK and dV of 128 keys.
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, bool SPARSE>
 __device__ __forceinline__ void kv_body(const Args& a, int bh, int kb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
@@ -163,13 +169,25 @@ __device__ __forceinline__ void kv_body(const Args& a, int bh, int kb, char* sme
 
     const int ng = (N + kKvQRows - 1) / kKvQRows;
     const int g0 = CAUSAL ? (kb * kKvKeys) / kKvQRows : 0;
-    const int nst = ng - g0;
+    // block-sparse: the 64-row halves of the kept query blocks of mask column kb
+    static_assert(!SPARSE || kKvKeys == kSparseBlock, "a key workgroup covers one block column of the mask");
+    BlockWalk walk;
+    int nst;
+    if constexpr (SPARSE) {
+        walk.init(a.mask_cols + (size_t)bh * a.head_words + (size_t)kb * a.W, CAUSAL ? kb : 0, ng);
+        nst = walk.count(CAUSAL ? kb : 0, a.nb - 1);
+    } else {
+        nst = ng - g0;
+    }
+    int slot_unit[kSlots];  // query stage (64 rows) held by each ring slot
 
     // stage s (query rows (g0 + s) * 64 ..) in slot s % 4: [lse2 x64][-D x64][Q rows][dO rows]
     uint32_t dma_off[kKvTC / 4];
     stage_offsets<kKvTC>(dma_off, wave, lane);
     auto issue = [&](int s, int slot) {
-        const int r0 = (g0 + s) * kKvQRows;
+        const int g = SPARSE ? walk.next() : g0 + s;
+        slot_unit[slot] = g;
+        const int r0 = g * kKvQRows;
         const i32x4 qr = rows_rsrc<kRowB>(Q, N, r0), dr = rows_rsrc<kRowB>(dO, N, r0);
         char* sb = smem + slot * kStage + kKvRowsOff + wave * 1024;
 #pragma unroll
@@ -350,7 +368,7 @@ __device__ __forceinline__ void kv_body(const Args& a, int bh, int kb, char* sme
         barrier();
         if (s + kSlots - 1 < nst) issue(s + kSlots - 1, (SLOT + kSlots - 1) % kSlots);
         const uint32_t sb = slot_base<SLOT>();
-        const int g = g0 + s;
+        const int g = SPARSE ? slot_unit[SLOT] : g0 + s;
         auto half = [&](auto hh_c) {
             const int qt0 = g * kKvQRows + 32 * decltype(hh_c)::value;
             const bool active = kw0 < N && qt0 < N && (!CAUSAL || qt0 + 31 >= kw0);
@@ -371,7 +389,7 @@ __device__ __forceinline__ void kv_body(const Args& a, int bh, int kb, char* sme
 }
 
 // Query workgroup: dQ of 128 queries.
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, bool SPARSE>
 __device__ __forceinline__ void q_body(const Args& a, int bh, int qb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
@@ -386,8 +404,18 @@ __device__ __forceinline__ void q_body(const Args& a, int bh, int qb, char* smem
     const int qload = min(qrow, N - 1);
 
     const int nkb_all = (N + kQKeys - 1) / kQKeys;
-    const int nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * kQRows) - 1) / kQKeys + 1) : nkb_all;
+    // block-sparse: the 64-key halves of the kept key blocks of mask row qb
+    static_assert(!SPARSE || kQRows == kSparseBlock, "a query workgroup covers one block row of the mask");
+    BlockWalk walk;
+    int nkb;
+    if constexpr (SPARSE) {
+        walk.init(a.mask_rows + (size_t)bh * a.head_words + (size_t)qb * a.W, 0, nkb_all);
+        nkb = walk.count(0, CAUSAL ? qb : a.nb - 1);
+    } else {
+        nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * kQRows) - 1) / kQKeys + 1) : nkb_all;
+    }
     const int nkw = !wave_active ? 0 : (CAUSAL ? min(nkb, min(q0 + 31, N - 1) / kQKeys + 1) : nkb);
+    int slot_unit[kSlots];  // key block (64 keys) held by each ring slot
 
     f32x16 dqa[DT];
 #pragma unroll
@@ -397,6 +425,8 @@ __device__ __forceinline__ void q_body(const Args& a, int bh, int qb, char* smem
     uint32_t dma_off[kQTC / 4];
     stage_offsets<kQTC>(dma_off, wave, lane);
     auto issue = [&](int b, int slot) {
+        if constexpr (SPARSE) b = walk.next();
+        slot_unit[slot] = b;
         const int r0 = b * kQKeys;
         const i32x4 kr = rows_rsrc<kRowB>(K, N, r0), vr = rows_rsrc<kRowB>(V, N, r0);
         char* sb = smem + slot * kStage + wave * 1024;
@@ -529,9 +559,13 @@ __device__ __forceinline__ void q_body(const Args& a, int bh, int qb, char* smem
         wait_stages<kQCpw, kSlots - 2>(min(kSlots - 2, nkb - 1 - kb));
         barrier();
         if (kb + kSlots - 1 < nkb) issue(kb + kSlots - 1, (SLOT + kSlots - 1) % kSlots);
-        if (kb >= nkw) return;
+        const int key0 = (SPARSE ? slot_unit[SLOT] : kb) * kQKeys;
+        if constexpr (SPARSE) {
+            if (!wave_active || (CAUSAL && key0 > q0 + 31)) return;
+        } else {
+            if (kb >= nkw) return;
+        }
         const uint32_t sb = slot_base<SLOT>();
-        const int key0 = kb * kQKeys;
         auto one = [&](auto kt_c) {
             const int k0 = key0 + 32 * decltype(kt_c)::value;
             if (k0 >= N || (CAUSAL && k0 > q0 + 31)) return;  // no visible key in this tile
@@ -549,21 +583,34 @@ __device__ __forceinline__ void q_body(const Args& a, int bh, int qb, char* smem
     }
 }
 
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 1) void bwd128_fused_kernel(Args a) {
     __shared__ __attribute__((aligned(1024))) char smem[kSmem];
     int bh, blk;
     bool is_q;
     map_block(blockIdx.x, a, CAUSAL, bh, is_q, blk);
-    if (is_q) q_body<T, CAUSAL>(a, bh, blk, smem);
-    else kv_body<T, CAUSAL>(a, bh, blk, smem);
+    if (is_q) q_body<T, CAUSAL, SPARSE>(a, bh, blk, smem);
+    else kv_body<T, CAUSAL, SPARSE>(a, bh, blk, smem);
 }
 
-}  // namespace
+template <bool SPARSE>
+hipError_t launch(Args a, bool causal, int dtype, hipStream_t stream) {
+    static_assert(kKvKeys == kQRows, "both kinds of workgroup cover 128 rows");
+    a.nblk = (a.N + kKvKeys - 1) / kKvKeys;
+    a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+    const dim3 grid((unsigned)(a.BH * 2 * a.nblk));
+    if (dtype == 0) {
+        if (causal) hipLaunchKernelGGL((bwd128_fused_kernel<Bf16, true, SPARSE>), grid, dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((bwd128_fused_kernel<Bf16, false, SPARSE>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+        if (causal) hipLaunchKernelGGL((bwd128_fused_kernel<F16, true, SPARSE>), grid, dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((bwd128_fused_kernel<F16, false, SPARSE>), grid, dim3(kThreads), 0, stream, a);
+    }
+    return hipGetLastError();
+}
 
-hipError_t bwd128_fused(const void* q, const void* k, const void* v, const void* dout, const float* delta,
-                        const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale, bool causal,
-                        int dtype, hipStream_t stream) {
+Args make_args(const void* q, const void* k, const void* v, const void* dout, const float* delta, const float* lse2,
+               void* dq, void* dk, void* dv, int B, int H, int N, float scale) {
     Args a;
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
@@ -576,20 +623,35 @@ hipError_t bwd128_fused(const void* q, const void* k, const void* v, const void*
     a.dv = static_cast<uint16_t*>(dv);
     a.BH = B * H;
     a.N = N;
-    static_assert(kKvKeys == kQRows, "both kinds of workgroup cover 128 rows");
-    a.nblk = (N + kKvKeys - 1) / kKvKeys;
-    a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+    a.nblk = 0;
+    a.heads_per_xcd = 0;
     a.c = scale * kLog2e;
     a.scale = scale;
-    const dim3 grid((unsigned)(a.BH * 2 * a.nblk));
-    if (dtype == 0) {
-        if (causal) hipLaunchKernelGGL((bwd128_fused_kernel<Bf16, true>), grid, dim3(kThreads), 0, stream, a);
-        else hipLaunchKernelGGL((bwd128_fused_kernel<Bf16, false>), grid, dim3(kThreads), 0, stream, a);
-    } else {
-        if (causal) hipLaunchKernelGGL((bwd128_fused_kernel<F16, true>), grid, dim3(kThreads), 0, stream, a);
-        else hipLaunchKernelGGL((bwd128_fused_kernel<F16, false>), grid, dim3(kThreads), 0, stream, a);
-    }
-    return hipGetLastError();
+    a.mask_rows = a.mask_cols = nullptr;
+    a.W = a.nb = 0;
+    a.head_words = 0;
+    return a;
+}
+
+}  // namespace
+
+hipError_t bwd128_fused(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                        const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale, bool causal,
+                        int dtype, hipStream_t stream) {
+    return launch<false>(make_args(q, k, v, dout, delta, lse2, dq, dk, dv, B, H, N, scale), causal, dtype, stream);
+}
+
+hipError_t bwd128_fused_sparse(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                               const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale,
+                               bool causal, int dtype, const uint64_t* mask_rows, const uint64_t* mask_cols, int W,
+                               int64_t head_words, hipStream_t stream) {
+    Args a = make_args(q, k, v, dout, delta, lse2, dq, dk, dv, B, H, N, scale);
+    a.mask_rows = mask_rows;
+    a.mask_cols = mask_cols;
+    a.W = W;
+    a.nb = (N + kSparseBlock - 1) / kSparseBlock;
+    a.head_words = head_words;
+    return launch<true>(a, causal, dtype, stream);
 }
 
 }  // namespace fa

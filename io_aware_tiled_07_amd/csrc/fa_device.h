@@ -123,6 +123,66 @@ __device__ __forceinline__ void for_ring(int n, F&& body) {
     }
 }
 
+// ---------------------------------------------------------------- block-sparse walk
+// Block-sparse attention keeps or drops whole 128 x 128 blocks of the score
+// matrix. A row (or column) of the block mask arrives packed: bit b of word w
+// stands for block 64 w + b. A walk hands out, in increasing order, the 64-row
+// units (ring stages) of the kept blocks lo .. hi: units 2k and 2k + 1 of
+// block k, the second only if it starts before the end of the sequence
+// (nunits = ceil(N / 64)). All state is wave-uniform (scalar registers); the
+// caller asks for exactly count() units.
+constexpr int kSparseBlock = 128;
+
+// 8-byte load through the scalar cache into SGPRs, waited for at once. (The
+// compiler would use a vector load here whenever an LDS-DMA copy precedes it,
+// since it cannot tell that the copy leaves the mask alone; a vector load's
+// wait would also drain the DMA ring.) No LDS read may be in flight: the wait
+// covers them too.
+__device__ __forceinline__ uint64_t sload64(const uint64_t* p) {
+    uint64_t v;
+    asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+}
+
+struct BlockWalk {
+    const uint64_t* words;
+    uint64_t cur;  // bits of word wi not handed out yet
+    int wi, nunits, pending;
+
+    __device__ __forceinline__ void init(const uint64_t* w, int lo, int nunits_) {
+        words = w;
+        nunits = nunits_;
+        pending = -1;
+        wi = lo >> 6;
+        cur = sload64(words + wi) & (~0ull << (lo & 63));
+    }
+    // units of the kept blocks lo .. hi
+    __device__ __forceinline__ int count(int lo, int hi) const {
+        int c = 0;
+        for (int w = lo >> 6; w <= (hi >> 6); ++w) {
+            uint64_t x = sload64(words + w);
+            if (w == (lo >> 6)) x &= ~0ull << (lo & 63);
+            if (w == (hi >> 6) && (hi & 63) != 63) x &= (2ull << (hi & 63)) - 1;
+            c += 2 * __builtin_popcountll(x);
+        }
+        const int last = (nunits - 1) >> 1;  // block of the last unit; it holds one unit if nunits is odd
+        if ((nunits & 1) && last >= lo && last <= hi && ((sload64(words + (last >> 6)) >> (last & 63)) & 1)) --c;
+        return c;
+    }
+    __device__ __forceinline__ int next() {
+        if (pending >= 0) {
+            const int u = pending;
+            pending = -1;
+            return u;
+        }
+        while (cur == 0) cur = sload64(words + ++wi);
+        const int b = (wi << 6) + __builtin_ctzll(cur);
+        cur &= cur - 1;
+        if (2 * b + 1 < nunits) pending = 2 * b + 1;
+        return 2 * b;
+    }
+};
+
 // buffer_load_dwordx4 ... lds: the same 16-byte-per-lane copy, addressed as
 // a wave-uniform buffer resource plus a per-lane byte offset. A lane whose
 // offset lies at or past the resource's byte count reads zeros, so a block

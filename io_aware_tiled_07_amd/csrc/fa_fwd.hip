@@ -72,6 +72,11 @@ struct FwdArgs {
     int heads_per_xcd;  // > 0: XCD-aware mapping (B*H multiple of 8)
     int cu_rounds;      // > 0: every workgroup is resident at once, cu_rounds per CU (causal only)
     float c;            // scale * log2(e)
+    // block-sparse attention: packed block-mask rows, W words each, nb rows per
+    // mask; head bh uses the mask at bh * head_words (0: one mask for all heads)
+    const uint64_t* mask_rows;
+    int W, nb;
+    int64_t head_words;
 };
 
 constexpr int kCusPerXcd = 32;  // MI350-series: 256 CUs in 8 XCDs
@@ -99,7 +104,7 @@ __device__ __forceinline__ void map_block(int bid, const FwdArgs& a, int& bh, in
     }
 }
 
-template <typename T, int D, bool CAUSAL, int NW>
+template <typename T, int D, bool CAUSAL, int NW, bool SPARSE>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     constexpr int KS = D / 16;           // k-steps of the score MFMA
     constexpr int DT = D / 32;           // 32-wide output tiles
@@ -130,7 +135,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     const bool wave_active = q0 < N;
 
     const int nkb_all = (N + kBc - 1) / kBc;
-    const int nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * BR) - 1) / kBc + 1) : nkb_all;
+    // key blocks this workgroup visits; block-sparse: the 64-key halves of the
+    // kept 128-key blocks of mask row qb (causal: up to the diagonal), in order
+    static_assert(!SPARSE || BR == kSparseBlock, "a workgroup covers one block row of the mask");
+    BlockWalk walk;
+    int nkb;
+    if constexpr (SPARSE) {
+        walk.init(a.mask_rows + (size_t)bh * a.head_words + (size_t)qb * a.W, 0, nkb_all);
+        nkb = walk.count(0, CAUSAL ? qb : a.nb - 1);
+    } else {
+        nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * BR) - 1) / kBc + 1) : nkb_all;
+    }
+    int unit[STAGES];  // key block held by each ring slot
 
     f32x16 oacc[DT];
 #pragma unroll
@@ -151,6 +167,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     }
     auto issue = [&](int kb, auto slot_c) {
         constexpr int SLOT = decltype(slot_c)::value;
+        if constexpr (SPARSE) kb = walk.next();
+        unit[SLOT] = kb;
         const i32x4 kr = rows_rsrc<D * 2>(K, N, kb * kBc);
         const i32x4 vr = rows_rsrc<D * 2>(V, N, kb * kBc);
         char* sb = smem + SLOT * SB + wave * 1024;
@@ -191,7 +209,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
     }
-    issue(0, Int<0>{});
+    if (!SPARSE || nkb > 0) issue(0, Int<0>{});
     if (STAGES == 3 && nkb > 1) {
         issue(1, Int<1>{});
         wait_vmcnt<4 * HALF>();
@@ -214,7 +232,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
         } else {
             if (kb + 1 < nkb) issue(kb + 1, Int<(SLOT + 1) % 2>{});
         }
-        const int key0 = kb * kBc;
+        const int key0 = (SPARSE ? unit[SLOT] : kb) * kBc;
         if (!wave_active || (CAUSAL && key0 > q0 + 31)) return;
 
         // ---- S^T (64 keys x 32 queries): two 32x32 tiles. All K operand reads
@@ -333,8 +351,16 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     const int qrow = q0 + l32;
     if (wave_active) {
         char* stage = smem + (nkb % STAGES) * SB + wave * (2048 * DT);
-        store_rows<T, DT>(oacc, 1.f / l_tot, a.o + head + (size_t)q0 * D, D, N - q0, stage);
-        if (h == 0 && qrow < N) a.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+        if constexpr (SPARSE) {
+            // a block row that keeps no key: O = 0 and lse = -inf
+            const bool any = l_tot > 0.f;
+            store_rows<T, DT>(oacc, any ? 1.f / l_tot : 0.f, a.o + head + (size_t)q0 * D, D, N - q0, stage);
+            if (h == 0 && qrow < N)
+                a.lse[(size_t)bh * N + qrow] = any ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        } else {
+            store_rows<T, DT>(oacc, 1.f / l_tot, a.o + head + (size_t)q0 * D, D, N - q0, stage);
+            if (h == 0 && qrow < N) a.lse[(size_t)bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+        }
     }
 }
 
@@ -344,7 +370,7 @@ struct FwdShape {  // waves per workgroup and query rows per workgroup
     static constexpr int BR = 32 * NW;
 };
 
-template <typename T, int D, bool C>
+template <typename T, int D, bool C, bool SPARSE>
 hipError_t launch(FwdArgs a, hipStream_t stream) {
     using S = FwdShape<D>;
     a.nqb = (a.N + S::BR - 1) / S::BR;
@@ -352,16 +378,17 @@ hipError_t launch(FwdArgs a, hipStream_t stream) {
     // resident workgroups per CU: 3 at head dim 64, 2 at 128 (registers and LDS)
     constexpr int kResident = D == 64 ? 3 : 2;
     const int per_xcd = a.heads_per_xcd * a.nqb;
-    a.cu_rounds = (C && a.heads_per_xcd > 0 && per_xcd % kCusPerXcd == 0 && per_xcd <= kResident * kCusPerXcd)
+    a.cu_rounds = (C && !SPARSE && a.heads_per_xcd > 0 && per_xcd % kCusPerXcd == 0 &&
+                   per_xcd <= kResident * kCusPerXcd)
                       ? per_xcd / kCusPerXcd : 0;
-    hipLaunchKernelGGL((fwd_kernel<T, D, C, S::NW>), dim3(a.BH * a.nqb), dim3(64 * S::NW), 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<T, D, C, S::NW, SPARSE>), dim3(a.BH * a.nqb), dim3(64 * S::NW), 0, stream, a);
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool SPARSE>
 hipError_t dispatch_d(const FwdArgs& a, int d, bool causal, hipStream_t s) {
-    if (d == 64) return causal ? launch<T, 64, true>(a, s) : launch<T, 64, false>(a, s);
-    return causal ? launch<T, 128, true>(a, s) : launch<T, 128, false>(a, s);
+    if (d == 64) return causal ? launch<T, 64, true, SPARSE>(a, s) : launch<T, 64, false, SPARSE>(a, s);
+    return causal ? launch<T, 128, true, SPARSE>(a, s) : launch<T, 128, false, SPARSE>(a, s);
 }
 
 }  // namespace
@@ -380,7 +407,32 @@ hipError_t fwd_mfma(const void* q, const void* k, const void* v, void* o, float*
     a.heads_per_xcd = 0;
     a.cu_rounds = 0;
     a.c = scale * kLog2e;
-    return dtype == 0 ? dispatch_d<Bf16>(a, d, causal, stream) : dispatch_d<F16>(a, d, causal, stream);
+    a.mask_rows = nullptr;
+    a.W = a.nb = 0;
+    a.head_words = 0;
+    return dtype == 0 ? dispatch_d<Bf16, false>(a, d, causal, stream) : dispatch_d<F16, false>(a, d, causal, stream);
+}
+
+hipError_t fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                      float scale, bool causal, int dtype, const uint64_t* mask_rows, int W, int64_t head_words,
+                      hipStream_t stream) {
+    FwdArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse;
+    a.BH = B * H;
+    a.N = N;
+    a.nqb = 0;
+    a.heads_per_xcd = 0;
+    a.cu_rounds = 0;
+    a.c = scale * kLog2e;
+    a.mask_rows = mask_rows;
+    a.W = W;
+    a.nb = (N + kSparseBlock - 1) / kSparseBlock;
+    a.head_words = head_words;
+    return dtype == 0 ? dispatch_d<Bf16, true>(a, d, causal, stream) : dispatch_d<F16, true>(a, d, causal, stream);
 }
 
 }  // namespace fa

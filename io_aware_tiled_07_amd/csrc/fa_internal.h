@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -31,6 +32,25 @@ hipError_t bwd_atomic_prep(const void* o, const void* dout, int B, int H, int N,
 hipError_t bwd_atomic_main(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                            void* dq, void* dk, void* dv, int B, int H, int N, float scale, bool causal, int dtype,
                            const float* delta, float* dq_acc, hipStream_t stream);
+
+// Block-sparse attention (128 x 128 blocks): the byte mask ([nm][nb][nb],
+// mask m at m * head_stride bytes) packed into bit rows and bit columns
+// ([nm][nb][W] words each, W = ceil(nb / 64)); then the forward and the fused
+// backward that walk them (head bh reads mask bh * head_words words in; 0 = one
+// mask for all heads).
+hipError_t sparse_mask_bits(const uint8_t* mask, int64_t head_stride, int nm, int nb, uint64_t* rows, uint64_t* cols,
+                            hipStream_t stream);
+hipError_t fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                      float scale, bool causal, int dtype, const uint64_t* mask_rows, int W, int64_t head_words,
+                      hipStream_t stream);
+hipError_t bwd_fused_sparse(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                            const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale,
+                            bool causal, int dtype, const uint64_t* mask_rows, const uint64_t* mask_cols, int W,
+                            int64_t head_words, hipStream_t stream);
+hipError_t bwd128_fused_sparse(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                               const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale,
+                               bool causal, int dtype, const uint64_t* mask_rows, const uint64_t* mask_cols, int W,
+                               int64_t head_words, hipStream_t stream);
 
 // fp32 forward and backward, d = 64.
 hipError_t fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,

@@ -163,3 +163,14 @@ def choice_rows(seed: int, tensor_id: int, n: int, count: int) -> np.ndarray:
                 if len(picked) == count:
                     break
     return np.array(sorted(picked), dtype=np.int64)
+
+
+TENSOR_MASK = 8
+
+
+def block_mask(seed: int, tensor_id: int, shape, density: float) -> np.ndarray:
+    """uint8 array of ``shape`` whose entries are 1 with probability ``density``
+    (independently, from the seeded stream) and 0 otherwise: a block mask for
+    block-sparse attention."""
+    n = int(np.prod(shape))
+    return (uniform01(seed, tensor_id, n) < density).astype(np.uint8).reshape(shape)

@@ -36,7 +36,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_prep", "fa_bwd_main",
-                          "fa_bwd_workspace_size", "fa_status_string"}
+                          "fa_bwd_workspace_size", "fa_status_string", "fa_fwd_sparse", "fa_bwd_sparse",
+                          "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -205,3 +206,72 @@ def test_library_never_allocates():
     forbidden = sorted(s for s in imported if re.match(r"hip(Ext)?(Malloc|Free|HostMalloc|HostFree|MallocAsync|"
                                                         r"FreeAsync|MallocManaged|HostAlloc|MemAlloc)", s))
     assert forbidden == []
+
+
+# ---------------------------------------------------------------- block-sparse entry points
+
+def test_sparse_workspace_sizes(lib):
+    def up(x):
+        return (x + 255) // 256 * 256
+    nb, W = 128, 2  # N = 16384: 128 blocks per side, two 64-bit words per mask row
+    assert fa.fa_fwd_sparse_workspace_size(1, 16, 16384, 0) == 2 * up(nb * W * 8)
+    assert fa.fa_fwd_sparse_workspace_size(1, 16, 16384, nb * nb) == 2 * up(16 * nb * W * 8)
+    rows = 2 * 3 * 1000
+    assert fa.fa_bwd_sparse_workspace_size(2, 3, 1000, 0) == 2 * up(rows * 4) + 2 * up(8 * 8)
+    assert fa.fa_fwd_sparse_workspace_size(0, 1, 10, 0) == 0
+    assert fa.fa_bwd_sparse_workspace_size(1, 1, 10, -1) == 0
+
+
+def sparse_fwd(lib, B=2, H=3, N=1000, d=64, dtype=0, mask=None, stride=0, ws=None, ws_bytes=None, **over):
+    names = ["q", "k", "v", "o", "lse"]
+    p = dict(zip(names, ptrs(5)))
+    p.update({k: v for k, v in over.items() if k in names})
+    mask = A + 6 * GAP if mask is None else mask
+    need = fa.fa_fwd_sparse_workspace_size(B, H, N, max(stride, 0))
+    ws = A + 7 * GAP if ws is None else ws
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return lib.fa_fwd_sparse(*[ctypes.c_void_p(p[n]) for n in names], B, H, N, d, ctypes.c_float(0.125), 0, dtype,
+                             ctypes.c_void_p(mask), stride, ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+def sparse_bwd(lib, B=2, H=3, N=1000, d=64, dtype=0, mask=None, stride=0, ws=None, ws_bytes=None, **over):
+    names = ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"]
+    p = dict(zip(names, ptrs(9)))
+    p.update({k: v for k, v in over.items() if k in names})
+    mask = A + 10 * GAP if mask is None else mask
+    need = fa.fa_bwd_sparse_workspace_size(B, H, N, max(stride, 0))
+    ws = A + 11 * GAP if ws is None else ws
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return lib.fa_bwd_sparse(*[ctypes.c_void_p(p[n]) for n in names], B, H, N, d, ctypes.c_float(0.125), 0, dtype,
+                             ctypes.c_void_p(mask), stride, ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+SPARSE_REJECTS = [
+    (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),   # 16-bit only
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(mask=0), fa.FA_ERR_INVALID_ARG),             # no mask
+    (dict(stride=5), fa.FA_ERR_INVALID_ARG),           # per-head masks would overlap (nb * nb = 64)
+    (dict(stride=-64), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=0), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=64), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 12 * GAP + 64), fa.FA_ERR_WORKSPACE),  # not 256-byte aligned
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,code", SPARSE_REJECTS + [
+    (dict(o=A), fa.FA_ERR_INVALID_ARG),                # o aliases q
+    (dict(ws=A + 6 * GAP), fa.FA_ERR_INVALID_ARG),     # workspace overlaps the mask
+    (dict(o=A + 6 * GAP), fa.FA_ERR_INVALID_ARG),      # o overlaps the mask
+])
+def test_fwd_sparse_rejects(lib, kw, code):
+    assert sparse_fwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", SPARSE_REJECTS + [
+    (dict(dk=A), fa.FA_ERR_INVALID_ARG),               # dk aliases q
+    (dict(ws=A + 10 * GAP), fa.FA_ERR_INVALID_ARG),    # workspace overlaps the mask
+    (dict(dq=A + 10 * GAP), fa.FA_ERR_INVALID_ARG),    # dq overlaps the mask
+])
+def test_bwd_sparse_rejects(lib, kw, code):
+    assert sparse_bwd(lib, **kw) == code

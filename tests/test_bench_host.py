@@ -55,3 +55,21 @@ def test_traffic_is_calibrated_and_goes_stale(monkeypatch):
     monkeypatch.setattr(bench, "sources_sha", lambda stage: "changed")
     assert bench.traffic_bytes("toy", "main") is None
     assert bench.traffic_bytes("toy", "fwd") is None
+
+
+def test_kept_pairs_by_brute_force():
+    """The block-sparse FLOP credit counts exactly the kept (query, key) pairs."""
+    import numpy as np
+    rng = np.random.default_rng(3)
+    for N, causal in ((300, False), (300, True), (129, True), (1, False)):
+        nb = (N + 127) // 128
+        m = (rng.random((nb, nb)) < 0.5).astype(np.uint8)
+        i, j = np.meshgrid(np.arange(N), np.arange(N), indexing="ij")
+        keep = m[i // 128, j // 128] != 0
+        if causal:
+            keep &= j <= i
+        assert bench.kept_pairs(N, m, causal) == int(keep.sum())
+    w = dict(bench.WORKLOADS["gpt2_small_causal"])
+    assert bench.pairs_per_head(w) == 1024 * 1024 / 2
+    w["pairs"] = 1234
+    assert bench.flops(w, "fwd") == 4 * 8 * 12 * 64 * 1234

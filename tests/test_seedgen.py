@@ -67,3 +67,13 @@ def test_choice_rows():
     r = seedgen.choice_rows(1005, 16, 65536, 32)
     assert r.size == 32 and len(set(r.tolist())) == 32 and r.min() >= 0 and r.max() < 65536
     np.testing.assert_array_equal(r, seedgen.choice_rows(1005, 16, 65536, 32))
+
+
+def test_block_mask_is_seeded_and_has_its_density():
+    a = seedgen.block_mask(5, seedgen.TENSOR_MASK, (64, 64), 0.3)
+    b = seedgen.block_mask(5, seedgen.TENSOR_MASK, (64, 64), 0.3)
+    c = seedgen.block_mask(6, seedgen.TENSOR_MASK, (64, 64), 0.3)
+    assert a.dtype == np.uint8 and a.shape == (64, 64)
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+    assert set(np.unique(a).tolist()) <= {0, 1}
+    assert abs(a.mean() - 0.3) < 0.03
