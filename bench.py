@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA, published
 PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector, published
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA (published 5.0 PFLOP/s: twice the bf16 rate)
 SPARSE_BLOCK = 128         # block size of block-sparse attention (fa.h FA_SPARSE_BLOCK)
 
 WORKLOADS = {
@@ -43,6 +44,9 @@ WORKLOADS = {
     # each block kept with probability 1/4, the diagonal always kept
     "blocksparse_16k": dict(B=1, H=16, N=16384, d=64, causal=False, dtype="bf16", seed=1006, mul=1.0,
                             sparse=dict(density=0.25, mask_seed=1006)),
+    # FP8 (e4m3) forward only, descale factors 1: the long causal shape
+    "fp8_fwd_long_causal_16k": dict(B=1, H=16, N=16384, d=64, causal=True, dtype="fp8e4m3", seed=1007, mul=1.0,
+                                    fwd_only=True),
 }
 
 # kernel names as rocprofv3 reports them, per stage of the default strategy
@@ -149,8 +153,9 @@ def io_bytes(w):
     reading them for the softmax, writing the probabilities and reading them for PV),
     both at the workload's element size, scores and probabilities at that size too."""
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
-    elt = 4 if w["dtype"] == "fp32" else 2
-    fa_b = B * H * (4 * N * d * elt + 4 * N)
+    elt = {"fp32": 4, "fp8e4m3": 1}.get(w["dtype"], 2)
+    out_elt = 2 if w["dtype"] == "fp8e4m3" else elt  # the fp8 forward writes O in bf16
+    fa_b = B * H * (3 * N * d * elt + N * d * out_elt + 4 * N)
     std_b = B * H * (4 * N * d + 4 * score_entries(N)) * elt
     return fa_b, std_b
 
@@ -167,32 +172,42 @@ def cpu_model():
 
 
 def cpu_baseline(w, shape, scale, causal, min_seconds=10.0):
-    """The fp64 oracle (as it stands) on the host cores: whole fwd+bwd passes over the
-    same seeded inputs, repeated until at least ``min_seconds`` have elapsed, or over a
-    subset of (batch, head) pairs when one pass would take longer than that."""
+    """The fp64 oracle (as it stands) on the host cores: whole fwd+bwd passes (forward
+    passes for a forward-only workload) over the same seeded inputs, repeated until at
+    least ``min_seconds`` have elapsed, or over a subset of (batch, head) pairs when one
+    pass would take longer than that."""
     import oracle
     import seedgen
     B, H, N, d = shape
     heads = B * H
     drawn = [seedgen.draw(w["seed"], t, shape, w["dtype"], mul=w["mul"]).f64.reshape(heads, N, d) for t in range(4)]
     mask = block_mask(w)
+    fwd_only = w.get("fwd_only", False)
+
+    def one_pass(xs):
+        if fwd_only:
+            oracle.fwd(*xs[:3], scale, causal)
+        else:
+            oracle.bwd(*xs, scale, causal, block_mask=mask, block=SPARSE_BLOCK)
+
     # time one head first to size the sample
     one = [x[:1].reshape(1, 1, N, d) for x in drawn]
     t0 = time.perf_counter()
-    oracle.bwd(*one, scale, causal, block_mask=mask, block=SPARSE_BLOCK)
+    one_pass(one)
     t_head = max(time.perf_counter() - t0, 1e-6)
     nh = max(1, min(heads, int(min_seconds / t_head)))
     sample = [x[:nh].reshape(1, nh, N, d) for x in drawn]
     reps, t_total = 0, 0.0
     while t_total < min_seconds and reps < 1000:
         t0 = time.perf_counter()
-        oracle.bwd(*sample, scale, causal, block_mask=mask, block=SPARSE_BLOCK)
+        one_pass(sample)
         t_total += time.perf_counter() - t0
         reps += 1
-    credited = flops(dict(w, B=1, H=nh), "step") * reps
+    credited = flops(dict(w, B=1, H=nh), "fwd" if fwd_only else "step") * reps
+    kind = "forward" if fwd_only else "fwd+bwd"
     return {"value": round(credited / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "cpu_model": cpu_model(),
-            "sample": f"{reps} fwd+bwd pass(es) of the fp64 oracle over {nh} of {heads} (batch, head) pairs "
+            "sample": f"{reps} {kind} pass(es) of the fp64 oracle over {nh} of {heads} (batch, head) pairs "
                       f"of the same workload, {t_total:.2f} s; credited with the same rule as the GPU"}
 
 
@@ -234,15 +249,20 @@ def main():
     dev = "cuda"
     drawn = [seedgen.draw(w["seed"], t, shape, w["dtype"], mul=w["mul"], want_f64=False) for t in range(4)]
     q, k, v, do = (x.torch(dev) for x in drawn)
-    o = torch.empty_like(q)
+    fp8 = w["dtype"] == "fp8e4m3"
+    fwd_only = w.get("fwd_only", False)
+    o = torch.empty(shape, dtype=torch.bfloat16, device=dev) if fp8 else torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    code = fa.dtype_code(q)
-    ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d, code), dtype=torch.uint8, device=dev)
+    if not fwd_only:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        code = fa.dtype_code(q)
+        ws = torch.empty(fa.fa_bwd_workspace_size(B, H, N, d, code), dtype=torch.uint8, device=dev)
     strategy = {"default": fa.FA_DQ_DEFAULT, "atomic": fa.FA_DQ_ATOMIC, "separate": fa.FA_DQ_SEPARATE}[args.dq]
     stream = torch.cuda.current_stream()
 
-    if sparse:
+    if fwd_only:
+        stages = ("fwd",)
+    elif sparse:
         # block-sparse: each stage is one entry point (mask packing + forward;
         # mask packing + prep + fused backward)
         stages = ("fwd", "main")
@@ -257,7 +277,9 @@ def main():
         evs = evs or {}
         for name in stages:
             if name in evs: evs[name][0].record(stream)
-            if sparse and name == "fwd":
+            if fp8:
+                fa.fa_fwd_fp8(q, k, v, o, lse, causal, scale, 1.0, 1.0, 1.0, stream)
+            elif sparse and name == "fwd":
                 fa.fa_fwd_sparse(q, k, v, o, lse, mask_dev, causal, scale, ws_f, stream)
             elif sparse:
                 fa.fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, mask_dev, causal, scale, ws_b, stream)
@@ -284,7 +306,7 @@ def main():
         run(brk[i])
     torch.cuda.synchronize()
     stage_ms = {name: statistics.mean(e[name][0].elapsed_time(e[name][1]) for e in brk) for name in stages}
-    dom = "main" if stage_ms["main"] >= stage_ms["fwd"] else "fwd"
+    dom = "main" if "main" in stage_ms and stage_ms["main"] >= stage_ms["fwd"] else "fwd"
 
     # Timed region: K whole steps; only the dominant kernel's launches carry
     # events, which give its average launch duration for the roofline entry.
@@ -301,12 +323,13 @@ def main():
     ms_step = t_start.elapsed_time(t_end) / K
     dom_ms = statistics.mean(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev)
 
-    tf_step = flops(w, "step") / (ms_step * 1e-3) / 1e12
+    step_rule = "fwd" if fwd_only else "step"
+    tf_step = flops(w, step_rule) / (ms_step * 1e-3) / 1e12
     tf_fwd = flops(w, "fwd") / (stage_ms["fwd"] * 1e-3) / 1e12
-    bwd_ms = stage_ms.get("prep", 0.0) + stage_ms["main"]
-    tf_bwd = flops(w, "bwd") / (bwd_ms * 1e-3) / 1e12
+    bwd_ms = stage_ms.get("prep", 0.0) + stage_ms.get("main", 0.0)
+    tf_bwd = flops(w, "bwd") / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else None
     fp32 = w["dtype"] == "fp32"
-    peak = PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+    peak = PEAK_FP32_TFLOPS if fp32 else PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
 
     # roofline of the dominant kernel: algorithmic FLOP per launch / its average duration
     dom_flop = flops(w, "bwd") if dom == "main" else flops(w, "fwd")
@@ -321,6 +344,9 @@ def main():
         "flop_per_launch": dom_flop, "avg_launch_ms": round(dom_ms, 5),
         "flop_rule": "fwd 4*B*H*N^2*d, bwd 10*B*H*N^2*d (five products), halved for causal",
     }
+    if fp8:
+        roofline.update({"traffic": None, "algorithmic_bytes": None, "kernel": "fwd_fp8_kernel",
+                         "flop_rule": "fwd 4*B*H*N^2*d, halved for causal; peak: dense fp8 MFMA"})
     if sparse:
         roofline.update({
             "traffic": None, "algorithmic_bytes": None,
@@ -344,7 +370,7 @@ def main():
         del scratch
         cms = statistics.median(cold_ms)
         cold = {"ms_per_step_median": round(cms, 5), "ms_min": round(min(cold_ms), 5), "ms_max": round(max(cold_ms), 5),
-                "tflops_10x": round(flops(w, "step") / (cms * 1e-3) / 1e12, 3),
+                "tflops": round(flops(w, step_rule) / (cms * 1e-3) / 1e12, 3),
                 "note": "each step after a 512 MiB scratch write; events around each step"}
 
     if args.copy_probe_mib > 0:
@@ -366,6 +392,7 @@ def main():
                     "kept_pairs_per_head": w["pairs"]})
     out = {
         "metric": ("attention TFLOP/s fwd+bwd (10*B*H*d per kept query-key pair)" if sparse else
+                   "attention TFLOP/s fwd, fp8 inputs (4*B*H*N^2*d, halved for causal)" if fp8 else
                    "attention TFLOP/s fwd+bwd (10*B*H*N^2*d, halved for causal)"),
         "value": round(tf_step, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -373,10 +400,11 @@ def main():
         "config": cfg,
         "stage_breakdown": "per-stage means from a separate pass with events around every launch",
         "fwd": {"ms": round(stage_ms["fwd"], 5), "tflops": round(tf_fwd, 3), "frac_peak": round(tf_fwd / peak, 4)},
-        "bwd": {"ms": round(bwd_ms, 5), "prep_ms": round(stage_ms.get("prep", 0.0), 5),
-                "main_ms": round(stage_ms["main"], 5), "tflops_10x": round(tf_bwd, 3)},
-        "fwd_bwd": {"tflops_10x": round(tf_step, 3), "frac_peak": round(tf_step / peak, 4),
-                    "tflops_14x_algorithmic": round(flops(w, "step_alg") / (ms_step * 1e-3) / 1e12, 3)},
+        "bwd": None if fwd_only else {"ms": round(bwd_ms, 5), "prep_ms": round(stage_ms.get("prep", 0.0), 5),
+                                      "main_ms": round(stage_ms["main"], 5), "tflops_10x": round(tf_bwd, 3)},
+        "fwd_bwd": None if fwd_only else {
+            "tflops_10x": round(tf_step, 3), "frac_peak": round(tf_step / peak, 4),
+            "tflops_14x_algorithmic": round(flops(w, "step_alg") / (ms_step * 1e-3) / 1e12, 3)},
         "io_fwd": {"flash_bytes": io_bytes(w)[0], "standard_bytes": io_bytes(w)[1],
                    "standard_over_flash": round(io_bytes(w)[1] / io_bytes(w)[0], 2)},
         "roofline": roofline, "cpu_baseline": cpu, "wall_s_timed": round(wall, 4),

@@ -168,6 +168,23 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, co
                   const void* block_mask, long long mask_head_stride,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * FP8 forward (the lower-precision continuation of the method that the
+ * groundtruth.day page names in its lineage paragraph without defining it;
+ * reading: the same attention on e4m3 inputs, the softmax in fp32, the weights
+ * rounded to e4m3 for the P V product).
+ *   q, k, v : [B,H,N,d] OCP e4m3 bytes (1 byte per element), device memory.
+ *   *_descale: positive finite fp32 factors; the real inputs are byte value x descale.
+ *   o       : [B,H,N,d] bf16 output; lse: [B,H,N] fp32 (natural log of the scaled scores,
+ *             as fa_fwd writes it).
+ * d in {64, 128}; any N >= 1; causal 0/1; scale as fa_fwd. Rounding the weights to
+ * 3 mantissa bits costs about 2 % relative RMS on O for Gaussian inputs. Errors as
+ * fa_fwd (non-positive or non-finite descale -> FA_ERR_INVALID_ARG). Returns a fa_status.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               float q_descale, float k_descale, float v_descale, void* stream);
+
 /* Static, human-readable name of a fa_status value. Never NULL. */
 const char* fa_status_string(int status);
 

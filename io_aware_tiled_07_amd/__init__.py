@@ -7,9 +7,10 @@ fails, an exception is raised.
 
 The raw entry points keep the C names (``fa_fwd``, ``fa_bwd``, ``fa_bwd_dq``,
 ``fa_bwd_prep``, ``fa_bwd_main``, ``fa_bwd_workspace_size``, ``fa_status_string``,
-and for block-sparse attention ``fa_fwd_sparse``, ``fa_bwd_sparse`` and their
-workspace sizes) and take caller-allocated torch tensors; ``fwd``, ``bwd``,
-``fwd_sparse`` and ``bwd_sparse`` allocate their outputs.
+for block-sparse attention ``fa_fwd_sparse``, ``fa_bwd_sparse`` and their
+workspace sizes, and the FP8 forward ``fa_fwd_fp8``) and take caller-allocated
+torch tensors; ``fwd``, ``bwd``, ``fwd_sparse``, ``bwd_sparse`` and ``fwd_fp8``
+allocate their outputs.
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ __all__ = [
     "FaError", "library_path", "load", "fa_status_string", "fa_bwd_workspace_size",
     "fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_prep", "fa_bwd_main", "fwd", "bwd", "dtype_code",
     "FA_SPARSE_BLOCK", "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size", "fa_fwd_sparse",
-    "fa_bwd_sparse", "fwd_sparse", "bwd_sparse",
+    "fa_bwd_sparse", "fwd_sparse", "bwd_sparse", "fa_fwd_fp8", "fwd_fp8",
 ]
 
 FA_BF16, FA_FP16, FA_FP32 = 0, 1, 2
@@ -78,6 +79,8 @@ def load():
         lib.fa_fwd_sparse.restype = _i
         lib.fa_bwd_sparse.argtypes = [_vp] * 9 + [_i, _i, _i, _i, _f, _i, _i, _vp, _ll, _vp, _sz, _vp]
         lib.fa_bwd_sparse.restype = _i
+        lib.fa_fwd_fp8.argtypes = [_vp] * 5 + [_i, _i, _i, _i, _f, _i, _f, _f, _f, _vp]
+        lib.fa_fwd_fp8.restype = _i
         _lib = lib
     return _lib
 
@@ -299,3 +302,37 @@ def bwd_sparse(q, k, v, o, do, lse, block_mask, causal: bool = False, scale=None
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, block_mask, causal, scale, None, stream)
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------- FP8 forward
+
+def fa_fwd_fp8(q, k, v, o, lse, causal: bool = False, scale=None, q_descale: float = 1.0,
+               k_descale: float = 1.0, v_descale: float = 1.0, stream=None) -> None:
+    """FP8 forward into caller-allocated ``o`` ([B,H,N,d] bfloat16) and ``lse``: q, k, v
+    hold e4m3 bytes (torch uint8 or float8_e4m3fn), real value = byte value x descale."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,N,d]")
+    B, H, N, d = q.shape
+    if q.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"q must hold e4m3 bytes, got {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bhnd(name, t, q.shape, q.dtype)
+    _check_bhnd("o", o, q.shape, torch.bfloat16)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32)
+    st = load().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                           _scale(scale, d), int(bool(causal)), float(q_descale), float(k_descale),
+                           float(v_descale), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
+
+
+def fwd_fp8(q, k, v, causal: bool = False, scale=None, q_descale: float = 1.0, k_descale: float = 1.0,
+            v_descale: float = 1.0, stream=None):
+    """Allocate O (bfloat16) and lse and run the FP8 forward. Returns (o, lse)."""
+    import torch
+    B, H, N, d = q.shape
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd_fp8(q, k, v, o, lse, causal, scale, q_descale, k_descale, v_descale, stream)
+    return o, lse

@@ -362,4 +362,26 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, co
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, float q_descale, float k_descale, float v_descale, void* stream) {
+    int st = check_common(B, H, N, d, scale, causal, FA_BF16);
+    if (st != FA_OK) return st;
+    const float ds[] = {q_descale, k_descale, v_descale};
+    for (float x : ds)
+        if (!(x > 0.f) || !isfinite(x)) return FA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, o, lse};
+    for (const void* p : ptrs)
+        if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
+    const size_t n = (size_t)B * H * N * d;
+    const Range ro = range(o, 2 * n), rl = range(lse, (size_t)B * H * N * sizeof(float));
+    const Range ins[] = {range(q, n), range(k, n), range(v, n)};
+    for (const Range& r : ins)
+        if (overlap(ro, r) || overlap(rl, r)) return FA_ERR_INVALID_ARG;
+    if (overlap(ro, rl)) return FA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    const hipError_t e = fa::fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, causal != 0, q_descale, k_descale,
+                                     v_descale, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // extern "C"

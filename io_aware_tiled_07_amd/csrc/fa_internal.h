@@ -52,6 +52,11 @@ hipError_t bwd128_fused_sparse(const void* q, const void* k, const void* v, cons
                                bool causal, int dtype, const uint64_t* mask_rows, const uint64_t* mask_cols, int W,
                                int64_t head_words, hipStream_t stream);
 
+// FP8 (e4m3) forward, d in {64, 128}: O in bf16, lse in fp32; the descale
+// factors turn the stored bytes into the real values.
+hipError_t fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, bool causal, float q_descale, float k_descale, float v_descale, hipStream_t stream);
+
 // fp32 forward and backward, d = 64.
 hipError_t fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                    int N, float scale, bool causal, hipStream_t stream);

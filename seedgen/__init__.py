@@ -92,6 +92,40 @@ def round_f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
+def _e4m3_positive_values() -> np.ndarray:
+    """Values of the e4m3 (OCP, 'fn') codes 0x00 .. 0x7E, increasing: 3 mantissa
+    bits, exponent bias 7, subnormals below 2^-6, largest finite 448."""
+    codes = np.arange(0x7F)
+    e, m = codes >> 3, codes & 7
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+_E4M3 = _e4m3_positive_values()
+
+
+def round_f32_to_e4m3_bits(x32: np.ndarray) -> np.ndarray:
+    """fp32 -> e4m3 codes (uint8), round to nearest, ties to the even code.
+    Magnitudes above 448 (the largest finite value) are rejected."""
+    x = np.asarray(x32, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(a > 448.0) or np.any(np.isnan(a)):
+        raise ValueError("value outside the e4m3 range")
+    hi = np.clip(np.searchsorted(_E4M3, a, side="left"), 1, 0x7E)
+    lo = hi - 1
+    dlo, dhi = a - _E4M3[lo], _E4M3[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == 0, 0, code)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of finite e4m3 codes to fp64."""
+    b = np.asarray(bits, dtype=np.uint8)
+    v = _E4M3[np.minimum(b & 0x7F, 0x7E)]
+    return np.where(b & 0x80, -v, v)
+
+
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to fp64."""
     u = bits.astype(np.uint32) << np.uint32(16)
@@ -100,7 +134,8 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 class Drawn:
     """A drawn tensor: ``stored`` holds the storage bits (uint16 for bf16/fp16,
-    float32 for fp32) and ``f64`` the same values widened exactly to fp64."""
+    uint8 for fp8e4m3, float32 for fp32) and ``f64`` the same values widened
+    exactly to fp64."""
 
     __slots__ = ("dtype", "shape", "stored", "f64")
 
@@ -114,6 +149,8 @@ class Drawn:
             t = torch.from_numpy(self.stored.view(np.int16).copy()).view(torch.bfloat16)
         elif self.dtype == "fp16":
             t = torch.from_numpy(self.stored.view(np.int16).copy()).view(torch.float16)
+        elif self.dtype == "fp8e4m3":
+            t = torch.from_numpy(self.stored.copy())  # the bytes, as uint8
         else:
             t = torch.from_numpy(self.stored.copy())
         return t.reshape(self.shape).to(device)
@@ -121,7 +158,7 @@ class Drawn:
 
 def draw(seed: int, tensor_id: int, shape, dtype: str, mul: float = 1.0,
          want_f64: bool = True) -> Drawn:
-    """i.i.d. ``mul * N(0,1)`` values of ``shape``, stored as ``dtype`` in {bf16, fp16, fp32}."""
+    """i.i.d. ``mul * N(0,1)`` values of ``shape``, stored as ``dtype`` in {bf16, fp16, fp32, fp8e4m3}."""
     count = int(np.prod(shape)) if len(shape) else 1
     x = normal_f64(seed, tensor_id, count)
     if mul != 1.0:
@@ -138,6 +175,9 @@ def draw(seed: int, tensor_id: int, shape, dtype: str, mul: float = 1.0,
     elif dtype == "fp32":
         stored = x32
         f64 = x32.astype(np.float64) if want_f64 else None
+    elif dtype == "fp8e4m3":
+        stored = round_f32_to_e4m3_bits(x32)
+        f64 = e4m3_bits_to_f64(stored) if want_f64 else None
     else:
         raise ValueError(f"unknown dtype {dtype!r}")
     stored = stored.reshape(shape)

@@ -37,7 +37,7 @@ def test_exports_every_declared_function(lib):
     names = header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_prep", "fa_bwd_main",
                           "fa_bwd_workspace_size", "fa_status_string", "fa_fwd_sparse", "fa_bwd_sparse",
-                          "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size"}
+                          "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size", "fa_fwd_fp8"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -275,3 +275,28 @@ def test_fwd_sparse_rejects(lib, kw, code):
 ])
 def test_bwd_sparse_rejects(lib, kw, code):
     assert sparse_bwd(lib, **kw) == code
+
+
+# ---------------------------------------------------------------- FP8 forward
+
+def fwd8(lib, B=2, H=3, N=100, d=64, qd=1.0, kd=1.0, vd=0.5, causal=0, **over):
+    names = ["q", "k", "v", "o", "lse"]
+    p = dict(zip(names, ptrs(5)))
+    p.update({k: v for k, v in over.items() if k in names})
+    return lib.fa_fwd_fp8(*[ctypes.c_void_p(p[n]) for n in names], B, H, N, d, ctypes.c_float(0.125), causal,
+                          ctypes.c_float(qd), ctypes.c_float(kd), ctypes.c_float(vd), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(qd=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(kd=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(vd=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=A + 4 * GAP + 4), fa.FA_ERR_INVALID_ARG),   # misaligned
+    (dict(o=A + GAP), fa.FA_ERR_INVALID_ARG),             # o aliases k
+])
+def test_fwd_fp8_rejects(lib, kw, code):
+    assert fwd8(lib, **kw) == code

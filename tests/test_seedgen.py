@@ -77,3 +77,24 @@ def test_block_mask_is_seeded_and_has_its_density():
     assert np.array_equal(a, b) and not np.array_equal(a, c)
     assert set(np.unique(a).tolist()) <= {0, 1}
     assert abs(a.mean() - 0.3) < 0.03
+
+
+def test_e4m3_rounding_matches_torch():
+    """The generator's fp32 -> e4m3 rounding (nearest, ties to even) against torch's
+    float8_e4m3fn conversion, and exact widening back."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(20000) * 3, rng.standard_normal(5000) * 0.01,
+                        rng.uniform(-448, 448, 5000), np.array([0.0, -0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10,
+                                                                1.0625, 1.1875, 0.0029296875])]).astype(np.float32)
+    ours = seedgen.round_f32_to_e4m3_bits(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ours & 0x7F, ref & 0x7F)
+    nz = (ref & 0x7F) != 0
+    np.testing.assert_array_equal(ours[nz], ref[nz])
+    back = torch.from_numpy(ours.copy()).view(torch.float8_e4m3fn).double().numpy()
+    np.testing.assert_array_equal(seedgen.e4m3_bits_to_f64(ours), back)
+    d = seedgen.draw(3, 0, (4, 5), "fp8e4m3")
+    assert d.stored.dtype == np.uint8 and d.f64.shape == (4, 5)
+    with pytest.raises(ValueError):
+        seedgen.round_f32_to_e4m3_bits(np.array([500.0], dtype=np.float32))
