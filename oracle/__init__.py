@@ -59,6 +59,8 @@ def _load():
         lib.oracle_bwd.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_double, ctypes.c_int,
                                    _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.oracle_fwd_kv.argtypes = [_dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_double, ctypes.c_int, _dp, _dp]
         mask_args = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64]
         lib.oracle_fwd_masked.argtypes = ([_dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_double, ctypes.c_int] + mask_args + [_dp, _dp])
@@ -116,6 +118,24 @@ def fwd(q, k, v, scale: float, causal: bool, block_mask=None, block: int = 128):
         m, nb, stride = _block_mask(block_mask, B, H, N, block)
         _load().oracle_fwd_masked(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, float(scale), int(bool(causal)),
                                   m.ctypes.data, nb, block, stride, _ptr(o), _ptr(lse))
+    return o, lse
+
+
+def fwd_kv(q, k, v, scale: float, causal: bool):
+    """Attention of Nq queries ([B,H,Nq,d]) over Nk cached keys and values ([B,H,Nk,d]),
+    the queries being the last Nq positions (causal: query t sees keys j <= t + Nk - Nq).
+    Returns (O [B,H,Nq,d], lse [B,H,Nq])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B,H,Nk,d] with q's B, H and d")
+    if causal and Nq > Nk:
+        raise ValueError("causal attention over a cache needs Nq <= Nk")
+    o = np.empty_like(q)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    _load().oracle_fwd_kv(_ptr(q), _ptr(k), _ptr(v), B, H, Nq, Nk, d, float(scale), int(bool(causal)),
+                          _ptr(o), _ptr(lse))
     return o, lse
 
 

@@ -62,6 +62,7 @@ static double dot(const double* a, const double* b, int d)
  * head's block mask (NULL: every block). */
 typedef struct {
     int causal;
+    int offset;            /* causal: query i sees keys j <= i + offset */
     const uint8_t* blocks; /* nb x nb, row = query block, column = key block */
     int nb, bs;
 } Visibility;
@@ -69,7 +70,7 @@ typedef struct {
 /* Is pair (query i, key j) kept? */
 static int visible(const Visibility* vis, int i, int j)
 {
-    if (vis->causal && j > i) return 0;
+    if (vis->causal && j > i + vis->offset) return 0;
     return vis->blocks == NULL || vis->blocks[(size_t)(i / vis->bs) * vis->nb + j / vis->bs] != 0;
 }
 
@@ -113,6 +114,7 @@ static Visibility head_visibility(int causal, const uint8_t* mask, int nb, int b
 {
     Visibility v;
     v.causal = causal;
+    v.offset = 0;
     v.blocks = mask ? mask + mask_stride * bh : NULL;
     v.nb = nb;
     v.bs = bs;
@@ -145,6 +147,33 @@ void oracle_fwd(const double* q, const double* k, const double* v, int B, int H,
                 double scale, int causal, double* o, double* lse)
 {
     oracle_fwd_masked(q, k, v, B, H, N, d, scale, causal, NULL, 0, 1, 0, o, lse);
+}
+
+/*
+ * Forward with Nq queries against Nk keys per head (attention over a key/value
+ * cache): q, o are [B,H,Nq,d], k, v [B,H,Nk,d], lse [B,H,Nq]. The queries are
+ * the last Nq positions of the sequence, so with causal masking query t sees
+ * keys j <= t + (Nk - Nq).
+ */
+void oracle_fwd_kv(const double* q, const double* k, const double* v, int B, int H, int Nq, int Nk, int d,
+                   double scale, int causal, double* o, double* lse)
+{
+    const int64_t rows = (int64_t)B * H * Nq;
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)Nk);
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < rows; ++r) {
+            const int64_t bh = r / Nq;
+            const int t = (int)(r % Nq);
+            Visibility vis = head_visibility(causal, NULL, 0, 1, 0, bh);
+            vis.offset = Nk - Nq;
+            const size_t kv_head = (size_t)bh * Nk * d;
+            forward_row(q + (size_t)bh * Nq * d, k + kv_head, v + kv_head, Nk, d, scale, &vis, t, p,
+                        o + (size_t)r * d, lse + r);
+        }
+        free(p);
+    }
 }
 
 /*

@@ -20,8 +20,9 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 MUTANTS = [
     ("fwd_scale_dropped", "p[j] = scale * dot(Q + (size_t)i * d, K + (size_t)j * d, d);",
      "p[j] = dot(Q + (size_t)i * d, K + (size_t)j * d, d);"),
-    ("causal_ignored", "if (vis->causal && j > i) return 0;", "if (0) return 0;"),
-    ("causal_off_by_one", "if (vis->causal && j > i) return 0;", "if (vis->causal && j > i + 1) return 0;"),
+    ("causal_ignored", "if (vis->causal && j > i + vis->offset) return 0;", "if (0) return 0;"),
+    ("causal_off_by_one", "if (vis->causal && j > i + vis->offset) return 0;",
+     "if (vis->causal && j > i + vis->offset + 1) return 0;"),
     ("lse_max_dropped", "*lse_i = m + log(l);", "*lse_i = log(l);"),
     ("normalisation_dropped", "for (int j = 0; j < N; ++j) if (visible(vis, i, j)) p[j] /= l;", ""),
     ("o_uses_k", "o_i[c] += p[j] * V[(size_t)j * d + c];", "o_i[c] += p[j] * K[(size_t)j * d + c];"),
@@ -48,6 +49,10 @@ MUTANTS = [
     ("column_pass_ignores_blocks", "if (!visible(&vis, i, j)) continue;   /*",
      "if (vis.causal && j > i) continue;   /*"),
     ("head_stride_ignored", "v.blocks = mask ? mask + mask_stride * bh : NULL;", "v.blocks = mask;"),
+    # queries over a key/value cache
+    ("cache_offset_dropped", "vis.offset = Nk - Nq;", "vis.offset = 0;"),
+    ("cache_offset_off_by_one", "vis.offset = Nk - Nq;", "vis.offset = Nk - Nq - 1;"),
+    ("cache_query_head_stride", "forward_row(q + (size_t)bh * Nq * d,", "forward_row(q + (size_t)bh * Nk * d,"),
     ("dS_uses_pass1_D_minus", "const double ds = pij * (dpij - D_h[i]);", "const double ds = pij * dpij;"),
 ]
 

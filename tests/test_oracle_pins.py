@@ -437,3 +437,43 @@ def test_per_head_masks():
             o1, l1 = oracle.fwd(q, k, v, 0.5, False, block_mask=bms[b, h], block=block)
             np.testing.assert_array_equal(o[b, h], o1[b, h])
             np.testing.assert_array_equal(lse[b, h], l1[b, h])
+
+
+# ---------------------------------------------------------------- queries over a key/value cache
+# Decoding with a key/value cache (the pages name the cache beside the method, GT payoff
+# paragraph): a few new queries, the last positions of the sequence, attend to every
+# cached key (causal: up to their own position).
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_cache_with_every_query_is_dense_attention(causal):
+    q, k, v = qkv(41, 2, 2, 23, 8)
+    o, lse = oracle.fwd_kv(q, k, v, 0.4, causal)
+    o2, lse2 = oracle.fwd(q, k, v, 0.4, causal)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq", [1, 3, 9])
+def test_cache_queries_are_the_last_rows(causal, nq):
+    """The last nq rows of full attention over the whole sequence, bit for bit."""
+    q, k, v = qkv(42, 2, 3, 31, 8)
+    o, lse = oracle.fwd_kv(q[:, :, -nq:], k, v, 0.3, causal)
+    o2, lse2 = oracle.fwd(q, k, v, 0.3, causal)
+    np.testing.assert_array_equal(o, o2[:, :, -nq:])
+    np.testing.assert_array_equal(lse, lse2[:, :, -nq:])
+
+
+def test_cache_matches_torch_cpu_fp64():
+    """torch's CPU float64 attention with the bottom-right causal mask (independent)."""
+    torch = pytest.importorskip("torch")
+    nq, nk, d, scale = 5, 27, 16, 0.25
+    q = rnd(43, 0, (2, 2, nq, d))
+    k, v = rnd(43, 1, (2, 2, nk, d)), rnd(43, 2, (2, 2, nk, d))
+    o, lse = oracle.fwd_kv(q, k, v, scale, True)
+    keep = torch.arange(nk)[None, :] <= torch.arange(nq)[:, None] + (nk - nq)
+    to = torch.nn.functional.scaled_dot_product_attention(torch.tensor(q), torch.tensor(k), torch.tensor(v),
+                                                          attn_mask=keep, scale=scale)
+    np.testing.assert_allclose(o, to.numpy(), atol=1e-12)
+    s = (scale * torch.tensor(q) @ torch.tensor(k).transpose(-1, -2)).masked_fill(~keep, float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, -1).numpy(), atol=1e-12)
