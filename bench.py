@@ -44,6 +44,9 @@ WORKLOADS = {
     # each block kept with probability 1/4, the diagonal always kept
     "blocksparse_16k": dict(B=1, H=16, N=16384, d=64, causal=False, dtype="bf16", seed=1006, mul=1.0,
                             sparse=dict(density=0.25, mask_seed=1006)),
+    # attention of one new query over a 16384-long key/value cache, 8 x 32 heads of 128
+    "decode_8x32_16k": dict(B=8, H=32, N=16384, d=128, causal=True, dtype="bf16", seed=1008, mul=1.0,
+                            decode=dict(Nq=1)),
     # FP8 (e4m3) forward only, descale factors 1: the long causal shape
     "fp8_fwd_long_causal_16k": dict(B=1, H=16, N=16384, d=64, causal=True, dtype="fp8e4m3", seed=1007, mul=1.0,
                                     fwd_only=True),
@@ -211,6 +214,84 @@ def cpu_baseline(w, shape, scale, causal, min_seconds=10.0):
                       f"of the same workload, {t_total:.2f} s; credited with the same rule as the GPU"}
 
 
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def decode_bytes(w):
+    """Compulsory HBM bytes of one call of attention over the cache: read Q, K, V,
+    write O and lse."""
+    B, H, Nk, d, Nq = w["B"], w["H"], w["N"], w["d"], w["decode"]["Nq"]
+    return B * H * (2 * Nq * d * 2 + 2 * Nk * d * 2 + 4 * Nq)
+
+
+def run_decode(args, w):
+    """Bench line for attention over a key/value cache: HBM bound, so the value is
+    compulsory bytes per second."""
+    import torch
+
+    import io_aware_tiled_07_amd as fa
+    import seedgen
+    B, H, Nk, d, Nq = w["B"], w["H"], w["N"], w["d"], w["decode"]["Nq"]
+    causal, scale, dev = w["causal"], 1.0 / math.sqrt(d), "cuda"
+    q = seedgen.draw(w["seed"], 0, (B, H, Nq, d), w["dtype"], want_f64=False).torch(dev)
+    k = seedgen.draw(w["seed"], 1, (B, H, Nk, d), w["dtype"], want_f64=False).torch(dev)
+    v = seedgen.draw(w["seed"], 2, (B, H, Nk, d), w["dtype"], want_f64=False).torch(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_decode_workspace_size(B, H, Nq, Nk, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        fa.fa_decode(q, k, v, o, lse, causal, scale, ws, stream)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(K):
+        evs[i][0].record(stream)
+        fa.fa_decode(q, k, v, o, lse, causal, scale, ws, stream)
+        evs[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / K
+    call_ms = statistics.mean(a.elapsed_time(b) for a, b in evs)
+    nbytes = decode_bytes(w)
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    call_gbs = nbytes / (call_ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        qd = seedgen.draw(w["seed"], 0, (B, H, Nq, d), w["dtype"]).f64.reshape(B * H, Nq, d)
+        kd = seedgen.draw(w["seed"], 1, (B, H, Nk, d), w["dtype"]).f64.reshape(B * H, Nk, d)
+        vd = seedgen.draw(w["seed"], 2, (B, H, Nk, d), w["dtype"]).f64.reshape(B * H, Nk, d)
+        reps, t_total, nh = 0, 0.0, B * H
+        while t_total < 10.0 and reps < 1000:
+            a = time.perf_counter()
+            oracle.fwd_kv(qd[None, :nh], kd[None, :nh], vd[None, :nh], scale, causal)
+            t_total += time.perf_counter() - a
+            reps += 1
+        cpu = {"value": round(nbytes * reps / t_total / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "cpu_model": cpu_model(),
+               "sample": f"{reps} pass(es) of the fp64 oracle over all {nh} heads of the same workload, "
+                         f"{t_total:.2f} s; credited with the same compulsory bytes"}
+    out = {
+        "metric": "attention over a key/value cache: GB/s of compulsory HBM traffic (read Q, K, V; write O, lse)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w["dtype"], "data": "synthetic: seeded i.i.d. N(0,1) query and cache of the workload's shape",
+        "config": {"workload": args.workload, "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "causal": causal,
+                   "dtype": w["dtype"], "scale": scale},
+        "roofline": {"bound": "hbm", "achieved": round(call_gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(call_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": nbytes, "kernel": "fa_decode: decode_split_kernel + decode_merge_kernel",
+                     "avg_launch_ms": round(call_ms, 5)},
+        "cpu_baseline": cpu, "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +319,9 @@ def main():
     import seedgen
 
     w = dict(WORKLOADS[args.workload])
+    if "decode" in w:
+        run_decode(args, w)
+        return
     mask_np = block_mask(w)
     sparse = mask_np is not None
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]

@@ -185,6 +185,27 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int causal,
                float q_descale, float k_descale, float v_descale, void* stream);
 
+/*
+ * Attention of a few new queries over a long key/value cache (decoding; the pages
+ * name the cache beside the method, groundtruth.day payoff paragraph). The same
+ * exact attention, tiled with an online softmax and split over the keys; the
+ * splits are merged with their row statistics (lse = log sum exp lse_s,
+ * O = sum exp(lse_s - lse) O_s).
+ *   q       : [B,H,Nq,d] of `dtype`, the last Nq positions of the sequence, 1 <= Nq <= 8.
+ *   k, v    : [B,H,Nk,d] of `dtype`, the cache (Nk >= 1; causal needs Nk >= Nq).
+ *   o, lse  : [B,H,Nq,d] of `dtype` and [B,H,Nq] fp32 (natural log).
+ *   causal  : 1 = query t sees keys j <= t + Nk - Nq; 0 = every key.
+ *   workspace: caller-owned device memory, 256-byte aligned, at least
+ *             fa_decode_workspace_size() bytes (the per-split partial results).
+ * bf16/fp16, d in {64, 128} (else FA_ERR_UNSUPPORTED, also for Nq > 8). Errors
+ * and semantics otherwise as fa_fwd. Returns a fa_status.
+ */
+size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d);
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a fa_status value. Never NULL. */
 const char* fa_status_string(int status);
 

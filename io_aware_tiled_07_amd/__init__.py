@@ -8,9 +8,10 @@ fails, an exception is raised.
 The raw entry points keep the C names (``fa_fwd``, ``fa_bwd``, ``fa_bwd_dq``,
 ``fa_bwd_prep``, ``fa_bwd_main``, ``fa_bwd_workspace_size``, ``fa_status_string``,
 for block-sparse attention ``fa_fwd_sparse``, ``fa_bwd_sparse`` and their
-workspace sizes, and the FP8 forward ``fa_fwd_fp8``) and take caller-allocated
-torch tensors; ``fwd``, ``bwd``, ``fwd_sparse``, ``bwd_sparse`` and ``fwd_fp8``
-allocate their outputs.
+workspace sizes, the FP8 forward ``fa_fwd_fp8``, and attention over a key/value
+cache ``fa_decode`` with ``fa_decode_workspace_size``) and take caller-allocated
+torch tensors; ``fwd``, ``bwd``, ``fwd_sparse``, ``bwd_sparse``, ``fwd_fp8`` and
+``decode`` allocate their outputs.
 """
 from __future__ import annotations
 
@@ -24,7 +25,8 @@ __all__ = [
     "FaError", "library_path", "load", "fa_status_string", "fa_bwd_workspace_size",
     "fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_prep", "fa_bwd_main", "fwd", "bwd", "dtype_code",
     "FA_SPARSE_BLOCK", "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size", "fa_fwd_sparse",
-    "fa_bwd_sparse", "fwd_sparse", "bwd_sparse", "fa_fwd_fp8", "fwd_fp8",
+    "fa_bwd_sparse", "fwd_sparse", "bwd_sparse", "fa_fwd_fp8", "fwd_fp8", "fa_decode_workspace_size",
+    "fa_decode", "decode",
 ]
 
 FA_BF16, FA_FP16, FA_FP32 = 0, 1, 2
@@ -81,6 +83,10 @@ def load():
         lib.fa_bwd_sparse.restype = _i
         lib.fa_fwd_fp8.argtypes = [_vp] * 5 + [_i, _i, _i, _i, _f, _i, _f, _f, _f, _vp]
         lib.fa_fwd_fp8.restype = _i
+        lib.fa_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i]
+        lib.fa_decode_workspace_size.restype = _sz
+        lib.fa_decode.argtypes = [_vp] * 5 + [_i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]
+        lib.fa_decode.restype = _i
         _lib = lib
     return _lib
 
@@ -335,4 +341,41 @@ def fwd_fp8(q, k, v, causal: bool = False, scale=None, q_descale: float = 1.0, k
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     fa_fwd_fp8(q, k, v, o, lse, causal, scale, q_descale, k_descale, v_descale, stream)
+    return o, lse
+
+
+# ---------------------------------------------------------------- attention over a key/value cache
+
+def fa_decode_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load().fa_decode_workspace_size(B, H, Nq, Nk, d))
+
+
+def fa_decode(q, k, v, o, lse, causal: bool = True, scale=None, workspace=None, stream=None) -> None:
+    """Attention of q ([B,H,Nq,d], the last Nq positions, Nq <= 8) over the cache k, v
+    ([B,H,Nk,d]) into caller-allocated ``o`` ([B,H,Nq,d]) and ``lse`` ([B,H,Nq] float32)."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B,H,N,d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _check_bhnd("q", q)
+    for name, t in (("k", k), ("v", v)):
+        _check_bhnd(name, t, (B, H, Nk, d), q.dtype)
+    _check_bhnd("o", o, q.shape, q.dtype)
+    _check_bhnd("lse", lse, (B, H, Nq), torch.float32)
+    workspace, nbytes = _workspace(q, fa_decode_workspace_size(B, H, Nq, Nk, d), workspace)
+    st = load().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
+                          _scale(scale, d), int(bool(causal)), dtype_code(q), workspace.data_ptr(), nbytes,
+                          _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode")
+
+
+def decode(q, k, v, causal: bool = True, scale=None, stream=None):
+    """Allocate O and lse and run attention over the cache. Returns (o, lse)."""
+    import torch
+    B, H, Nq, _ = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fa_decode(q, k, v, o, lse, causal, scale, None, stream)
     return o, lse

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfa.so")
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd128.hip", "fa_bwd_atomic.hip", "fa_fp32.hip",
-           "fa_sparse.hip", "fa_fwd_fp8.hip"]
+           "fa_sparse.hip", "fa_fwd_fp8.hip", "fa_decode.hip"]
 # MFMA results stay in arch VGPRs (the softmax reads them directly, no AGPR
 # copies) everywhere except the head-dim-128 backward, whose fp32 accumulators
 # need the AGPRs beside the 256 VGPRs.

@@ -146,6 +146,22 @@ int check_sparse(int dtype, const void* mask, int N, long long head_stride, cons
     return FA_OK;
 }
 
+// ---------------------------------------------------------------- attention over a key/value cache
+constexpr int kDecodeMaxQ = 8;
+
+struct DecodeLayout {
+    size_t part_o, part_lse, bytes;
+};
+DecodeLayout decode_layout(int B, int H, int Nq, int Nk, int d) {
+    const fa::DecodeSplit sp = fa::decode_split(B, H, Nk);
+    const size_t rows = (size_t)B * H * sp.S * Nq;
+    DecodeLayout L;
+    L.part_o = 0;
+    L.part_lse = round_up(rows * d * sizeof(float), 256);
+    L.bytes = L.part_lse + round_up(rows * sizeof(float), 256);
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -381,6 +397,44 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     (void)hipGetLastError();
     const hipError_t e = fa::fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, causal != 0, q_descale, k_descale,
                                      v_descale, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d) {
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return 0;
+    return decode_layout(B, H, Nq, Nk, d).bytes;
+}
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+              int d, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (Nq > kDecodeMaxQ) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (causal && Nq > Nk) return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+    const int64_t bh = (int64_t)B * H;
+    if ((int64_t)Nk > kMaxN || bh > kMaxGrid || bh * fa::decode_split(B, H, Nk).S > kMaxGrid) return FA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, o, lse};
+    for (const void* p : ptrs)
+        if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
+    const DecodeLayout L = decode_layout(B, H, Nq, Nk, d);
+    if (workspace == nullptr || !aligned256(workspace) || workspace_bytes < L.bytes) return FA_ERR_WORKSPACE;
+    const size_t qbytes = (size_t)bh * Nq * d * 2, kvbytes = (size_t)bh * Nk * d * 2;
+    const Range outs[] = {range(o, qbytes), range(lse, (size_t)bh * Nq * sizeof(float)), range(workspace, L.bytes)};
+    const Range ins[] = {range(q, qbytes), range(k, kvbytes), range(v, kvbytes)};
+    for (int i = 0; i < 3; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return FA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
+    }
+    char* base = static_cast<char*>(workspace);
+    (void)hipGetLastError();
+    const hipError_t e = fa::decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype,
+                                    reinterpret_cast<float*>(base + L.part_o), reinterpret_cast<float*>(base + L.part_lse),
+                                    static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

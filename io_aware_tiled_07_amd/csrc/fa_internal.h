@@ -57,6 +57,18 @@ hipError_t bwd128_fused_sparse(const void* q, const void* k, const void* v, cons
 hipError_t fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                    float scale, bool causal, float q_descale, float k_descale, float v_descale, hipStream_t stream);
 
+// Attention of Nq <= 8 queries over an Nk-long key/value cache (16-bit, d in
+// {64, 128}), split over the keys: the split plan, and the launch that writes
+// per-split partial results (part_o [BH][S][Nq][d], part_lse [BH][S][Nq], fp32)
+// and merges them into o and lse.
+struct DecodeSplit {
+    int S;      // splits of the keys
+    int chunk;  // keys per split
+};
+DecodeSplit decode_split(int B, int H, int Nk);
+hipError_t decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                  int d, float scale, bool causal, int dtype, float* part_o, float* part_lse, hipStream_t stream);
+
 // fp32 forward and backward, d = 64.
 hipError_t fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                    int N, float scale, bool causal, hipStream_t stream);

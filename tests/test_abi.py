@@ -37,7 +37,8 @@ def test_exports_every_declared_function(lib):
     names = header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_prep", "fa_bwd_main",
                           "fa_bwd_workspace_size", "fa_status_string", "fa_fwd_sparse", "fa_bwd_sparse",
-                          "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size", "fa_fwd_fp8"}
+                          "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size", "fa_fwd_fp8",
+                          "fa_decode", "fa_decode_workspace_size"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -300,3 +301,46 @@ def fwd8(lib, B=2, H=3, N=100, d=64, qd=1.0, kd=1.0, vd=0.5, causal=0, **over):
 ])
 def test_fwd_fp8_rejects(lib, kw, code):
     assert fwd8(lib, **kw) == code
+
+
+# ---------------------------------------------------------------- attention over a key/value cache
+
+def test_decode_workspace_size(lib):
+    # 8 x 32 heads over 16384 keys: 2048 keys per split, 8 splits
+    def up(x):
+        return (x + 255) // 256 * 256
+    rows = 8 * 32 * 8 * 1
+    assert fa.fa_decode_workspace_size(8, 32, 1, 16384, 128) == up(rows * 128 * 4) + up(rows * 4)
+    # a small cache: one split of at least 256 keys
+    assert fa.fa_decode_workspace_size(1, 2, 4, 100, 64) == up(2 * 4 * 64 * 4) + up(2 * 4 * 4)
+    assert fa.fa_decode_workspace_size(1, 2, 0, 100, 64) == 0
+
+
+def dec(lib, B=2, H=3, Nq=1, Nk=1000, d=64, causal=1, dtype=0, ws=None, ws_bytes=None, **over):
+    names = ["q", "k", "v", "o", "lse"]
+    p = dict(zip(names, ptrs(5)))
+    p.update({k: v for k, v in over.items() if k in names})
+    need = fa.fa_decode_workspace_size(B, H, max(Nq, 1), max(Nk, 1), d)
+    ws = A + 6 * GAP if ws is None else ws
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return lib.fa_decode(*[ctypes.c_void_p(p[n]) for n in names], B, H, Nq, Nk, d, ctypes.c_float(0.125), causal,
+                         dtype, ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nq=9), fa.FA_ERR_UNSUPPORTED),               # at most 8 queries
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=4, Nk=3), fa.FA_ERR_INVALID_ARG),         # causal needs Nk >= Nq
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=A + GAP), fa.FA_ERR_INVALID_ARG),          # o aliases k
+    (dict(ws=0), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=8), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 6 * GAP + 16), fa.FA_ERR_WORKSPACE),  # not 256-byte aligned
+    (dict(ws=A + 2 * GAP), fa.FA_ERR_INVALID_ARG),     # workspace overlaps v
+])
+def test_decode_rejects(lib, kw, code):
+    assert dec(lib, **kw) == code
