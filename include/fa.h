@@ -206,6 +206,33 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * General shapes for the 16-bit forward: strided layouts (for instance [B,N,H,d]
+ * storage, "BSHD", seen as [B,H,N,d]), Nq queries against Nk keys, and
+ * sequences of different lengths padded into one batch.
+ *   fa_strides      : element strides of a [B,H,N,d] view (the head-dim stride is 1);
+ *                     every stride >= 0 and a multiple of 8, each view's base 16-byte aligned.
+ *   q, o            : Nq rows per (batch, head); k, v: Nk rows.
+ *   lse             : [B,H,Nq] fp32, contiguous.
+ *   seqlens_q/_k    : NULL, or device arrays of B ints: sequence b has seqlens_q[b]
+ *                     queries and seqlens_k[b] keys (clamped to [0, Nq] / [0, Nk]); rows
+ *                     past a sequence's queries are neither computed nor written.
+ *   causal          : the queries are the last positions of their sequence: query i of
+ *                     sequence b sees keys j <= i + seqlens_k[b] - seqlens_q[b]; a row that
+ *                     sees no key gets O = 0 and lse = -inf.
+ * dtype bf16/fp16, d in {64, 128}. Errors as fa_fwd (overlapping views, bad strides or
+ * misaligned bases -> FA_ERR_INVALID_ARG). Returns a fa_status.
+ */
+typedef struct {
+    long long batch, head, row;
+} fa_strides;
+
+int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                   const fa_strides* q_strides, const fa_strides* k_strides,
+                   const fa_strides* v_strides, const fa_strides* o_strides,
+                   const int* seqlens_q, const int* seqlens_k, void* stream);
+
 /* Static, human-readable name of a fa_status value. Never NULL. */
 const char* fa_status_string(int status);
 

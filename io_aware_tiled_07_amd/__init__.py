@@ -9,9 +9,10 @@ The raw entry points keep the C names (``fa_fwd``, ``fa_bwd``, ``fa_bwd_dq``,
 ``fa_bwd_prep``, ``fa_bwd_main``, ``fa_bwd_workspace_size``, ``fa_status_string``,
 for block-sparse attention ``fa_fwd_sparse``, ``fa_bwd_sparse`` and their
 workspace sizes, the FP8 forward ``fa_fwd_fp8``, and attention over a key/value
-cache ``fa_decode`` with ``fa_decode_workspace_size``) and take caller-allocated
-torch tensors; ``fwd``, ``bwd``, ``fwd_sparse``, ``bwd_sparse``, ``fwd_fp8`` and
-``decode`` allocate their outputs.
+cache ``fa_decode`` with ``fa_decode_workspace_size``, and the forward over
+general shapes ``fa_fwd_general``) and take caller-allocated torch tensors;
+``fwd``, ``bwd``, ``fwd_sparse``, ``bwd_sparse``, ``fwd_fp8``, ``decode`` and
+``fwd_general`` allocate their outputs.
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ __all__ = [
     "fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_prep", "fa_bwd_main", "fwd", "bwd", "dtype_code",
     "FA_SPARSE_BLOCK", "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size", "fa_fwd_sparse",
     "fa_bwd_sparse", "fwd_sparse", "bwd_sparse", "fa_fwd_fp8", "fwd_fp8", "fa_decode_workspace_size",
-    "fa_decode", "decode",
+    "fa_decode", "decode", "fa_fwd_general", "fwd_general",
 ]
 
 FA_BF16, FA_FP16, FA_FP32 = 0, 1, 2
@@ -87,6 +88,8 @@ def load():
         lib.fa_decode_workspace_size.restype = _sz
         lib.fa_decode.argtypes = [_vp] * 5 + [_i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]
         lib.fa_decode.restype = _i
+        lib.fa_fwd_general.argtypes = [_vp] * 5 + [_i, _i, _i, _i, _i, _f, _i, _i] + [_vp] * 7
+        lib.fa_fwd_general.restype = _i
         _lib = lib
     return _lib
 
@@ -378,4 +381,54 @@ def decode(q, k, v, causal: bool = True, scale=None, stream=None):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     fa_decode(q, k, v, o, lse, causal, scale, None, stream)
+    return o, lse
+
+
+# ---------------------------------------------------------------- general shapes
+
+class _Strides(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_longlong), ("head", ctypes.c_longlong), ("row", ctypes.c_longlong)]
+
+
+def _strides(t):
+    """fa_strides of a [B,H,N,d] torch view whose last dimension is contiguous."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B,H,N,d] view with a contiguous last dimension")
+    return _Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def fa_fwd_general(q, k, v, o, lse, causal: bool = False, scale=None, seqlens_q=None, seqlens_k=None,
+                   stream=None) -> None:
+    """Forward over general shapes: q, o are [B,H,Nq,d] views and k, v [B,H,Nk,d] views with any
+    strides (last dimension contiguous), lse [B,H,Nq] float32; seqlens_q / seqlens_k are None or
+    int32 device tensors of B lengths (sequences padded into the batch)."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for name, t, n in (("q", q, Nq), ("k", k, Nk), ("v", v, Nk), ("o", o, Nq)):
+        if not t.is_cuda or tuple(t.shape) != (B, H, n, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a device tensor [B,H,{n},d] of q's dtype")
+    _check_bhnd("lse", lse, (B, H, Nq), torch.float32)
+    lens = []
+    for name, t in (("seqlens_q", seqlens_q), ("seqlens_k", seqlens_k)):
+        if t is None:
+            lens.append(None)
+        else:
+            _check_bhnd(name, t, (B,), torch.int32)
+            lens.append(t.data_ptr())
+    ss = [_strides(t) for t in (q, k, v, o)]
+    st = load().fa_fwd_general(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq,
+                               Nk, d, _scale(scale, d), int(bool(causal)), dtype_code(q),
+                               *[ctypes.byref(x) for x in ss], lens[0], lens[1], _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_general")
+
+
+def fwd_general(q, k, v, causal: bool = False, scale=None, seqlens_q=None, seqlens_k=None, stream=None):
+    """Allocate O (same layout as q) and lse and run the general-shape forward. Returns (o, lse)."""
+    import torch
+    B, H, Nq, _ = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd_general(q, k, v, o, lse, causal, scale, seqlens_q, seqlens_k, stream)
     return o, lse

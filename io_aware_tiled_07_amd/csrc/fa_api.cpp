@@ -162,6 +162,28 @@ DecodeLayout decode_layout(int B, int H, int Nq, int Nk, int d) {
     return L;
 }
 
+// ---------------------------------------------------------------- general shapes
+// A strided [B,H,N,d] view is valid when its strides are non-negative multiples
+// of 8 elements (16 bytes) and its base is 16-byte aligned.
+bool strides_ok(const fa_strides* s) {
+    return s != nullptr && s->batch >= 0 && s->head >= 0 && s->row >= 0 && s->batch % 8 == 0 && s->head % 8 == 0 &&
+           s->row % 8 == 0;
+}
+// Byte span of a strided view (first byte to one past the last).
+Range view_range(const void* p, const fa_strides* s, int B, int H, int N, int d, int elt) {
+    const size_t last = (size_t)(B - 1) * s->batch + (size_t)(H - 1) * s->head + (size_t)(N - 1) * s->row + d;
+    return range(p, last * elt);
+}
+// Distinct (batch, head, row) reach distinct rows of d elements: the output is
+// not written twice. Checked for the plain orderings (rows innermost or heads
+// innermost).
+bool view_disjoint(const fa_strides* s, int B, int H, int N, int d) {
+    const long long r = s->row, h = s->head, b = s->batch;
+    const bool rows_in = r >= d && (H == 1 || h >= r * N) && (B == 1 || b >= h * H) && (B == 1 || b >= r * N);
+    const bool heads_in = h >= d && (N == 1 || r >= h * H) && (B == 1 || b >= r * N);
+    return rows_in || heads_in;
+}
+
 }  // namespace
 
 extern "C" {
@@ -435,6 +457,44 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
     const hipError_t e = fa::decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype,
                                     reinterpret_cast<float*>(base + L.part_o), reinterpret_cast<float*>(base + L.part_lse),
                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                   int d, float scale, int causal, int dtype, const fa_strides* q_strides,
+                   const fa_strides* k_strides, const fa_strides* v_strides, const fa_strides* o_strides,
+                   const int* seqlens_q, const int* seqlens_k, void* stream) {
+    if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+    const int64_t bh = (int64_t)B * H;
+    if ((int64_t)Nq > kMaxN || (int64_t)Nk > kMaxN || bh > kMaxGrid || bh * ((Nq + 127) / 128) > kMaxGrid)
+        return FA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, o, lse};
+    for (const void* p : ptrs)
+        if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
+    const fa_strides* ss[] = {q_strides, k_strides, v_strides, o_strides};
+    for (const fa_strides* x : ss)
+        if (!strides_ok(x)) return FA_ERR_INVALID_ARG;
+    if (!view_disjoint(o_strides, B, H, Nq, d)) return FA_ERR_INVALID_ARG;
+    if (((uintptr_t)seqlens_q & 3u) != 0 || ((uintptr_t)seqlens_k & 3u) != 0) return FA_ERR_INVALID_ARG;
+    const Range ro = view_range(o, o_strides, B, H, Nq, d, 2), rl = range(lse, (size_t)bh * Nq * sizeof(float));
+    const Range ins[] = {view_range(q, q_strides, B, H, Nq, d, 2), view_range(k, k_strides, B, H, Nk, d, 2),
+                         view_range(v, v_strides, B, H, Nk, d, 2),
+                         seqlens_q ? range(seqlens_q, (size_t)B * sizeof(int)) : Range{0, 0},
+                         seqlens_k ? range(seqlens_k, (size_t)B * sizeof(int)) : Range{0, 0}};
+    for (const Range& r : ins)
+        if (overlap(ro, r) || overlap(rl, r)) return FA_ERR_INVALID_ARG;
+    if (overlap(ro, rl)) return FA_ERR_INVALID_ARG;
+    const int64_t sq[3] = {q_strides->batch, q_strides->head, q_strides->row};
+    const int64_t sk[3] = {k_strides->batch, k_strides->head, k_strides->row};
+    const int64_t sv[3] = {v_strides->batch, v_strides->head, v_strides->row};
+    const int64_t so[3] = {o_strides->batch, o_strides->head, o_strides->row};
+    (void)hipGetLastError();
+    const hipError_t e = fa::fwd_general(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype, sq, sk, sv, so,
+                                         seqlens_q, seqlens_k, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -220,6 +220,16 @@ __device__ __forceinline__ i32x4 rows_rsrc(const void* base, int n, int r0) {
     return buffer_rsrc(static_cast<const char*>(base) + (int64_t)r0 * RB, left);
 }
 
+// The same for rows `stride` bytes apart, each RB bytes long: lanes address
+// row r (relative to r0) at r * stride + column bytes, and rows at or past n
+// read as zeros. Precondition: r0 < n.
+template <int RB>
+__device__ __forceinline__ i32x4 strided_rows_rsrc(const void* base, int n, int r0, uint32_t stride) {
+    const uint64_t left = (uint64_t)(n - r0 - 1) * stride + RB;
+    return buffer_rsrc(static_cast<const char*>(base) + (int64_t)r0 * stride,
+                       (uint32_t)(left < 0xFFFFFFFFull ? left : 0xFFFFFFFFull));
+}
+
 // ---------------------------------------------------------------- row stores
 // A wave's 32 x (32 DT) block in MFMA accumulator order (lane l holds column
 // l % 32; register 4g + k of tile u holds element 32u + 8g + 4(l / 32) + k of

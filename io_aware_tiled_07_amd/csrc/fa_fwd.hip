@@ -77,6 +77,13 @@ struct FwdArgs {
     const uint64_t* mask_rows;
     int W, nb;
     int64_t head_words;
+    // general shapes: element strides (batch, head, row) of q, k, v, o; N is
+    // the query extent, Nk the key extent; per-sequence lengths (nullptr: the
+    // extents); causal alignment at the end (query i sees keys j <= i + nk - nq)
+    int64_t sq[3], sk[3], sv[3], so[3];
+    int H, Nk;
+    const int* lens_q;
+    const int* lens_k;
 };
 
 constexpr int kCusPerXcd = 32;  // MI350-series: 256 CUs in 8 XCDs
@@ -104,7 +111,7 @@ __device__ __forceinline__ void map_block(int bid, const FwdArgs& a, int& bh, in
     }
 }
 
-template <typename T, int D, bool CAUSAL, int NW, bool SPARSE>
+template <typename T, int D, bool CAUSAL, int NW, bool SPARSE, bool GEN = false>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     constexpr int KS = D / 16;           // k-steps of the score MFMA
     constexpr int DT = D / 32;           // 32-wide output tiles
@@ -126,15 +133,36 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     int bh, qb;
     map_block(blockIdx.x, a, bh, qb);
     const int N = a.N;
+    // queries, keys, causal offset (query i sees keys j <= i + off), tensor bases
+    // and row strides (elements; K and V rows in bytes)
+    int nq = N, nk = N, off = 0;
+    int64_t qrs = D, ors = D;
+    uint32_t krs = 2 * D, vrs = 2 * D;
     const size_t head = (size_t)bh * N * D;
     const uint16_t* __restrict__ Q = a.q + head;
     const char* __restrict__ K = reinterpret_cast<const char*>(a.k + head);
     const char* __restrict__ V = reinterpret_cast<const char*>(a.v + head);
+    uint16_t* __restrict__ O = a.o + head;
+    if constexpr (GEN) {
+        const int b = bh / a.H, hh = bh % a.H;
+        nq = a.lens_q ? min(max(a.lens_q[b], 0), N) : N;  // lengths beyond the extents are clamped
+        nk = a.lens_k ? min(max(a.lens_k[b], 0), a.Nk) : a.Nk;
+        off = nk - nq;
+        if (qb * BR >= nq) return;  // the whole workgroup: past this sequence's queries
+        qrs = a.sq[2];
+        ors = a.so[2];
+        krs = (uint32_t)(2 * a.sk[2]);
+        vrs = (uint32_t)(2 * a.sv[2]);
+        Q = a.q + b * a.sq[0] + hh * a.sq[1];
+        K = reinterpret_cast<const char*>(a.k + b * a.sk[0] + hh * a.sk[1]);
+        V = reinterpret_cast<const char*>(a.v + b * a.sv[0] + hh * a.sv[1]);
+        O = a.o + b * a.so[0] + hh * a.so[1];
+    }
 
     const int q0 = qb * BR + wave * 32;  // first query row of this wave
-    const bool wave_active = q0 < N;
+    const bool wave_active = q0 < nq;
 
-    const int nkb_all = (N + kBc - 1) / kBc;
+    const int nkb_all = (nk + kBc - 1) / kBc;
     // key blocks this workgroup visits; block-sparse: the 64-key halves of the
     // kept 128-key blocks of mask row qb (causal: up to the diagonal), in order
     static_assert(!SPARSE || BR == kSparseBlock, "a workgroup covers one block row of the mask");
@@ -143,6 +171,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     if constexpr (SPARSE) {
         walk.init(a.mask_rows + (size_t)bh * a.head_words + (size_t)qb * a.W, 0, nkb_all);
         nkb = walk.count(0, CAUSAL ? qb : a.nb - 1);
+    } else if constexpr (GEN) {
+        const int last = min(nq, (qb + 1) * BR) - 1 + off;  // last key the workgroup's rows see
+        nkb = CAUSAL ? (last < 0 ? 0 : min(nkb_all, last / kBc + 1)) : nkb_all;
     } else {
         nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * BR) - 1) / kBc + 1) : nkb_all;
     }
@@ -159,23 +190,38 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     // same lane offsets serve the K and the V block; rows past the end of the
     // sequence read as zeros (and are masked).
     uint32_t dma_off[HALF];  // byte offset of the lane's granule from the block's first row
+    uint32_t dma_off_v[GEN ? HALF : 1];  // the same for V when its rows are strided differently
 #pragma unroll
     for (int j = 0; j < HALF; ++j) {
         const int p = (j * NW + wave) * 64 + lane;
         const int r = p / CH, c = (p % CH) ^ swz<D>(r);
-        dma_off[j] = (uint32_t)((r * D + c * 8) * 2);
+        if constexpr (GEN) {
+            dma_off[j] = (uint32_t)r * krs + c * 16;
+            dma_off_v[j] = (uint32_t)r * vrs + c * 16;
+        } else {
+            dma_off[j] = (uint32_t)((r * D + c * 8) * 2);
+        }
     }
     auto issue = [&](int kb, auto slot_c) {
         constexpr int SLOT = decltype(slot_c)::value;
         if constexpr (SPARSE) kb = walk.next();
         unit[SLOT] = kb;
-        const i32x4 kr = rows_rsrc<D * 2>(K, N, kb * kBc);
-        const i32x4 vr = rows_rsrc<D * 2>(V, N, kb * kBc);
         char* sb = smem + SLOT * SB + wave * 1024;
+        if constexpr (GEN) {
+            const i32x4 kr = strided_rows_rsrc<D * 2>(K, nk, kb * kBc, krs);
+            const i32x4 vr = strided_rows_rsrc<D * 2>(V, nk, kb * kBc, vrs);
 #pragma unroll
-        for (int j = 0; j < HALF; ++j) dma16(kr, dma_off[j], sb + j * NW * 1024);
+            for (int j = 0; j < HALF; ++j) dma16(kr, dma_off[j], sb + j * NW * 1024);
 #pragma unroll
-        for (int j = 0; j < HALF; ++j) dma16(vr, dma_off[j], sb + TB + j * NW * 1024);
+            for (int j = 0; j < HALF; ++j) dma16(vr, dma_off_v[j], sb + TB + j * NW * 1024);
+        } else {
+            const i32x4 kr = rows_rsrc<D * 2>(K, N, kb * kBc);
+            const i32x4 vr = rows_rsrc<D * 2>(V, N, kb * kBc);
+#pragma unroll
+            for (int j = 0; j < HALF; ++j) dma16(kr, dma_off[j], sb + j * NW * 1024);
+#pragma unroll
+            for (int j = 0; j < HALF; ++j) dma16(vr, dma_off[j], sb + TB + j * NW * 1024);
+        }
     };
 
     // Loop-invariant LDS addresses; slot, key tile and key chunk are immediates.
@@ -205,11 +251,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     // into a register is pending inside the loop (else it drains the ring there).
     u32x4 qf[KS];
     {
-        const uint16_t* qp = Q + (size_t)min(q0 + l32, N - 1) * D + 8 * h;
+        const uint16_t* qp = Q + (size_t)min(q0 + l32, nq - 1) * qrs + 8 * h;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
     }
-    if (!SPARSE || nkb > 0) issue(0, Int<0>{});
+    if (!(SPARSE || GEN) || nkb > 0) issue(0, Int<0>{});
     if (STAGES == 3 && nkb > 1) {
         issue(1, Int<1>{});
         wait_vmcnt<4 * HALF>();
@@ -233,7 +279,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
             if (kb + 1 < nkb) issue(kb + 1, Int<(SLOT + 1) % 2>{});
         }
         const int key0 = (SPARSE ? unit[SLOT] : kb) * kBc;
-        if (!wave_active || (CAUSAL && key0 > q0 + 31)) return;
+        if (!wave_active || (CAUSAL && key0 > q0 + 31 + off)) return;
 
         // ---- S^T (64 keys x 32 queries): two 32x32 tiles. All K operand reads
         // go out first so their LDS latency overlaps.
@@ -274,9 +320,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
 
         // ---- mask: causal diagonal block and ragged end of the sequence.
         // Register i of key tile kt holds key key0 + 32 kt + 16 (i/8) + 8 h + i%8.
-        if ((CAUSAL && key0 + kBc - 1 > q0) || key0 + kBc > N) {
+        if ((CAUSAL && key0 + kBc - 1 > q0 + off) || key0 + kBc > nk) {
             const int qrow = q0 + l32;
-            const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - key0 - 8 * h;  // last visible offset
+            const int lim = (CAUSAL ? min(qrow + off, nk - 1) : nk - 1) - key0 - 8 * h;  // last visible offset
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -351,11 +397,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a) {
     const int qrow = q0 + l32;
     if (wave_active) {
         char* stage = smem + (nkb % STAGES) * SB + wave * (2048 * DT);
-        if constexpr (SPARSE) {
-            // a block row that keeps no key: O = 0 and lse = -inf
+        if constexpr (SPARSE || GEN) {
+            // a row that sees no key (block mask, or causal with more queries
+            // than keys): O = 0 and lse = -inf
             const bool any = l_tot > 0.f;
-            store_rows<T, DT>(oacc, any ? 1.f / l_tot : 0.f, a.o + head + (size_t)q0 * D, D, N - q0, stage);
-            if (h == 0 && qrow < N)
+            store_rows<T, DT>(oacc, any ? 1.f / l_tot : 0.f, O + (size_t)q0 * ors, (int)ors, nq - q0, stage);
+            if (h == 0 && qrow < nq)
                 a.lse[(size_t)bh * N + qrow] = any ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
         } else {
             store_rows<T, DT>(oacc, 1.f / l_tot, a.o + head + (size_t)q0 * D, D, N - q0, stage);
@@ -382,6 +429,16 @@ hipError_t launch(FwdArgs a, hipStream_t stream) {
                    per_xcd <= kResident * kCusPerXcd)
                       ? per_xcd / kCusPerXcd : 0;
     hipLaunchKernelGGL((fwd_kernel<T, D, C, S::NW, SPARSE>), dim3(a.BH * a.nqb), dim3(64 * S::NW), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D, bool C>
+hipError_t launch_general(FwdArgs a, hipStream_t stream) {
+    using S = FwdShape<D>;
+    a.nqb = (a.N + S::BR - 1) / S::BR;
+    a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
+    a.cu_rounds = 0;
+    hipLaunchKernelGGL((fwd_kernel<T, D, C, S::NW, false, true>), dim3(a.BH * a.nqb), dim3(64 * S::NW), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -433,6 +490,43 @@ hipError_t fwd_sparse(const void* q, const void* k, const void* v, void* o, floa
     a.nb = (N + kSparseBlock - 1) / kSparseBlock;
     a.head_words = head_words;
     return dtype == 0 ? dispatch_d<Bf16, true>(a, d, causal, stream) : dispatch_d<F16, true>(a, d, causal, stream);
+}
+
+hipError_t fwd_general(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                       int d, float scale, bool causal, int dtype, const int64_t* sq, const int64_t* sk,
+                       const int64_t* sv, const int64_t* so, const int* lens_q, const int* lens_k,
+                       hipStream_t stream) {
+    FwdArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse;
+    a.BH = B * H;
+    a.N = Nq;
+    a.nqb = 0;
+    a.heads_per_xcd = 0;
+    a.cu_rounds = 0;
+    a.c = scale * kLog2e;
+    a.mask_rows = nullptr;
+    a.W = a.nb = 0;
+    a.head_words = 0;
+    for (int i = 0; i < 3; ++i) {
+        a.sq[i] = sq[i];
+        a.sk[i] = sk[i];
+        a.sv[i] = sv[i];
+        a.so[i] = so[i];
+    }
+    a.H = H;
+    a.Nk = Nk;
+    a.lens_q = lens_q;
+    a.lens_k = lens_k;
+    if (dtype == 0) {
+        if (d == 64) return causal ? launch_general<Bf16, 64, true>(a, stream) : launch_general<Bf16, 64, false>(a, stream);
+        return causal ? launch_general<Bf16, 128, true>(a, stream) : launch_general<Bf16, 128, false>(a, stream);
+    }
+    if (d == 64) return causal ? launch_general<F16, 64, true>(a, stream) : launch_general<F16, 64, false>(a, stream);
+    return causal ? launch_general<F16, 128, true>(a, stream) : launch_general<F16, 128, false>(a, stream);
 }
 
 }  // namespace fa

@@ -52,6 +52,14 @@ hipError_t bwd128_fused_sparse(const void* q, const void* k, const void* v, cons
                                bool causal, int dtype, const uint64_t* mask_rows, const uint64_t* mask_cols, int W,
                                int64_t head_words, hipStream_t stream);
 
+// 16-bit forward over general shapes: element strides (batch, head, row) per
+// tensor, Nq queries and Nk keys (causal alignment at the end), optional
+// per-sequence lengths (device arrays of B ints, clamped to the extents).
+hipError_t fwd_general(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                       int d, float scale, bool causal, int dtype, const int64_t* sq, const int64_t* sk,
+                       const int64_t* sv, const int64_t* so, const int* lens_q, const int* lens_k,
+                       hipStream_t stream);
+
 // FP8 (e4m3) forward, d in {64, 128}: O in bf16, lse in fp32; the descale
 // factors turn the stored bytes into the real values.
 hipError_t fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,

@@ -123,15 +123,14 @@ def fwd(q, k, v, scale: float, causal: bool, block_mask=None, block: int = 128):
 
 def fwd_kv(q, k, v, scale: float, causal: bool):
     """Attention of Nq queries ([B,H,Nq,d]) over Nk cached keys and values ([B,H,Nk,d]),
-    the queries being the last Nq positions (causal: query t sees keys j <= t + Nk - Nq).
+    the queries being the last Nq positions (causal: query t sees keys j <= t + Nk - Nq; with
+    Nq > Nk the first Nq - Nk rows see none: O = 0, lse = -inf).
     Returns (O [B,H,Nq,d], lse [B,H,Nq])."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     if k.shape != (B, H, Nk, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B,H,Nk,d] with q's B, H and d")
-    if causal and Nq > Nk:
-        raise ValueError("causal attention over a cache needs Nq <= Nk")
     o = np.empty_like(q)
     lse = np.empty((B, H, Nq), dtype=np.float64)
     _load().oracle_fwd_kv(_ptr(q), _ptr(k), _ptr(v), B, H, Nq, Nk, d, float(scale), int(bool(causal)),

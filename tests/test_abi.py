@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_prep", "fa_bwd_main",
                           "fa_bwd_workspace_size", "fa_status_string", "fa_fwd_sparse", "fa_bwd_sparse",
                           "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size", "fa_fwd_fp8",
-                          "fa_decode", "fa_decode_workspace_size"}
+                          "fa_decode", "fa_decode_workspace_size", "fa_fwd_general"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -344,3 +344,32 @@ def dec(lib, B=2, H=3, Nq=1, Nk=1000, d=64, causal=1, dtype=0, ws=None, ws_bytes
 ])
 def test_decode_rejects(lib, kw, code):
     assert dec(lib, **kw) == code
+
+
+# ---------------------------------------------------------------- general shapes
+
+def gen(lib, B=2, H=3, Nq=100, Nk=200, d=64, causal=1, dtype=0, st=None, lens=(None, None), **over):
+    names = ["q", "k", "v", "o", "lse"]
+    p = dict(zip(names, ptrs(5)))
+    p.update({k: v for k, v in over.items() if k in names})
+    bshd = lambda n: fa._Strides(n * H * d, d, H * d)
+    ss = st or [bshd(Nq), bshd(Nk), bshd(Nk), bshd(Nq)]
+    return lib.fa_fwd_general(*[ctypes.c_void_p(p[n]) for n in names], B, H, Nq, Nk, d, ctypes.c_float(0.125),
+                              causal, dtype, *[ctypes.byref(x) for x in ss],
+                              *[ctypes.c_void_p(x) if x else None for x in lens], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(v=A + 2 * GAP + 8), fa.FA_ERR_INVALID_ARG),   # misaligned
+    (dict(st=[fa._Strides(0, 64, 4)] * 4), fa.FA_ERR_INVALID_ARG),            # row stride not a multiple of 8
+    (dict(st=[fa._Strides(19200, 64, 192), fa._Strides(38400, 64, 192), fa._Strides(38400, 64, 192),
+              fa._Strides(19200, 64, 32)]), fa.FA_ERR_INVALID_ARG),         # output rows overlap
+    (dict(o=A + GAP), fa.FA_ERR_INVALID_ARG),           # o overlaps k
+    (dict(lens=(A + 4 * GAP + 4, None)), fa.FA_ERR_INVALID_ARG),  # lengths overlap lse
+])
+def test_fwd_general_rejects(lib, kw, code):
+    assert gen(lib, **kw) == code

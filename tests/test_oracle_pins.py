@@ -477,3 +477,16 @@ def test_cache_matches_torch_cpu_fp64():
     np.testing.assert_allclose(o, to.numpy(), atol=1e-12)
     s = (scale * torch.tensor(q) @ torch.tensor(k).transpose(-1, -2)).masked_fill(~keep, float("-inf"))
     np.testing.assert_allclose(lse, torch.logsumexp(s, -1).numpy(), atol=1e-12)
+
+
+def test_cache_with_more_queries_than_keys():
+    """Causal with Nq > Nk: the first Nq - Nk queries see no key (O = 0, lse = -inf);
+    the others are the rows of a run on the last Nk queries."""
+    q = rnd(44, 0, (1, 2, 9, 4))
+    k, v = rnd(44, 1, (1, 2, 5, 4)), rnd(44, 2, (1, 2, 5, 4))
+    o, lse = oracle.fwd_kv(q, k, v, 0.5, True)
+    assert np.all(np.isneginf(lse[:, :, :4]))
+    np.testing.assert_array_equal(o[:, :, :4], 0.0)
+    o2, lse2 = oracle.fwd_kv(q[:, :, 4:], k, v, 0.5, True)
+    np.testing.assert_array_equal(o[:, :, 4:], o2)
+    np.testing.assert_array_equal(lse[:, :, 4:], lse2)
