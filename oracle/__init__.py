@@ -61,6 +61,9 @@ def _load():
                                    _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         lib.oracle_fwd_kv.argtypes = [_dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_double, ctypes.c_int, _dp, _dp]
+        lib.oracle_bwd_kv.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                                      _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         mask_args = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int64]
         lib.oracle_fwd_masked.argtypes = ([_dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_double, ctypes.c_int] + mask_args + [_dp, _dp])
@@ -175,4 +178,22 @@ def bwd(q, k, v, dout, scale: float, causal: bool, block_mask=None, block: int =
         m, nb, stride = _block_mask(block_mask, B, H, N, block)
         _load().oracle_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, N, d, float(scale),
                                   int(bool(causal)), m.ctypes.data, nb, block, stride, *outs)
+    return out
+
+
+def bwd_kv(q, k, v, dout, scale: float, causal: bool) -> dict:
+    """Forward plus analytic backward of ``L = sum(dout * O)`` for Nq queries ([B,H,Nq,d], the
+    last positions of the sequence) over Nk keys and values ([B,H,Nk,d]); causal alignment as
+    :func:`fwd_kv`. Returns the dict of :func:`bwd` (dq, D_* and lse over Nq rows, dk, dv over Nk)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError("k, v must be [B,H,Nk,d] and dout [B,H,Nq,d] with q's B, H and d")
+    out = {"o": np.empty_like(q), "dq": np.empty_like(q), "dk": np.empty_like(k), "dv": np.empty_like(k)}
+    for name in ("lse", "D_pdp", "D_odo"):
+        out[name] = np.empty((B, H, Nq), dtype=np.float64)
+    outs = [_ptr(out[n]) for n in ("o", "lse", "dq", "dk", "dv", "D_pdp", "D_odo")]
+    _load().oracle_bwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, Nq, Nk, d, float(scale),
+                          int(bool(causal)), *outs)
     return out

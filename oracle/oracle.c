@@ -202,36 +202,39 @@ void oracle_fwd_rows(const double* q, const double* k, const double* v, int B, i
 }
 
 /*
- * Forward and backward for every head.
- * Outputs: o, lse (as oracle_fwd), dq, dk, dv ([B,H,N,d]), D_pdp (sum_j P_ij dP_ij)
- * and D_odo (dO_i . O_i), both [B,H,N].
+ * Forward and backward for every head, Nq queries against Nk keys (q, o, dout,
+ * dq: [B,H,Nq,d]; k, v, dk, dv: [B,H,Nk,d]; lse, D_pdp, D_odo: [B,H,Nq]).
+ * Causal masking keeps j <= i + offset.
+ * Outputs: o, lse (as the forward), dq, dk, dv, D_pdp (sum_j P_ij dP_ij) and
+ * D_odo (dO_i . O_i).
  *
  * Pass 1 runs over query rows: P_i, O_i, lse_i, dP_i, D_i, dS_i and dQ_i.
  * Pass 2 runs over key columns: with lse_i and D_i of every row known, it forms
  * column j of P, dP and dS (P_ij = exp(S_ij - lse_i), the same value as pass 1's
  * exp(S_ij - m_i) / l_i) and sums dV_j and dK_j.
  */
-void oracle_bwd_masked(const double* q, const double* k, const double* v, const double* dout,
-                       int B, int H, int N, int d, double scale, int causal,
-                       const uint8_t* mask, int nb, int bs, int64_t mask_stride,
-                       double* o, double* lse, double* dq, double* dk, double* dv,
-                       double* D_pdp, double* D_odo)
+static void bwd_heads(const double* q, const double* k, const double* v, const double* dout,
+                      int B, int H, int Nq, int Nk, int d, double scale, int causal, int offset,
+                      const uint8_t* mask, int nb, int bs, int64_t mask_stride,
+                      double* o, double* lse, double* dq, double* dk, double* dv,
+                      double* D_pdp, double* D_odo)
 {
-    const int64_t rows = (int64_t)B * H * N;
+    const int64_t rows = (int64_t)B * H * Nq, cols = (int64_t)B * H * Nk;
 #pragma omp parallel
     {
-        double* p = (double*)malloc(sizeof(double) * (size_t)N);
-        double* dp = (double*)malloc(sizeof(double) * (size_t)N);
+        double* p = (double*)malloc(sizeof(double) * (size_t)Nk);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)Nk);
 #pragma omp for schedule(dynamic, 8)
         for (int64_t r = 0; r < rows; ++r) {
-            const int64_t bh = r / N;
-            const int i = (int)(r % N);
-            const size_t head = (size_t)bh * N * d;
-            const double *Q = q + head, *K = k + head, *V = v + head, *dO = dout + head;
-            const Visibility vis = head_visibility(causal, mask, nb, bs, mask_stride, bh);
-            forward_row(Q, K, V, N, d, scale, &vis, i, p, o + (size_t)r * d, lse + r);
+            const int64_t bh = r / Nq;
+            const int i = (int)(r % Nq);
+            const size_t qh = (size_t)bh * Nq * d, kh = (size_t)bh * Nk * d;
+            const double *Q = q + qh, *K = k + kh, *V = v + kh, *dO = dout + qh;
+            Visibility vis = head_visibility(causal, mask, nb, bs, mask_stride, bh);
+            vis.offset = offset;
+            forward_row(Q, K, V, Nk, d, scale, &vis, i, p, o + (size_t)r * d, lse + r);
             double Dp = 0.0;
-            for (int j = 0; j < N; ++j) {
+            for (int j = 0; j < Nk; ++j) {
                 if (!visible(&vis, i, j)) continue;
                 dp[j] = dot(dO + (size_t)i * d, V + (size_t)j * d, d);
                 Dp += p[j] * dp[j];
@@ -240,7 +243,7 @@ void oracle_bwd_masked(const double* q, const double* k, const double* v, const 
             D_odo[r] = dot(dO + (size_t)i * d, o + (size_t)r * d, d);
             double* dq_i = dq + (size_t)r * d;
             for (int c = 0; c < d; ++c) dq_i[c] = 0.0;
-            for (int j = 0; j < N; ++j) {
+            for (int j = 0; j < Nk; ++j) {
                 if (!visible(&vis, i, j)) continue;
                 const double ds = p[j] * (dp[j] - Dp);
                 for (int c = 0; c < d; ++c) dq_i[c] += ds * K[(size_t)j * d + c];
@@ -252,18 +255,19 @@ void oracle_bwd_masked(const double* q, const double* k, const double* v, const 
     }
     /* pass 2: one key column at a time */
 #pragma omp parallel for schedule(dynamic, 8)
-    for (int64_t r = 0; r < rows; ++r) {
-        const int64_t bh = r / N;
-        const int j = (int)(r % N);
-        const size_t head = (size_t)bh * N * d;
-        const double *Q = q + head, *K = k + head, *V = v + head, *dO = dout + head;
-        const double* lse_h = lse + (size_t)bh * N;
-        const double* D_h = D_pdp + (size_t)bh * N;
+    for (int64_t r = 0; r < cols; ++r) {
+        const int64_t bh = r / Nk;
+        const int j = (int)(r % Nk);
+        const size_t kh = (size_t)bh * Nk * d, qh = (size_t)bh * Nq * d;
+        const double *Q = q + qh, *K = k + kh, *V = v + kh, *dO = dout + qh;
+        const double* lse_h = lse + (size_t)bh * Nq;
+        const double* D_h = D_pdp + (size_t)bh * Nq;
         double* dk_j = dk + (size_t)r * d;
         double* dv_j = dv + (size_t)r * d;
         for (int c = 0; c < d; ++c) { dk_j[c] = 0.0; dv_j[c] = 0.0; }
-        const Visibility vis = head_visibility(causal, mask, nb, bs, mask_stride, bh);
-        for (int i = 0; i < N; ++i) {
+        Visibility vis = head_visibility(causal, mask, nb, bs, mask_stride, bh);
+        vis.offset = offset;   /* pass 2 */
+        for (int i = 0; i < Nq; ++i) {
             if (!visible(&vis, i, j)) continue;   /* query i does not attend to key j */
             const double pij = exp(scale * dot(Q + (size_t)i * d, K + (size_t)j * d, d) - lse_h[i]);
             const double dpij = dot(dO + (size_t)i * d, V + (size_t)j * d, d);
@@ -275,6 +279,30 @@ void oracle_bwd_masked(const double* q, const double* k, const double* v, const 
         }
         for (int c = 0; c < d; ++c) dk_j[c] *= scale;
     }
+}
+
+/* Forward and backward over N x N heads; mask NULL for dense attention. */
+void oracle_bwd_masked(const double* q, const double* k, const double* v, const double* dout,
+                       int B, int H, int N, int d, double scale, int causal,
+                       const uint8_t* mask, int nb, int bs, int64_t mask_stride,
+                       double* o, double* lse, double* dq, double* dk, double* dv,
+                       double* D_pdp, double* D_odo)
+{
+    bwd_heads(q, k, v, dout, B, H, N, N, d, scale, causal, 0, mask, nb, bs, mask_stride, o, lse, dq, dk, dv,
+              D_pdp, D_odo);
+}
+
+/*
+ * Forward and backward of Nq queries, the last positions of their sequence,
+ * over Nk keys (causal: query t sees keys j <= t + Nk - Nq, as oracle_fwd_kv).
+ */
+void oracle_bwd_kv(const double* q, const double* k, const double* v, const double* dout,
+                   int B, int H, int Nq, int Nk, int d, double scale, int causal,
+                   double* o, double* lse, double* dq, double* dk, double* dv,
+                   double* D_pdp, double* D_odo)
+{
+    bwd_heads(q, k, v, dout, B, H, Nq, Nk, d, scale, causal, Nk - Nq /* causal offset */, NULL, 0, 1, 0,
+              o, lse, dq, dk, dv, D_pdp, D_odo);
 }
 
 void oracle_bwd(const double* q, const double* k, const double* v, const double* dout,

@@ -54,6 +54,12 @@ MUTANTS = [
     ("cache_offset_off_by_one", "vis.offset = Nk - Nq;", "vis.offset = Nk - Nq - 1;"),
     ("cache_query_head_stride", "forward_row(q + (size_t)bh * Nq * d,", "forward_row(q + (size_t)bh * Nk * d,"),
     ("dS_uses_pass1_D_minus", "const double ds = pij * (dpij - D_h[i]);", "const double ds = pij * dpij;"),
+    # backward over Nq queries and Nk keys
+    ("bwd_kv_offset_dropped", "Nk - Nq /* causal offset */", "0 /* causal offset */"),
+    ("pass2_offset_dropped", "vis.offset = offset;   /* pass 2 */", ""),
+    ("pass2_query_head_stride", "kh = (size_t)bh * Nk * d, qh = (size_t)bh * Nq * d;",
+     "kh = (size_t)bh * Nk * d, qh = (size_t)bh * Nk * d;"),
+    ("pass2_lse_head_stride", "lse_h = lse + (size_t)bh * Nq;", "lse_h = lse + (size_t)bh * Nk;"),
 ]
 
 

@@ -490,3 +490,68 @@ def test_cache_with_more_queries_than_keys():
     o2, lse2 = oracle.fwd_kv(q[:, :, 4:], k, v, 0.5, True)
     np.testing.assert_array_equal(o[:, :, 4:], o2)
     np.testing.assert_array_equal(lse[:, :, 4:], lse2)
+
+
+# ---------------------------------------------------------------- backward over Nq queries and Nk keys
+# The same chain rule over the cache layout: the queries are the last Nq positions, so
+# causal masking keeps j <= i + Nk - Nq. Reading taken for general shapes (strided
+# layouts, padded batches): each sequence is this computation on its own rows.
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(3, 6), (6, 3)])
+def test_backward_kv_matches_finite_differences(causal, nq, nk):
+    """Central differences of L = sum(dO * O) through fwd_kv (pinned above), step 1e-5."""
+    scale, h = 0.6, 1e-5
+    q = rnd(45, 0, (1, 2, nq, 4))
+    k, v = rnd(45, 1, (1, 2, nk, 4)), rnd(45, 2, (1, 2, nk, 4))
+    do = rnd(45, 3, q.shape)
+    r = oracle.bwd_kv(q, k, v, do, scale, causal)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.fwd_kv(q_, k_, v_, scale, causal)
+        return float(np.sum(do * o))
+
+    for name, x, g in (("q", q, r["dq"]), ("k", k, r["dk"]), ("v", v, r["dv"])):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        err = np.linalg.norm(fd - g) / max(np.linalg.norm(g), 1e-300)
+        assert err <= 1e-7, f"d{name}: relative error {err}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_kv_is_the_dense_backward_with_silent_rows(causal):
+    """Prepend Nk - Nq arbitrary query rows with dO = 0: the dense N = Nk backward
+    (pinned by finite differences above) gives the same dK, dV and, on the last
+    rows, the same dQ (rows with dO = 0 have dP = 0 and D = 0, so dS = 0)."""
+    nq, nk = 5, 13
+    qf, k, v = qkv(46, 2, 2, nk, 8)
+    do = np.zeros_like(qf)
+    do[:, :, -nq:] = rnd(46, 3, (2, 2, nq, 8))
+    full = oracle.bwd(qf, k, v, do, 0.45, causal)
+    r = oracle.bwd_kv(qf[:, :, -nq:], k, v, do[:, :, -nq:], 0.45, causal)
+    np.testing.assert_allclose(r["dq"], full["dq"][:, :, -nq:], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r["dk"], full["dk"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r["dv"], full["dv"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(r["lse"], full["lse"][:, :, -nq:])
+
+
+def test_backward_kv_rows_without_keys_and_unseen_keys():
+    """Causal, Nq > Nk: the first Nq - Nk queries see no key and get dQ = 0; with Nq < Nk,
+    non-causal, every key is seen (dV sums to the sum of dO)."""
+    q = rnd(47, 0, (1, 2, 9, 4))
+    k, v = rnd(47, 1, (1, 2, 5, 4)), rnd(47, 2, (1, 2, 5, 4))
+    do = rnd(47, 3, q.shape)
+    r = oracle.bwd_kv(q, k, v, do, 0.5, True)
+    np.testing.assert_array_equal(r["dq"][:, :, :4], 0.0)
+    r2 = oracle.bwd_kv(q[:, :, 4:], k, v, do[:, :, 4:], 0.5, True)
+    for name in ("dk", "dv"):
+        np.testing.assert_allclose(r[name], r2[name], rtol=1e-13, atol=1e-14)
+    r3 = oracle.bwd_kv(q[:, :, :3], k, v, do[:, :, :3], 0.5, False)
+    np.testing.assert_allclose(r3["dv"].sum(2), do[:, :, :3].sum(2), atol=1e-12)
+    np.testing.assert_allclose(r3["dk"].sum(2), 0.0, atol=1e-12)
