@@ -27,6 +27,8 @@ import statistics
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -50,6 +52,10 @@ WORKLOADS = {
     # FP8 (e4m3) forward only, descale factors 1: the long causal shape
     "fp8_fwd_long_causal_16k": dict(B=1, H=16, N=16384, d=64, causal=True, dtype="fp8e4m3", seed=1007, mul=1.0,
                                     fwd_only=True),
+    # general shapes: the GPT-2-small causal batch stored [B,N,H,d] ("BSHD"), its eight
+    # sequences of seeded lengths uniform over [N/4, N] padded to N rows
+    "gpt2_varlen_bshd": dict(B=8, H=12, N=1024, d=64, causal=True, dtype="bf16", seed=1009, mul=1.0,
+                             general=dict(len_lo=256)),
 }
 
 # kernel names as rocprofv3 reports them, per stage of the default strategy
@@ -70,9 +76,9 @@ COPY_PROBE_KIB = 262144
 COUNTERS = {
     # workload: {stage: (FETCH_SIZE KiB, WRITE_SIZE KiB, copy FETCH_SIZE KiB, copy WRITE_SIZE KiB, sources sha)}
     "gpt2_small_causal": {
-        "fwd": (18536.3, 12672.0, 131089.1, 262144.0, "523496d11c4bb23a"),
-        "prep": (12493.3, 768.0, 131089.1, 262144.0, "cbc3cdc1c4827d5b"),
-        "main": (64237.4, 36864.0, 131089.1, 262144.0, "cbc3cdc1c4827d5b"),
+        "fwd": (18545.3, 12672.0, 131093.1, 262144.0, "67a35d39f0ef5702"),
+        "prep": (12492.9, 768.0, 131093.1, 262144.0, "1b1c1bd166e5f220"),
+        "main": (64145.5, 36864.0, 131093.1, 262144.0, "1b1c1bd166e5f220"),
     },
 }
 
@@ -292,6 +298,112 @@ def run_decode(args, w):
     print(json.dumps(out), flush=True)
 
 
+def varlen_lengths(w):
+    """The workload's seeded per-sequence lengths (queries = keys = L_b)."""
+    import seedgen
+    return seedgen.lengths(w["seed"], seedgen.TENSOR_LENS, w["B"], w["general"]["len_lo"], w["N"])
+
+
+def run_general(args, w):
+    """Bench line for general shapes: fa_fwd_general + fa_bwd_general over a padded
+    batch in [B,N,H,d] storage. Credited FLOP: 10*H*d per visible query-key pair of
+    each sequence, L_b^2 / 2 per head for causal (the dense rule applied per sequence)."""
+    import torch
+
+    import io_aware_tiled_07_amd as fa
+    import seedgen
+    B, H, N, d, causal = w["B"], w["H"], w["N"], w["d"], w["causal"]
+    scale, dev = 1.0 / math.sqrt(d), "cuda"
+    lens = varlen_lengths(w)
+    pair_rule = 0.5 if causal else 1.0
+    w["pairs"] = float(sum(int(L) ** 2 for L in lens) * pair_rule / B)  # mean per head, for flops()
+    store = (B, N, H, d)
+    q, k, v, do = (seedgen.draw(w["seed"], t, store, w["dtype"], want_f64=False).torch(dev).transpose(1, 2)
+                   for t in range(4))
+    o, dq, dk, dv = (torch.empty(store, dtype=q.dtype, device=dev).transpose(1, 2) for _ in range(4))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    sl = torch.from_numpy(lens).to(dev)
+    ws = torch.empty(fa.fa_bwd_general_workspace_size(B, H, N), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    stages = ("fwd", "main")
+
+    def run(evs=None):
+        evs = evs or {}
+        for name in stages:
+            if name in evs: evs[name][0].record(stream)
+            if name == "fwd":
+                fa.fa_fwd_general(q, k, v, o, lse, causal, scale, sl, sl, stream)
+            else:
+                fa.fa_bwd_general(q, k, v, o, do, lse, dq, dk, dv, causal, scale, sl, sl, ws, stream)
+            if name in evs: evs[name][1].record(stream)
+
+    def ev_pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    K = args.steps
+    brk = [{name: ev_pair() for name in stages} for _ in range(K)]
+    for i in range(K):
+        run(brk[i])
+    torch.cuda.synchronize()
+    stage_ms = {name: statistics.mean(e[name][0].elapsed_time(e[name][1]) for e in brk) for name in stages}
+    dom_ev = [{"main": ev_pair()} for _ in range(K)]
+    t_start, t_end = ev_pair()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        run(dom_ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / K
+    dom_ms = statistics.mean(e["main"][0].elapsed_time(e["main"][1]) for e in dom_ev)
+    tf_step = flops(w, "step") / (ms_step * 1e-3) / 1e12
+    dom_tf = flops(w, "bwd") / (dom_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        full = [seedgen.draw(w["seed"], t, store, w["dtype"]).f64.transpose(0, 2, 1, 3) for t in range(4)]
+        reps, t_total, credited, b = 0, 0.0, 0.0, 0
+        while t_total < 10.0 and reps < 1000:
+            L = int(lens[b % B])
+            xs = [np.ascontiguousarray(x[b % B:b % B + 1, :, :L]) for x in full]
+            a = time.perf_counter()
+            oracle.bwd_kv(*xs, scale, causal)
+            t_total += time.perf_counter() - a
+            credited += 10 * H * d * L * L * pair_rule
+            reps += 1
+            b += 1
+        cpu = {"value": round(credited / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "cpu_model": cpu_model(),
+               "sample": f"fwd+bwd of the fp64 oracle over {reps} sequence(s) of the same batch (all heads each), "
+                         f"{t_total:.2f} s; credited with the same rule as the GPU"}
+    out = {
+        "metric": "attention TFLOP/s fwd+bwd over a padded batch (10*H*d per visible pair, L_b^2/2 per head causal)",
+        "value": round(tf_step, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic: seeded i.i.d. N(0,1) inputs stored [B,N,H,d], seeded lengths uniform over [N/4, N]",
+        "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "causal": causal, "dtype": w["dtype"],
+                   "scale": scale, "layout": "BSHD", "lengths": lens.tolist()},
+        "fwd": {"ms": round(stage_ms["fwd"], 5),
+                "tflops": round(flops(w, "fwd") / (stage_ms["fwd"] * 1e-3) / 1e12, 3)},
+        "bwd": {"ms": round(stage_ms["main"], 5),
+                "tflops_10x": round(flops(w, "bwd") / (stage_ms["main"] * 1e-3) / 1e12, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(dom_tf, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(dom_tf / peak, 4), "traffic": None, "algorithmic_bytes": None,
+                     "kernel": "fa_bwd_general: bwd_prep_kernel (general) + bwd_fused_kernel (general)",
+                     "flop_per_launch": flops(w, "bwd"), "avg_launch_ms": round(dom_ms, 5),
+                     "flop_rule": "bwd 10*H*d per visible query-key pair of each sequence"},
+        "cpu_baseline": cpu, "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +433,9 @@ def main():
     w = dict(WORKLOADS[args.workload])
     if "decode" in w:
         run_decode(args, w)
+        return
+    if "general" in w:
+        run_general(args, w)
         return
     mask_np = block_mask(w)
     sparse = mask_np is not None

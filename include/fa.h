@@ -211,7 +211,8 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
  * storage, "BSHD", seen as [B,H,N,d]), Nq queries against Nk keys, and
  * sequences of different lengths padded into one batch.
  *   fa_strides      : element strides of a [B,H,N,d] view (the head-dim stride is 1);
- *                     every stride >= 0 and a multiple of 8, each view's base 16-byte aligned.
+ *                     every stride >= 0 and a multiple of 8, the row stride below 2^23,
+ *                     each view's base 16-byte aligned.
  *   q, o            : Nq rows per (batch, head); k, v: Nk rows.
  *   lse             : [B,H,Nq] fp32, contiguous.
  *   seqlens_q/_k    : NULL, or device arrays of B ints: sequence b has seqlens_q[b]
@@ -232,6 +233,37 @@ int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* 
                    const fa_strides* q_strides, const fa_strides* k_strides,
                    const fa_strides* v_strides, const fa_strides* o_strides,
                    const int* seqlens_q, const int* seqlens_k, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd_general needs: D_i = dO_i . O_i and
+ * lse_i * log2(e), [B,H,Nq] float each, each part rounded up to 256 bytes.
+ * Returns 0 for invalid shapes.
+ */
+size_t fa_bwd_general_workspace_size(int B, int H, int Nq);
+
+/*
+ * Backward over the general shapes of fa_fwd_general (recomputation from lse as
+ * in fa_bwd): strided q, k, v, o, dout, dq, dk, dv views, Nq queries against Nk
+ * keys, per-sequence lengths, causal alignment at the end.
+ *   q, o, dout, dq  : Nq rows per (batch, head); k, v, dk, dv: Nk rows.
+ *   lse             : [B,H,Nq] fp32, contiguous, as fa_fwd_general wrote it.
+ *   seqlens_q/_k    : as fa_fwd_general. Rows of dq past a sequence's queries and
+ *                     rows of dk, dv past its keys are neither computed nor written;
+ *                     a key that no query sees gets dK = dV = 0.
+ *   workspace       : caller-owned, 256-byte aligned, at least
+ *                     fa_bwd_general_workspace_size() bytes.
+ * dtype bf16/fp16, d in {64, 128}. Errors as fa_fwd_general (outputs that overlap
+ * each other, an input or the workspace -> FA_ERR_INVALID_ARG). Returns a fa_status.
+ */
+int fa_bwd_general(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                   const fa_strides* q_strides, const fa_strides* k_strides,
+                   const fa_strides* v_strides, const fa_strides* o_strides,
+                   const fa_strides* dout_strides, const fa_strides* dq_strides,
+                   const fa_strides* dk_strides, const fa_strides* dv_strides,
+                   const int* seqlens_q, const int* seqlens_k,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a fa_status value. Never NULL. */
 const char* fa_status_string(int status);

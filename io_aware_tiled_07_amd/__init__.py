@@ -9,10 +9,10 @@ The raw entry points keep the C names (``fa_fwd``, ``fa_bwd``, ``fa_bwd_dq``,
 ``fa_bwd_prep``, ``fa_bwd_main``, ``fa_bwd_workspace_size``, ``fa_status_string``,
 for block-sparse attention ``fa_fwd_sparse``, ``fa_bwd_sparse`` and their
 workspace sizes, the FP8 forward ``fa_fwd_fp8``, and attention over a key/value
-cache ``fa_decode`` with ``fa_decode_workspace_size``, and the forward over
-general shapes ``fa_fwd_general``) and take caller-allocated torch tensors;
-``fwd``, ``bwd``, ``fwd_sparse``, ``bwd_sparse``, ``fwd_fp8``, ``decode`` and
-``fwd_general`` allocate their outputs.
+cache ``fa_decode`` with ``fa_decode_workspace_size``, and the forward and
+backward over general shapes ``fa_fwd_general``, ``fa_bwd_general``) and take caller-allocated
+torch tensors; ``fwd``, ``bwd``, ``fwd_sparse``, ``bwd_sparse``, ``fwd_fp8``,
+``decode``, ``fwd_general`` and ``bwd_general`` allocate their outputs.
 """
 from __future__ import annotations
 
@@ -28,6 +28,7 @@ __all__ = [
     "FA_SPARSE_BLOCK", "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size", "fa_fwd_sparse",
     "fa_bwd_sparse", "fwd_sparse", "bwd_sparse", "fa_fwd_fp8", "fwd_fp8", "fa_decode_workspace_size",
     "fa_decode", "decode", "fa_fwd_general", "fwd_general",
+    "fa_bwd_general_workspace_size", "fa_bwd_general", "bwd_general",
 ]
 
 FA_BF16, FA_FP16, FA_FP32 = 0, 1, 2
@@ -90,6 +91,12 @@ def load():
         lib.fa_decode.restype = _i
         lib.fa_fwd_general.argtypes = [_vp] * 5 + [_i, _i, _i, _i, _i, _f, _i, _i] + [_vp] * 7
         lib.fa_fwd_general.restype = _i
+        lib.fa_bwd_general_workspace_size.argtypes = [_i, _i, _i]
+        lib.fa_bwd_general_workspace_size.restype = ctypes.c_size_t
+        # 9 tensors, 8 scalars, 8 stride structs, 2 length arrays, workspace, bytes, stream
+        lib.fa_bwd_general.argtypes = [_vp] * 9 + [_i, _i, _i, _i, _i, _f, _i, _i] + [_vp] * 11 + [ctypes.c_size_t,
+                                                                                               _vp]
+        lib.fa_bwd_general.restype = _i
         _lib = lib
     return _lib
 
@@ -397,6 +404,19 @@ def _strides(t):
     return _Strides(t.stride(0), t.stride(1), t.stride(2))
 
 
+def _seqlens(B, seqlens_q, seqlens_k):
+    """Device pointers (or None) of the optional per-sequence lengths."""
+    import torch
+    lens = []
+    for name, t in (("seqlens_q", seqlens_q), ("seqlens_k", seqlens_k)):
+        if t is None:
+            lens.append(None)
+        else:
+            _check_bhnd(name, t, (B,), torch.int32)
+            lens.append(t.data_ptr())
+    return lens
+
+
 def fa_fwd_general(q, k, v, o, lse, causal: bool = False, scale=None, seqlens_q=None, seqlens_k=None,
                    stream=None) -> None:
     """Forward over general shapes: q, o are [B,H,Nq,d] views and k, v [B,H,Nk,d] views with any
@@ -409,13 +429,7 @@ def fa_fwd_general(q, k, v, o, lse, causal: bool = False, scale=None, seqlens_q=
         if not t.is_cuda or tuple(t.shape) != (B, H, n, d) or t.dtype != q.dtype:
             raise ValueError(f"{name} must be a device tensor [B,H,{n},d] of q's dtype")
     _check_bhnd("lse", lse, (B, H, Nq), torch.float32)
-    lens = []
-    for name, t in (("seqlens_q", seqlens_q), ("seqlens_k", seqlens_k)):
-        if t is None:
-            lens.append(None)
-        else:
-            _check_bhnd(name, t, (B,), torch.int32)
-            lens.append(t.data_ptr())
+    lens = _seqlens(B, seqlens_q, seqlens_k)
     ss = [_strides(t) for t in (q, k, v, o)]
     st = load().fa_fwd_general(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq,
                                Nk, d, _scale(scale, d), int(bool(causal)), dtype_code(q),
@@ -432,3 +446,42 @@ def fwd_general(q, k, v, causal: bool = False, scale=None, seqlens_q=None, seqle
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     fa_fwd_general(q, k, v, o, lse, causal, scale, seqlens_q, seqlens_k, stream)
     return o, lse
+
+
+def fa_bwd_general_workspace_size(B: int, H: int, Nq: int) -> int:
+    return int(load().fa_bwd_general_workspace_size(B, H, Nq))
+
+
+def fa_bwd_general(q, k, v, o, do, lse, dq, dk, dv, causal: bool = False, scale=None, seqlens_q=None,
+                   seqlens_k=None, workspace=None, stream=None) -> None:
+    """Backward over general shapes into caller-allocated dq, dk, dv (views of any strides with a
+    contiguous last dimension; dq like q, dk / dv like k): the arguments of fa_fwd_general plus o,
+    do (dL/dO, like o) and lse as that forward wrote them."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for name, t, n in (("q", q, Nq), ("k", k, Nk), ("v", v, Nk), ("o", o, Nq), ("do", do, Nq), ("dq", dq, Nq),
+                       ("dk", dk, Nk), ("dv", dv, Nk)):
+        if not t.is_cuda or tuple(t.shape) != (B, H, n, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a device tensor [B,H,{n},d] of q's dtype")
+    _check_bhnd("lse", lse, (B, H, Nq), torch.float32)
+    lens = _seqlens(B, seqlens_q, seqlens_k)
+    ss = [_strides(t) for t in (q, k, v, o, do, dq, dk, dv)]
+    workspace, wbytes = _workspace(q, fa_bwd_general_workspace_size(B, H, Nq), workspace)
+    st = load().fa_bwd_general(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                               lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d,
+                               _scale(scale, d), int(bool(causal)), dtype_code(q),
+                               *[ctypes.byref(x) for x in ss], lens[0], lens[1], workspace.data_ptr(), wbytes,
+                               _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_general")
+
+
+def bwd_general(q, k, v, o, do, lse, causal: bool = False, scale=None, seqlens_q=None, seqlens_k=None,
+                workspace=None, stream=None):
+    """Allocate dQ, dK, dV (each in its input's layout) and run the general-shape backward.
+    Returns (dq, dk, dv)."""
+    import torch
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa_bwd_general(q, k, v, o, do, lse, dq, dk, dv, causal, scale, seqlens_q, seqlens_k, workspace, stream)
+    return dq, dk, dv

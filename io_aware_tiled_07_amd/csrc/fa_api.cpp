@@ -165,9 +165,11 @@ DecodeLayout decode_layout(int B, int H, int Nq, int Nk, int d) {
 // ---------------------------------------------------------------- general shapes
 // A strided [B,H,N,d] view is valid when its strides are non-negative multiples
 // of 8 elements (16 bytes) and its base is 16-byte aligned.
+// The row stride stays below 2^23 elements: a 128-row tile then spans under
+// 2 GiB, inside one buffer resource and a 32-bit lane offset.
 bool strides_ok(const fa_strides* s) {
     return s != nullptr && s->batch >= 0 && s->head >= 0 && s->row >= 0 && s->batch % 8 == 0 && s->head % 8 == 0 &&
-           s->row % 8 == 0;
+           s->row % 8 == 0 && s->row < (1LL << 23);
 }
 // Byte span of a strided view (first byte to one past the last).
 Range view_range(const void* p, const fa_strides* s, int B, int H, int N, int d, int elt) {
@@ -495,6 +497,80 @@ int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* 
     (void)hipGetLastError();
     const hipError_t e = fa::fwd_general(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype, sq, sk, sv, so,
                                          seqlens_q, seqlens_k, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_general_workspace_size(int B, int H, int Nq) {
+    if (B < 1 || H < 1 || Nq < 1) return 0;
+    return 2 * round_up((size_t)B * H * Nq * sizeof(float), 256);
+}
+
+int fa_bwd_general(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                   int dtype, const fa_strides* q_strides, const fa_strides* k_strides, const fa_strides* v_strides,
+                   const fa_strides* o_strides, const fa_strides* dout_strides, const fa_strides* dq_strides,
+                   const fa_strides* dk_strides, const fa_strides* dv_strides, const int* seqlens_q,
+                   const int* seqlens_k, void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+    const int64_t bh = (int64_t)B * H;
+    const int64_t nblk = ((int64_t)(Nq > Nk ? Nq : Nk) + 127) / 128;
+    if ((int64_t)Nq > kMaxN || (int64_t)Nk > kMaxN || bh * 2 * nblk > kMaxGrid) return FA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+    for (const void* p : ptrs)
+        if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
+    const fa_strides* ss[] = {q_strides,    k_strides,  v_strides,  o_strides,
+                              dout_strides, dq_strides, dk_strides, dv_strides};
+    for (const fa_strides* x : ss)
+        if (!strides_ok(x)) return FA_ERR_INVALID_ARG;
+    if (!view_disjoint(dq_strides, B, H, Nq, d) || !view_disjoint(dk_strides, B, H, Nk, d) ||
+        !view_disjoint(dv_strides, B, H, Nk, d))
+        return FA_ERR_INVALID_ARG;
+    if (((uintptr_t)seqlens_q & 3u) != 0 || ((uintptr_t)seqlens_k & 3u) != 0) return FA_ERR_INVALID_ARG;
+    const size_t need = fa_bwd_general_workspace_size(B, H, Nq);
+    if (workspace == nullptr || !aligned256(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    const Range outs[] = {view_range(dq, dq_strides, B, H, Nq, d, 2), view_range(dk, dk_strides, B, H, Nk, d, 2),
+                          view_range(dv, dv_strides, B, H, Nk, d, 2), range(workspace, need)};
+    const Range ins[] = {view_range(q, q_strides, B, H, Nq, d, 2),
+                         view_range(k, k_strides, B, H, Nk, d, 2),
+                         view_range(v, v_strides, B, H, Nk, d, 2),
+                         view_range(o, o_strides, B, H, Nq, d, 2),
+                         view_range(dout, dout_strides, B, H, Nq, d, 2),
+                         range(lse, (size_t)bh * Nq * sizeof(float)),
+                         seqlens_q ? range(seqlens_q, (size_t)B * sizeof(int)) : Range{0, 0},
+                         seqlens_k ? range(seqlens_k, (size_t)B * sizeof(int)) : Range{0, 0}};
+    for (int i = 0; i < 4; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return FA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
+    }
+    auto as3 = [](const fa_strides* x, int64_t* t) {
+        t[0] = x->batch;
+        t[1] = x->head;
+        t[2] = x->row;
+    };
+    int64_t so[3], st[7][3];
+    as3(o_strides, so);
+    const fa_strides* order[7] = {q_strides, k_strides, v_strides, dout_strides, dq_strides, dk_strides, dv_strides};
+    for (int t = 0; t < 7; ++t) as3(order[t], st[t]);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* base = static_cast<char*>(workspace);
+    float* delta = reinterpret_cast<float*>(base);
+    float* lse2 = reinterpret_cast<float*>(base + need / 2);
+    (void)hipGetLastError();
+    hipError_t e = fa::bwd_prep_general(o, dout, lse, B, H, Nq, d, dtype, so, st[3], seqlens_q, delta, lse2, s);
+    if (e == hipSuccess) {
+        if (d == 128)
+            e = fa::bwd128_fused_general(q, k, v, dout, delta, lse2, dq, dk, dv, B, H, Nq, Nk, scale, causal != 0,
+                                         dtype, st, seqlens_q, seqlens_k, s);
+        else
+            e = fa::bwd_fused_general(q, k, v, dout, delta, lse2, dq, dk, dv, B, H, Nq, Nk, scale, causal != 0, dtype,
+                                      st, seqlens_q, seqlens_k, s);
+    }
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -128,6 +128,13 @@ struct FusedArgs {
     const uint64_t* mask_cols;
     int W, nb;
     int64_t head_words;
+    // general shapes: element strides (batch, head, row) of q, k, v, dout, dq,
+    // dk, dv (in that order); N is the query extent, Nk the key extent;
+    // per-sequence lengths (nullptr: the extents); causal alignment at the end
+    int64_t st[7][3];
+    int H, Nk;
+    const int* lens_q;
+    const int* lens_k;
 };
 
 struct PrepArgs {
@@ -137,6 +144,11 @@ struct PrepArgs {
     float* delta;  // receives -D
     float* lse2;
     int64_t rows;
+    // general shapes: element strides (batch, head, row) of o and dout, heads,
+    // query extent, per-sequence query lengths (nullptr: the extent)
+    int64_t so[3], sd[3];
+    int H, N;
+    const int* lens_q;
 };
 
 // ---------------------------------------------------------------- 1. prep
@@ -148,19 +160,31 @@ constexpr int kPrepRounds = 1;
 template <int PD>
 constexpr int kPrepRows = kPrepRounds * kThreads / (PD / 8);
 
-template <typename T, int PD>
+template <typename T, int PD, bool GEN = false>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(PrepArgs a) {
     constexpr int LPR = PD / 8;
     constexpr int RPR = kThreads / LPR;  // rows per round
     const int tid = threadIdx.x, part = tid % LPR;
     const int64_t row0 = (int64_t)blockIdx.x * kPrepRows<PD> + tid / LPR;
     u32x4 ov[kPrepRounds], dv[kPrepRounds];
+    bool live[kPrepRounds];  // general shapes: the row belongs to its sequence
 #pragma unroll
     for (int k = 0; k < kPrepRounds; ++k) {
         const int64_t row = row0 + k * RPR;
         const int64_t r = row < a.rows ? row : a.rows - 1;
-        ov[k] = *reinterpret_cast<const u32x4*>(a.o + r * PD + part * 8);
-        dv[k] = *reinterpret_cast<const u32x4*>(a.dout + r * PD + part * 8);
+        if constexpr (GEN) {
+            const int64_t bh = r / a.N, i = r % a.N;
+            const int64_t b = bh / a.H, hh = bh % a.H;
+            const int nq = a.lens_q ? min(max(a.lens_q[b], 0), a.N) : a.N;
+            live[k] = row < a.rows && i < nq;
+            const int64_t ii = i < nq ? i : 0;
+            ov[k] = *reinterpret_cast<const u32x4*>(a.o + b * a.so[0] + hh * a.so[1] + ii * a.so[2] + part * 8);
+            dv[k] = *reinterpret_cast<const u32x4*>(a.dout + b * a.sd[0] + hh * a.sd[1] + ii * a.sd[2] + part * 8);
+        } else {
+            live[k] = row < a.rows;
+            ov[k] = *reinterpret_cast<const u32x4*>(a.o + r * PD + part * 8);
+            dv[k] = *reinterpret_cast<const u32x4*>(a.dout + r * PD + part * 8);
+        }
     }
 #pragma unroll
     for (int k = 0; k < kPrepRounds; ++k) {
@@ -173,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(PrepArgs a) {
 #pragma unroll
         for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
         const int64_t row = row0 + k * RPR;
-        if (row < a.rows) {
+        if (live[k]) {
             if (part == 0) a.delta[row] = -acc;  // stored negated: the initial dP accumulator
             if (part == 1) a.lse2[row] = a.lse[row] * kLog2e;
         }
@@ -200,7 +224,7 @@ __device__ __forceinline__ void map_fused(int bid, const FusedArgs& a, bool caus
 }
 
 // Key workgroup: dK and dV of 128 keys.
-template <typename T, bool CAUSAL, bool SPARSE>
+template <typename T, bool CAUSAL, bool SPARSE, bool GEN = false>
 __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
@@ -210,6 +234,33 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     const uint16_t* __restrict__ dO = a.dout + head;
     const float* __restrict__ lse2 = a.lse2 + (size_t)bh * N;
     const float* __restrict__ delta = a.delta + (size_t)bh * N;
+    // general shapes: this sequence's lengths, offset, bases and row strides (elements)
+    int nq = N, nk = N, off = 0;
+    int64_t q_rs = D, do_rs = D, k_rs = D, v_rs = D, dk_rs = D, dv_rs = D;
+    const uint16_t* Kb = a.k + head;
+    const uint16_t* Vb = a.v + head;
+    uint16_t* dKb = a.dk + head;
+    uint16_t* dVb = a.dv + head;
+    if constexpr (GEN) {
+        const int b = bh / a.H, hh = bh % a.H;
+        const SeqShape ss = seq_shape(a.lens_q, a.lens_k, b, N, a.Nk);
+        nq = ss.nq;
+        nk = ss.nk;
+        off = ss.off;
+        if (kb * kKvKeys >= nk) return;  // the whole workgroup: past this sequence's keys
+        Q = a.q + b * a.st[0][0] + hh * a.st[0][1];
+        Kb = a.k + b * a.st[1][0] + hh * a.st[1][1];
+        Vb = a.v + b * a.st[2][0] + hh * a.st[2][1];
+        dO = a.dout + b * a.st[3][0] + hh * a.st[3][1];
+        dKb = a.dk + b * a.st[5][0] + hh * a.st[5][1];
+        dVb = a.dv + b * a.st[6][0] + hh * a.st[6][1];
+        q_rs = a.st[0][2];
+        k_rs = a.st[1][2];
+        v_rs = a.st[2][2];
+        do_rs = a.st[3][2];
+        dk_rs = a.st[5][2];
+        dv_rs = a.st[6][2];
+    }
 
     const int kw0 = kb * kKvKeys + wave * 32;  // first key of this wave
     const int key = kw0 + l32;                 // key of this lane (and of lane ^ 32)
@@ -217,8 +268,9 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
 #pragma unroll
     for (int u = 0; u < DT; ++u) { dk[u] = f32x16{}; dv[u] = f32x16{}; }
 
-    const int ng = (N + kKvQRows - 1) / kKvQRows;          // query stages
-    const int g0 = CAUSAL ? (kb * kKvKeys) / kKvQRows : 0;  // first stage touching these keys
+    const int ng = (nq + kKvQRows - 1) / kKvQRows;          // query stages
+    // first stage touching these keys (causal: query rows >= first key - off)
+    const int g0 = CAUSAL ? (GEN ? max(0, kb * kKvKeys - off) : kb * kKvKeys) / kKvQRows : 0;
     // block-sparse: the 64-row halves of the kept query blocks of mask column kb
     static_assert(!SPARSE || kKvKeys == kSparseBlock, "a key workgroup covers one block column of the mask");
     BlockWalk walk;
@@ -227,7 +279,7 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         walk.init(a.mask_cols + (size_t)bh * a.head_words + (size_t)kb * a.W, CAUSAL ? kb : 0, ng);
         nst = walk.count(CAUSAL ? kb : 0, a.nb - 1);
     } else {
-        nst = ng - g0;
+        nst = GEN ? max(0, ng - g0) : ng - g0;
     }
     int slot_unit[kSlots];  // query stage (64 rows) held by each ring slot
 
@@ -237,24 +289,39 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     // 8 (c % kKvTC) + l / 8, stored chunk l % 8; the same lane offsets serve Q
     // and dO. Waves 0 and 1 also copy the statistics.
     uint32_t dma_off[kKvTC / 4];
+    uint32_t dma_off_d[GEN ? kKvTC / 4 : 1];  // dO rows when strided differently from Q
 #pragma unroll
     for (int j = 0; j < kKvTC / 4; ++j) {
         const int p = (j * 4 + wave) * 64 + lane;
         const int row = p / CH, c = (p % CH) ^ swz<D>(row);
-        dma_off[j] = (uint32_t)((row * D + c * 8) * 2);
+        if constexpr (GEN) {
+            dma_off[j] = (uint32_t)(row * q_rs * 2) + c * 16;
+            dma_off_d[j] = (uint32_t)(row * do_rs * 2) + c * 16;
+        } else {
+            dma_off[j] = (uint32_t)((row * D + c * 8) * 2);
+        }
     }
     auto issue = [&](int s, int slot) {
         const int g = SPARSE ? walk.next() : g0 + s;
         slot_unit[slot] = g;
         const int r0 = g * kKvQRows;
-        const i32x4 qr = rows_rsrc<kRowB>(Q, N, r0), dr = rows_rsrc<kRowB>(dO, N, r0);
         char* sb = smem + slot * kKvStage + kKvRowsOff + wave * 1024;
+        if constexpr (GEN) {
+            const i32x4 qr = strided_rows_rsrc<kRowB>(Q, nq, r0, (uint32_t)(q_rs * 2));
+            const i32x4 dr = strided_rows_rsrc<kRowB>(dO, nq, r0, (uint32_t)(do_rs * 2));
 #pragma unroll
-        for (int j = 0; j < kKvTC / 4; ++j) dma16(qr, dma_off[j], sb + j * 4 * 1024);
+            for (int j = 0; j < kKvTC / 4; ++j) dma16(qr, dma_off[j], sb + j * 4 * 1024);
 #pragma unroll
-        for (int j = 0; j < kKvTC / 4; ++j) dma16(dr, dma_off[j], sb + kKvTileB + j * 4 * 1024);
+            for (int j = 0; j < kKvTC / 4; ++j) dma16(dr, dma_off_d[j], sb + kKvTileB + j * 4 * 1024);
+        } else {
+            const i32x4 qr = rows_rsrc<kRowB>(Q, N, r0), dr = rows_rsrc<kRowB>(dO, N, r0);
+#pragma unroll
+            for (int j = 0; j < kKvTC / 4; ++j) dma16(qr, dma_off[j], sb + j * 4 * 1024);
+#pragma unroll
+            for (int j = 0; j < kKvTC / 4; ++j) dma16(dr, dma_off[j], sb + kKvTileB + j * 4 * 1024);
+        }
         if (wave < 2)
-            dma4(rows_rsrc<4>(wave == 0 ? lse2 : delta, N, r0), (uint32_t)lane * 4,
+            dma4(rows_rsrc<4>(wave == 0 ? lse2 : delta, nq, r0), (uint32_t)lane * 4,
                  smem + slot * kKvStage + wave * kKvStatB);
     };
 
@@ -285,11 +352,22 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     // loop (else it drains the ring there).
     u32x4 kf[KS], vf[KS];
     {
-        const size_t kr = head + (size_t)min(key, N - 1) * D + 8 * h;
+        if constexpr (GEN) {
+            const int krow = min(key, nk - 1);
+            const uint16_t* kp = Kb + (size_t)krow * k_rs + 8 * h;
+            const uint16_t* vp = Vb + (size_t)krow * v_rs + 8 * h;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            kf[ks] = *reinterpret_cast<const u32x4*>(a.k + kr + 16 * ks);
-            vf[ks] = *reinterpret_cast<const u32x4*>(a.v + kr + 16 * ks);
+            for (int ks = 0; ks < KS; ++ks) {
+                kf[ks] = *reinterpret_cast<const u32x4*>(kp + 16 * ks);
+                vf[ks] = *reinterpret_cast<const u32x4*>(vp + 16 * ks);
+            }
+        } else {
+            const size_t kr = head + (size_t)min(key, N - 1) * D + 8 * h;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                kf[ks] = *reinterpret_cast<const u32x4*>(a.k + kr + 16 * ks);
+                vf[ks] = *reinterpret_cast<const u32x4*>(a.v + kr + 16 * ks);
+            }
         }
     }
 #pragma unroll
@@ -378,8 +456,8 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
             auto elementwise = [&](auto mask_c) {
                 // mask bounds relative to the lane's first query qt0 + 8h; keys past
                 // the end see no query
-                const int dlim = key - qt0 - 8 * h;
-                const int nlim = key < N ? N - qt0 - 8 * h : -1;
+                const int dlim = GEN ? key - off - qt0 - 8 * h : key - qt0 - 8 * h;
+                const int nlim = GEN ? (key < nk ? nq - qt0 - 8 * h : -1) : (key < N ? N - qt0 - 8 * h : -1);
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     float p[2], ds[2];
@@ -435,9 +513,9 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         const int g = SPARSE ? slot_unit[SLOT] : g0 + s;
         auto half = [&](auto hh_c) {
             const int qt0 = g * kKvQRows + 32 * decltype(hh_c)::value;
-            const bool active = kw0 < N && qt0 < N && (!CAUSAL || qt0 + 31 >= kw0);
+            const bool active = GEN ? kw0 < nk && qt0 < nq && (!CAUSAL || qt0 + 31 + off >= kw0) : kw0 < N && qt0 < N && (!CAUSAL || qt0 + 31 >= kw0);
             if (!active) return;
-            const bool need_mask = (CAUSAL && kw0 + 31 > qt0) || kw0 + 32 > N || qt0 + 32 > N;
+            const bool need_mask = GEN ? (CAUSAL && kw0 + 31 > qt0 + off) || kw0 + 32 > nk || qt0 + 32 > nq : (CAUSAL && kw0 + 31 > qt0) || kw0 + 32 > N || qt0 + 32 > N;
             unit(slot_c, hh_c, need_mask, qt0);
         };
         half(Int<0>{});
@@ -448,13 +526,18 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     // last stage's barrier retired every earlier stage; nothing is in flight)
     {
         char* stage = smem + (nst % kSlots) * kKvStage + wave * (2048 * DT);
-        store_rows<T, DT>(dk, a.scale, a.dk + head + (size_t)kw0 * D, D, N - kw0, stage);
-        store_rows<T, DT>(dv, 1.f, a.dv + head + (size_t)kw0 * D, D, N - kw0, stage);
+        if constexpr (GEN) {
+            store_rows<T, DT>(dk, a.scale, dKb + (size_t)kw0 * dk_rs, (int)dk_rs, nk - kw0, stage);
+            store_rows<T, DT>(dv, 1.f, dVb + (size_t)kw0 * dv_rs, (int)dv_rs, nk - kw0, stage);
+        } else {
+            store_rows<T, DT>(dk, a.scale, a.dk + head + (size_t)kw0 * D, D, N - kw0, stage);
+            store_rows<T, DT>(dv, 1.f, a.dv + head + (size_t)kw0 * D, D, N - kw0, stage);
+        }
     }
 }
 
 // Query workgroup: dQ of 128 queries.
-template <typename T, bool CAUSAL, bool SPARSE>
+template <typename T, bool CAUSAL, bool SPARSE, bool GEN = false>
 __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
@@ -462,13 +545,37 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
     const size_t head = (size_t)bh * N * D;
     const uint16_t* __restrict__ K = a.k + head;
     const uint16_t* __restrict__ V = a.v + head;
+    // general shapes: this sequence's lengths, offset, bases and row strides (elements)
+    int nq = N, nk = N, off = 0;
+    int64_t q_rs = D, do_rs = D, k_rs = D, v_rs = D, dq_rs = D;
+    const uint16_t* Qb = a.q + head;
+    const uint16_t* dOb = a.dout + head;
+    uint16_t* dQb = a.dq + head;
+    if constexpr (GEN) {
+        const int b = bh / a.H, hh = bh % a.H;
+        const SeqShape ss = seq_shape(a.lens_q, a.lens_k, b, N, a.Nk);
+        nq = ss.nq;
+        nk = ss.nk;
+        off = ss.off;
+        if (qb * kQRows >= nq) return;  // the whole workgroup: past this sequence's queries
+        Qb = a.q + b * a.st[0][0] + hh * a.st[0][1];
+        K = a.k + b * a.st[1][0] + hh * a.st[1][1];
+        V = a.v + b * a.st[2][0] + hh * a.st[2][1];
+        dOb = a.dout + b * a.st[3][0] + hh * a.st[3][1];
+        dQb = a.dq + b * a.st[4][0] + hh * a.st[4][1];
+        q_rs = a.st[0][2];
+        k_rs = a.st[1][2];
+        v_rs = a.st[2][2];
+        do_rs = a.st[3][2];
+        dq_rs = a.st[4][2];
+    }
 
     const int q0 = qb * kQRows + wave * 32;  // first query of this wave
     const int qrow = q0 + l32;
-    const bool wave_active = q0 < N;
-    const int qload = min(qrow, N - 1);
+    const bool wave_active = q0 < nq;
+    const int qload = min(qrow, nq - 1);
 
-    const int nkb_all = (N + kQKeys - 1) / kQKeys;
+    const int nkb_all = (nk + kQKeys - 1) / kQKeys;
     // block-sparse: the 64-key halves of the kept key blocks of mask row qb
     static_assert(!SPARSE || kQRows == kSparseBlock, "a query workgroup covers one block row of the mask");
     BlockWalk walk;
@@ -476,11 +583,20 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
     if constexpr (SPARSE) {
         walk.init(a.mask_rows + (size_t)bh * a.head_words + (size_t)qb * a.W, 0, nkb_all);
         nkb = walk.count(0, CAUSAL ? qb : a.nb - 1);
+    } else if constexpr (GEN) {
+        const int last = min(nq, (qb + 1) * kQRows) - 1 + off;  // last key the workgroup's rows see
+        nkb = CAUSAL ? (last < 0 ? 0 : min(nkb_all, last / kQKeys + 1)) : nkb_all;
     } else {
         nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * kQRows) - 1) / kQKeys + 1) : nkb_all;
     }
     // blocks this wave computes: 0 .. nkw-1 (causal: up to the one holding its last row)
-    const int nkw = !wave_active ? 0 : (CAUSAL ? min(nkb, min(q0 + 31, N - 1) / kQKeys + 1) : nkb);
+    int nkw;
+    if constexpr (GEN) {
+        const int last = min(q0 + 31, nq - 1) + off;
+        nkw = !wave_active ? 0 : (CAUSAL ? (last < 0 ? 0 : min(nkb, last / kQKeys + 1)) : nkb);
+    } else {
+        nkw = !wave_active ? 0 : (CAUSAL ? min(nkb, min(q0 + 31, N - 1) / kQKeys + 1) : nkb);
+    }
     int slot_unit[kSlots];  // key block (64 keys) held by each ring slot
 
     f32x16 dqa[DT];
@@ -492,22 +608,37 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
     // block], each 64 rows in the swizzled layout. Chunk c of a stage is written
     // by wave c % 4; the same lane offsets serve K and V.
     uint32_t dma_off[kQTC / 4];
+    uint32_t dma_off_v[GEN ? kQTC / 4 : 1];  // V rows when strided differently from K
 #pragma unroll
     for (int j = 0; j < kQTC / 4; ++j) {
         const int p = (j * 4 + wave) * 64 + lane;
         const int row = p / CH, c = (p % CH) ^ swz<D>(row);
-        dma_off[j] = (uint32_t)((row * D + c * 8) * 2);
+        if constexpr (GEN) {
+            dma_off[j] = (uint32_t)(row * k_rs * 2) + c * 16;
+            dma_off_v[j] = (uint32_t)(row * v_rs * 2) + c * 16;
+        } else {
+            dma_off[j] = (uint32_t)((row * D + c * 8) * 2);
+        }
     }
     auto issue = [&](int b, int slot) {
         if constexpr (SPARSE) b = walk.next();
         slot_unit[slot] = b;
         const int r0 = b * kQKeys;
-        const i32x4 kr = rows_rsrc<kRowB>(K, N, r0), vr = rows_rsrc<kRowB>(V, N, r0);
         char* sb = smem + slot * kQStage + wave * 1024;
+        if constexpr (GEN) {
+            const i32x4 kr = strided_rows_rsrc<kRowB>(K, nk, r0, (uint32_t)(k_rs * 2));
+            const i32x4 vr = strided_rows_rsrc<kRowB>(V, nk, r0, (uint32_t)(v_rs * 2));
 #pragma unroll
-        for (int j = 0; j < kQTC / 4; ++j) dma16(kr, dma_off[j], sb + j * 4 * 1024);
+            for (int j = 0; j < kQTC / 4; ++j) dma16(kr, dma_off[j], sb + j * 4 * 1024);
 #pragma unroll
-        for (int j = 0; j < kQTC / 4; ++j) dma16(vr, dma_off[j], sb + kQTileB + j * 4 * 1024);
+            for (int j = 0; j < kQTC / 4; ++j) dma16(vr, dma_off_v[j], sb + kQTileB + j * 4 * 1024);
+        } else {
+            const i32x4 kr = rows_rsrc<kRowB>(K, N, r0), vr = rows_rsrc<kRowB>(V, N, r0);
+#pragma unroll
+            for (int j = 0; j < kQTC / 4; ++j) dma16(kr, dma_off[j], sb + j * 4 * 1024);
+#pragma unroll
+            for (int j = 0; j < kQTC / 4; ++j) dma16(vr, dma_off[j], sb + kQTileB + j * 4 * 1024);
+        }
     };
 
     const uint32_t smem_addr = lds_addr(smem);
@@ -529,11 +660,21 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
     // for as in the key workgroups.
     u32x4 qf[KS], dof[KS];
     {
-        const size_t off = head + (size_t)qload * D + 8 * h;
+        if constexpr (GEN) {
+            const uint16_t* qp = Qb + (size_t)qload * q_rs + 8 * h;
+            const uint16_t* dp = dOb + (size_t)qload * do_rs + 8 * h;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qf[ks] = *reinterpret_cast<const u32x4*>(a.q + off + 16 * ks);
-            dof[ks] = *reinterpret_cast<const u32x4*>(a.dout + off + 16 * ks);
+            for (int ks = 0; ks < KS; ++ks) {
+                qf[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+                dof[ks] = *reinterpret_cast<const u32x4*>(dp + 16 * ks);
+            }
+        } else {
+            const size_t off = head + (size_t)qload * D + 8 * h;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                qf[ks] = *reinterpret_cast<const u32x4*>(a.q + off + 16 * ks);
+                dof[ks] = *reinterpret_cast<const u32x4*>(a.dout + off + 16 * ks);
+            }
         }
     }
     const float l2q_ld = a.lse2[(size_t)bh * N + qload];
@@ -614,8 +755,8 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
                 ktr[2][u][hi] = tr_read<KO + 2 * 16 * kRowB>(tr_base[u][hi]);
                 ktr[3][u][hi] = tr_read<KO + 3 * 16 * kRowB>(tr_base[u][hi]);
             }
-        const int qlim = qrow - key0 - 8 * h;  // mask bounds relative to key0 + 8h
-        const int nlim = N - key0 - 8 * h;
+        const int qlim = GEN ? qrow + off - key0 - 8 * h : qrow - key0 - 8 * h;  // mask bounds relative to key0 + 8h
+        const int nlim = GEN ? nk - key0 - 8 * h : N - key0 - 8 * h;
         // ---- per key tile kt: dS^T = P^T (dP^T - D) with P^T = exp2(S^T c - lse2),
         // then dQ^T (64 dims x 32 queries) += K^T dS^T over its two 16-key chunks;
         // those MFMAs run while the next tile's element-wise work is issued
@@ -667,37 +808,39 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
         } else {
             if (kb >= nkw) return;
         }
-        const bool need_mask = (CAUSAL && key0 + kQKeys - 1 > q0) || (key0 + kQKeys > N);
+        const bool need_mask = (CAUSAL && key0 + kQKeys - 1 > q0 + off) || (key0 + kQKeys > nk);
         if (need_mask) block(slot_c, Masked{}, key0);
         else block(slot_c, Unmasked{}, key0);
     });
 
     if (wave_active) {
         char* stage = smem + (nkb % kSlots) * kQStage + wave * (2048 * DT);
-        store_rows<T, DT>(dqa, a.scale, a.dq + head + (size_t)q0 * D, D, N - q0, stage);
+        if constexpr (GEN) store_rows<T, DT>(dqa, a.scale, dQb + (size_t)q0 * dq_rs, (int)dq_rs, nq - q0, stage);
+        else store_rows<T, DT>(dqa, a.scale, a.dq + head + (size_t)q0 * D, D, N - q0, stage);
     }
 }
 
-template <typename T, bool CAUSAL, bool SPARSE>
+template <typename T, bool CAUSAL, bool SPARSE, bool GEN = false>
 __global__ __launch_bounds__(kThreads, 2) void bwd_fused_kernel(FusedArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[kSmem];
     int bh, blk;
     bool is_q;
     map_fused(blockIdx.x, a, CAUSAL, bh, is_q, blk);
-    if (is_q) q_body<T, CAUSAL, SPARSE>(a, bh, blk, smem);
-    else kv_body<T, CAUSAL, SPARSE>(a, bh, blk, smem);
+    if (is_q) q_body<T, CAUSAL, SPARSE, GEN>(a, bh, blk, smem);
+    else kv_body<T, CAUSAL, SPARSE, GEN>(a, bh, blk, smem);
 }
 
-template <typename T, bool SPARSE>
+template <typename T, bool SPARSE, bool GEN = false>
 hipError_t launch_fused(FusedArgs a, bool causal, hipStream_t stream) {
-    a.nblk = (a.N + kKvKeys - 1) / kKvKeys;
+    // general shapes: enough blocks of each kind for the longer of the query and key extents
+    a.nblk = ((GEN ? max(a.N, a.Nk) : a.N) + kKvKeys - 1) / kKvKeys;
     static_assert(kKvKeys == kQRows, "both kinds of workgroup cover 128 rows");
     a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
     const dim3 grid((unsigned)(a.BH * 2 * a.nblk));
     if (causal)
-        hipLaunchKernelGGL((bwd_fused_kernel<T, true, SPARSE>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((bwd_fused_kernel<T, true, SPARSE, GEN>), grid, dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((bwd_fused_kernel<T, false, SPARSE>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((bwd_fused_kernel<T, false, SPARSE, GEN>), grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -712,6 +855,10 @@ hipError_t bwd_prep(const void* o, const void* dout, const float* lse, int B, in
     p.delta = delta;
     p.lse2 = lse2;
     p.rows = (int64_t)B * H * N;
+    p.H = H;
+    p.N = N;
+    p.lens_q = nullptr;
+    for (int i = 0; i < 3; ++i) p.so[i] = p.sd[i] = 0;
     if (d == 128) {
         const dim3 grid((unsigned)((p.rows + kPrepRows<128> - 1) / kPrepRows<128>));
         if (dtype == 0)
@@ -779,6 +926,68 @@ hipError_t bwd_fused_sparse(const void* q, const void* k, const void* v, const v
     a.nb = (N + kSparseBlock - 1) / kSparseBlock;
     a.head_words = head_words;
     return dtype == 0 ? launch_fused<Bf16, true>(a, causal, stream) : launch_fused<F16, true>(a, causal, stream);
+}
+
+hipError_t bwd_prep_general(const void* o, const void* dout, const float* lse, int B, int H, int Nq, int d,
+                            int dtype, const int64_t* so, const int64_t* sd, const int* lens_q, float* delta,
+                            float* lse2, hipStream_t stream) {
+    PrepArgs p;
+    p.o = static_cast<const uint16_t*>(o);
+    p.dout = static_cast<const uint16_t*>(dout);
+    p.lse = lse;
+    p.delta = delta;
+    p.lse2 = lse2;
+    p.rows = (int64_t)B * H * Nq;
+    p.H = H;
+    p.N = Nq;
+    p.lens_q = lens_q;
+    for (int i = 0; i < 3; ++i) {
+        p.so[i] = so[i];
+        p.sd[i] = sd[i];
+    }
+    if (d == 128) {
+        const dim3 grid((unsigned)((p.rows + kPrepRows<128> - 1) / kPrepRows<128>));
+        if (dtype == 0) hipLaunchKernelGGL((bwd_prep_kernel<Bf16, 128, true>), grid, dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((bwd_prep_kernel<F16, 128, true>), grid, dim3(kThreads), 0, stream, p);
+    } else {
+        const dim3 grid((unsigned)((p.rows + kPrepRows<64> - 1) / kPrepRows<64>));
+        if (dtype == 0) hipLaunchKernelGGL((bwd_prep_kernel<Bf16, 64, true>), grid, dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL((bwd_prep_kernel<F16, 64, true>), grid, dim3(kThreads), 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t bwd_fused_general(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                             const float* lse2, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+                             float scale, bool causal, int dtype, const int64_t (*st)[3], const int* lens_q,
+                             const int* lens_k, hipStream_t stream) {
+    FusedArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.dout = static_cast<const uint16_t*>(dout);
+    a.lse2 = lse2;
+    a.delta = delta;
+    a.dq = static_cast<uint16_t*>(dq);
+    a.dk = static_cast<uint16_t*>(dk);
+    a.dv = static_cast<uint16_t*>(dv);
+    a.BH = B * H;
+    a.N = Nq;
+    a.nblk = 0;
+    a.heads_per_xcd = 0;
+    a.c = scale * kLog2e;
+    a.scale = scale;
+    a.mask_rows = a.mask_cols = nullptr;
+    a.W = a.nb = 0;
+    a.head_words = 0;
+    for (int t = 0; t < 7; ++t)
+        for (int i = 0; i < 3; ++i) a.st[t][i] = st[t][i];
+    a.H = H;
+    a.Nk = Nk;
+    a.lens_q = lens_q;
+    a.lens_k = lens_k;
+    return dtype == 0 ? launch_fused<Bf16, false, true>(a, causal, stream)
+                      : launch_fused<F16, false, true>(a, causal, stream);
 }
 
 }  // namespace fa

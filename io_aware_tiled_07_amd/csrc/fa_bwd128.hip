@@ -118,6 +118,12 @@ struct Args {
     const uint64_t* mask_cols;
     int W, nb;
     int64_t head_words;
+    // general shapes: element strides (batch, head, row) of q, k, v, dout, dq,
+    // dk, dv; N is the query extent, Nk the key extent; per-sequence lengths
+    int64_t st[7][3];
+    int H, Nk;
+    const int* lens_q;
+    const int* lens_k;
 };
 
 // Workgroup -> (head, kind, block): slot s of a head alternates key and query
@@ -138,19 +144,20 @@ __device__ __forceinline__ void map_block(int bid, const Args& a, bool causal, i
 }
 
 // Lane offsets of a stage's 16-byte DMA copies: chunk p of a 64-row tile
-// (swizzled layout) is written by wave p / 64 % 4 into LDS position p.
+// (swizzled layout) is written by wave p / 64 % 4 into LDS position p; source
+// rows are row_bytes apart.
 template <int TC>
-__device__ __forceinline__ void stage_offsets(uint32_t (&off)[TC / 4], int wave, int lane) {
+__device__ __forceinline__ void stage_offsets(uint32_t (&off)[TC / 4], int wave, int lane, uint32_t row_bytes) {
 #pragma unroll
     for (int j = 0; j < TC / 4; ++j) {
         const int p = (j * 4 + wave) * 64 + lane;
         const int row = p / CH, c = (p % CH) ^ swz<D>(row);
-        off[j] = (uint32_t)((row * D + c * 8) * 2);
+        off[j] = (uint32_t)row * row_bytes + c * 16;
     }
 }
 
 // Key workgroup: dK and dV of 128 keys.
-template <typename T, bool CAUSAL, bool SPARSE>
+template <typename T, bool CAUSAL, bool SPARSE, bool GEN = false>
 __device__ __forceinline__ void kv_body(const Args& a, int bh, int kb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
@@ -160,6 +167,33 @@ __device__ __forceinline__ void kv_body(const Args& a, int bh, int kb, char* sme
     const uint16_t* __restrict__ dO = a.dout + head;
     const float* __restrict__ lse2 = a.lse2 + (size_t)bh * N;
     const float* __restrict__ delta = a.delta + (size_t)bh * N;
+    // general shapes: this sequence's lengths, offset, bases and row strides (elements)
+    int nq = N, nk = N, off = 0;
+    int64_t q_rs = D, do_rs = D, k_rs = D, v_rs = D, dk_rs = D, dv_rs = D;
+    const uint16_t* Kb = a.k + head;
+    const uint16_t* Vb = a.v + head;
+    uint16_t* dKb = a.dk + head;
+    uint16_t* dVb = a.dv + head;
+    if constexpr (GEN) {
+        const int b = bh / a.H, hh = bh % a.H;
+        const SeqShape ss = seq_shape(a.lens_q, a.lens_k, b, N, a.Nk);
+        nq = ss.nq;
+        nk = ss.nk;
+        off = ss.off;
+        if (kb * kKvKeys >= nk) return;  // the whole workgroup: past this sequence's keys
+        Q = a.q + b * a.st[0][0] + hh * a.st[0][1];
+        Kb = a.k + b * a.st[1][0] + hh * a.st[1][1];
+        Vb = a.v + b * a.st[2][0] + hh * a.st[2][1];
+        dO = a.dout + b * a.st[3][0] + hh * a.st[3][1];
+        dKb = a.dk + b * a.st[5][0] + hh * a.st[5][1];
+        dVb = a.dv + b * a.st[6][0] + hh * a.st[6][1];
+        q_rs = a.st[0][2];
+        k_rs = a.st[1][2];
+        v_rs = a.st[2][2];
+        do_rs = a.st[3][2];
+        dk_rs = a.st[5][2];
+        dv_rs = a.st[6][2];
+    }
 
     const int kw0 = kb * kKvKeys + wave * 32;  // first key of this wave
     const int key = kw0 + l32;                 // key of this lane (and of lane ^ 32)
@@ -167,8 +201,8 @@ __device__ __forceinline__ void kv_body(const Args& a, int bh, int kb, char* sme
 #pragma unroll
     for (int u = 0; u < DT; ++u) { dk[u] = f32x16{}; dv[u] = f32x16{}; }
 
-    const int ng = (N + kKvQRows - 1) / kKvQRows;
-    const int g0 = CAUSAL ? (kb * kKvKeys) / kKvQRows : 0;
+    const int ng = (nq + kKvQRows - 1) / kKvQRows;
+    const int g0 = CAUSAL ? (GEN ? max(0, kb * kKvKeys - off) : kb * kKvKeys) / kKvQRows : 0;
     // block-sparse: the 64-row halves of the kept query blocks of mask column kb
     static_assert(!SPARSE || kKvKeys == kSparseBlock, "a key workgroup covers one block column of the mask");
     BlockWalk walk;
@@ -177,25 +211,39 @@ __device__ __forceinline__ void kv_body(const Args& a, int bh, int kb, char* sme
         walk.init(a.mask_cols + (size_t)bh * a.head_words + (size_t)kb * a.W, CAUSAL ? kb : 0, ng);
         nst = walk.count(CAUSAL ? kb : 0, a.nb - 1);
     } else {
-        nst = ng - g0;
+        nst = GEN ? max(0, ng - g0) : ng - g0;
     }
     int slot_unit[kSlots];  // query stage (64 rows) held by each ring slot
 
     // stage s (query rows (g0 + s) * 64 ..) in slot s % 4: [lse2 x64][-D x64][Q rows][dO rows]
-    uint32_t dma_off[kKvTC / 4];
-    stage_offsets<kKvTC>(dma_off, wave, lane);
+    uint32_t dma_off[kKvTC / 4], dma_off_d[GEN ? kKvTC / 4 : 1];  // dO rows when strided differently from Q
+    if constexpr (GEN) {
+        stage_offsets<kKvTC>(dma_off, wave, lane, (uint32_t)(2 * q_rs));
+        stage_offsets<kKvTC>(dma_off_d, wave, lane, (uint32_t)(2 * do_rs));
+    } else {
+        stage_offsets<kKvTC>(dma_off, wave, lane, kRowB);
+    }
     auto issue = [&](int s, int slot) {
         const int g = SPARSE ? walk.next() : g0 + s;
         slot_unit[slot] = g;
         const int r0 = g * kKvQRows;
-        const i32x4 qr = rows_rsrc<kRowB>(Q, N, r0), dr = rows_rsrc<kRowB>(dO, N, r0);
         char* sb = smem + slot * kStage + kKvRowsOff + wave * 1024;
+        if constexpr (GEN) {
+            const i32x4 qr = strided_rows_rsrc<kRowB>(Q, nq, r0, (uint32_t)(2 * q_rs));
+            const i32x4 dr = strided_rows_rsrc<kRowB>(dO, nq, r0, (uint32_t)(2 * do_rs));
 #pragma unroll
-        for (int j = 0; j < kKvTC / 4; ++j) dma16(qr, dma_off[j], sb + j * 4 * 1024);
+            for (int j = 0; j < kKvTC / 4; ++j) dma16(qr, dma_off[j], sb + j * 4 * 1024);
 #pragma unroll
-        for (int j = 0; j < kKvTC / 4; ++j) dma16(dr, dma_off[j], sb + kKvTileB + j * 4 * 1024);
+            for (int j = 0; j < kKvTC / 4; ++j) dma16(dr, dma_off_d[j], sb + kKvTileB + j * 4 * 1024);
+        } else {
+            const i32x4 qr = rows_rsrc<kRowB>(Q, N, r0), dr = rows_rsrc<kRowB>(dO, N, r0);
+#pragma unroll
+            for (int j = 0; j < kKvTC / 4; ++j) dma16(qr, dma_off[j], sb + j * 4 * 1024);
+#pragma unroll
+            for (int j = 0; j < kKvTC / 4; ++j) dma16(dr, dma_off[j], sb + kKvTileB + j * 4 * 1024);
+        }
         if (wave < 2)
-            dma4(rows_rsrc<4>(wave == 0 ? lse2 : delta, N, r0), (uint32_t)lane * 4,
+            dma4(rows_rsrc<4>(wave == 0 ? lse2 : delta, nq, r0), (uint32_t)lane * 4,
                  smem + slot * kStage + wave * kKvStatB);
     };
 
@@ -220,11 +268,22 @@ __device__ __forceinline__ void kv_body(const Args& a, int bh, int kb, char* sme
     // K and V rows of the wave (B operands of S = Q K^T and dP = dO V^T)
     u32x4 kf[KS], vf[KS];
     {
-        const size_t kr = head + (size_t)min(key, N - 1) * D + 8 * h;
+        if constexpr (GEN) {
+            const int krow = min(key, nk - 1);
+            const uint16_t* kp = Kb + (size_t)krow * k_rs + 8 * h;
+            const uint16_t* vp = Vb + (size_t)krow * v_rs + 8 * h;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            kf[ks] = *reinterpret_cast<const u32x4*>(a.k + kr + 16 * ks);
-            vf[ks] = *reinterpret_cast<const u32x4*>(a.v + kr + 16 * ks);
+            for (int ks = 0; ks < KS; ++ks) {
+                kf[ks] = *reinterpret_cast<const u32x4*>(kp + 16 * ks);
+                vf[ks] = *reinterpret_cast<const u32x4*>(vp + 16 * ks);
+            }
+        } else {
+            const size_t kr = head + (size_t)min(key, N - 1) * D + 8 * h;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                kf[ks] = *reinterpret_cast<const u32x4*>(a.k + kr + 16 * ks);
+                vf[ks] = *reinterpret_cast<const u32x4*>(a.v + kr + 16 * ks);
+            }
         }
     }
 #pragma unroll
@@ -297,8 +356,9 @@ __device__ __forceinline__ void kv_body(const Args& a, int bh, int kb, char* sme
                 dtr[0][u][hi] = tr_read<DO>(tr_off[u][hi] + sb);
                 qtr[0][u][hi] = tr_read<QO>(tr_off[u][hi] + sb);
             }
-        const int dlim = key - qt0 - 8 * h;  // mask bounds relative to the lane's first query qt0 + 8h
-        const int nlim = key < N ? N - qt0 - 8 * h : -1;
+        // mask bounds relative to the lane's first query qt0 + 8h
+        const int dlim = GEN ? key - off - qt0 - 8 * h : key - qt0 - 8 * h;
+        const int nlim = GEN ? (key < nk ? nq - qt0 - 8 * h : -1) : (key < N ? N - qt0 - 8 * h : -1);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             uint32_t pw[4], dsw[4];
@@ -371,9 +431,11 @@ __device__ __forceinline__ void kv_body(const Args& a, int bh, int kb, char* sme
         const int g = SPARSE ? slot_unit[SLOT] : g0 + s;
         auto half = [&](auto hh_c) {
             const int qt0 = g * kKvQRows + 32 * decltype(hh_c)::value;
-            const bool active = kw0 < N && qt0 < N && (!CAUSAL || qt0 + 31 >= kw0);
+            const bool active = GEN ? kw0 < nk && qt0 < nq && (!CAUSAL || qt0 + 31 + off >= kw0)
+                                    : kw0 < N && qt0 < N && (!CAUSAL || qt0 + 31 >= kw0);
             if (!active) return;
-            const bool need_mask = (CAUSAL && kw0 + 31 > qt0) || kw0 + 32 > N || qt0 + 32 > N;
+            const bool need_mask = GEN ? (CAUSAL && kw0 + 31 > qt0 + off) || kw0 + 32 > nk || qt0 + 32 > nq
+                                       : (CAUSAL && kw0 + 31 > qt0) || kw0 + 32 > N || qt0 + 32 > N;
             unit(sb, hh_c, need_mask, qt0);
         };
         half(Int<0>{});
@@ -383,13 +445,18 @@ __device__ __forceinline__ void kv_body(const Args& a, int bh, int kb, char* sme
     // dK, dV go out row by row through a ring slot no wave reads any more
     {
         char* stage = smem + (nst % kSlots) * kStage + wave * (2048 * DT);
-        store_rows<T, DT>(dk, a.scale, a.dk + head + (size_t)kw0 * D, D, N - kw0, stage);
-        store_rows<T, DT>(dv, 1.f, a.dv + head + (size_t)kw0 * D, D, N - kw0, stage);
+        if constexpr (GEN) {
+            store_rows<T, DT>(dk, a.scale, dKb + (size_t)kw0 * dk_rs, (int)dk_rs, nk - kw0, stage);
+            store_rows<T, DT>(dv, 1.f, dVb + (size_t)kw0 * dv_rs, (int)dv_rs, nk - kw0, stage);
+        } else {
+            store_rows<T, DT>(dk, a.scale, a.dk + head + (size_t)kw0 * D, D, N - kw0, stage);
+            store_rows<T, DT>(dv, 1.f, a.dv + head + (size_t)kw0 * D, D, N - kw0, stage);
+        }
     }
 }
 
 // Query workgroup: dQ of 128 queries.
-template <typename T, bool CAUSAL, bool SPARSE>
+template <typename T, bool CAUSAL, bool SPARSE, bool GEN = false>
 __device__ __forceinline__ void q_body(const Args& a, int bh, int qb, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, L16 = lane & 15;
@@ -397,13 +464,37 @@ __device__ __forceinline__ void q_body(const Args& a, int bh, int qb, char* smem
     const size_t head = (size_t)bh * N * D;
     const uint16_t* __restrict__ K = a.k + head;
     const uint16_t* __restrict__ V = a.v + head;
+    // general shapes: this sequence's lengths, offset, bases and row strides (elements)
+    int nq = N, nk = N, off = 0;
+    int64_t q_rs = D, do_rs = D, k_rs = D, v_rs = D, dq_rs = D;
+    const uint16_t* Qb = a.q + head;
+    const uint16_t* dOb = a.dout + head;
+    uint16_t* dQb = a.dq + head;
+    if constexpr (GEN) {
+        const int b = bh / a.H, hh = bh % a.H;
+        const SeqShape ss = seq_shape(a.lens_q, a.lens_k, b, N, a.Nk);
+        nq = ss.nq;
+        nk = ss.nk;
+        off = ss.off;
+        if (qb * kQRows >= nq) return;  // the whole workgroup: past this sequence's queries
+        Qb = a.q + b * a.st[0][0] + hh * a.st[0][1];
+        K = a.k + b * a.st[1][0] + hh * a.st[1][1];
+        V = a.v + b * a.st[2][0] + hh * a.st[2][1];
+        dOb = a.dout + b * a.st[3][0] + hh * a.st[3][1];
+        dQb = a.dq + b * a.st[4][0] + hh * a.st[4][1];
+        q_rs = a.st[0][2];
+        k_rs = a.st[1][2];
+        v_rs = a.st[2][2];
+        do_rs = a.st[3][2];
+        dq_rs = a.st[4][2];
+    }
 
     const int q0 = qb * kQRows + wave * 32;  // first query of this wave
     const int qrow = q0 + l32;
-    const bool wave_active = q0 < N;
-    const int qload = min(qrow, N - 1);
+    const bool wave_active = q0 < nq;
+    const int qload = min(qrow, nq - 1);
 
-    const int nkb_all = (N + kQKeys - 1) / kQKeys;
+    const int nkb_all = (nk + kQKeys - 1) / kQKeys;
     // block-sparse: the 64-key halves of the kept key blocks of mask row qb
     static_assert(!SPARSE || kQRows == kSparseBlock, "a query workgroup covers one block row of the mask");
     BlockWalk walk;
@@ -411,10 +502,19 @@ __device__ __forceinline__ void q_body(const Args& a, int bh, int qb, char* smem
     if constexpr (SPARSE) {
         walk.init(a.mask_rows + (size_t)bh * a.head_words + (size_t)qb * a.W, 0, nkb_all);
         nkb = walk.count(0, CAUSAL ? qb : a.nb - 1);
+    } else if constexpr (GEN) {
+        const int last = min(nq, (qb + 1) * kQRows) - 1 + off;  // last key the workgroup's rows see
+        nkb = CAUSAL ? (last < 0 ? 0 : min(nkb_all, last / kQKeys + 1)) : nkb_all;
     } else {
         nkb = CAUSAL ? min(nkb_all, (min(N, (qb + 1) * kQRows) - 1) / kQKeys + 1) : nkb_all;
     }
-    const int nkw = !wave_active ? 0 : (CAUSAL ? min(nkb, min(q0 + 31, N - 1) / kQKeys + 1) : nkb);
+    int nkw;
+    if constexpr (GEN) {
+        const int last = min(q0 + 31, nq - 1) + off;
+        nkw = !wave_active ? 0 : (CAUSAL ? (last < 0 ? 0 : min(nkb, last / kQKeys + 1)) : nkb);
+    } else {
+        nkw = !wave_active ? 0 : (CAUSAL ? min(nkb, min(q0 + 31, N - 1) / kQKeys + 1) : nkb);
+    }
     int slot_unit[kSlots];  // key block (64 keys) held by each ring slot
 
     f32x16 dqa[DT];
@@ -422,18 +522,32 @@ __device__ __forceinline__ void q_body(const Args& a, int bh, int qb, char* smem
     for (int u = 0; u < DT; ++u) dqa[u] = f32x16{};
 
     // stage b (keys b * 64 ..) in slot b % 4: [K block][V block]
-    uint32_t dma_off[kQTC / 4];
-    stage_offsets<kQTC>(dma_off, wave, lane);
+    uint32_t dma_off[kQTC / 4], dma_off_v[GEN ? kQTC / 4 : 1];  // V rows when strided differently from K
+    if constexpr (GEN) {
+        stage_offsets<kQTC>(dma_off, wave, lane, (uint32_t)(2 * k_rs));
+        stage_offsets<kQTC>(dma_off_v, wave, lane, (uint32_t)(2 * v_rs));
+    } else {
+        stage_offsets<kQTC>(dma_off, wave, lane, kRowB);
+    }
     auto issue = [&](int b, int slot) {
         if constexpr (SPARSE) b = walk.next();
         slot_unit[slot] = b;
         const int r0 = b * kQKeys;
-        const i32x4 kr = rows_rsrc<kRowB>(K, N, r0), vr = rows_rsrc<kRowB>(V, N, r0);
         char* sb = smem + slot * kStage + wave * 1024;
+        if constexpr (GEN) {
+            const i32x4 kr = strided_rows_rsrc<kRowB>(K, nk, r0, (uint32_t)(2 * k_rs));
+            const i32x4 vr = strided_rows_rsrc<kRowB>(V, nk, r0, (uint32_t)(2 * v_rs));
 #pragma unroll
-        for (int j = 0; j < kQTC / 4; ++j) dma16(kr, dma_off[j], sb + j * 4 * 1024);
+            for (int j = 0; j < kQTC / 4; ++j) dma16(kr, dma_off[j], sb + j * 4 * 1024);
 #pragma unroll
-        for (int j = 0; j < kQTC / 4; ++j) dma16(vr, dma_off[j], sb + kQTileB + j * 4 * 1024);
+            for (int j = 0; j < kQTC / 4; ++j) dma16(vr, dma_off_v[j], sb + kQTileB + j * 4 * 1024);
+        } else {
+            const i32x4 kr = rows_rsrc<kRowB>(K, N, r0), vr = rows_rsrc<kRowB>(V, N, r0);
+#pragma unroll
+            for (int j = 0; j < kQTC / 4; ++j) dma16(kr, dma_off[j], sb + j * 4 * 1024);
+#pragma unroll
+            for (int j = 0; j < kQTC / 4; ++j) dma16(vr, dma_off[j], sb + kQTileB + j * 4 * 1024);
+        }
     };
 
     const uint32_t smem_addr = lds_addr(smem);
@@ -453,11 +567,21 @@ __device__ __forceinline__ void q_body(const Args& a, int bh, int qb, char* smem
     // Q and dO rows (B operands of S^T = K Q^T and dP^T = V dO^T) and the row statistics
     u32x4 qf[KS], dof[KS];
     {
-        const size_t off = head + (size_t)qload * D + 8 * h;
+        if constexpr (GEN) {
+            const uint16_t* qp = Qb + (size_t)qload * q_rs + 8 * h;
+            const uint16_t* dp = dOb + (size_t)qload * do_rs + 8 * h;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qf[ks] = *reinterpret_cast<const u32x4*>(a.q + off + 16 * ks);
-            dof[ks] = *reinterpret_cast<const u32x4*>(a.dout + off + 16 * ks);
+            for (int ks = 0; ks < KS; ++ks) {
+                qf[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+                dof[ks] = *reinterpret_cast<const u32x4*>(dp + 16 * ks);
+            }
+        } else {
+            const size_t off = head + (size_t)qload * D + 8 * h;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                qf[ks] = *reinterpret_cast<const u32x4*>(a.q + off + 16 * ks);
+                dof[ks] = *reinterpret_cast<const u32x4*>(a.dout + off + 16 * ks);
+            }
         }
     }
     const float l2q_ld = a.lse2[(size_t)bh * N + qload];
@@ -518,8 +642,9 @@ __device__ __forceinline__ void q_body(const Args& a, int bh, int qb, char* smem
                 ktr[1][u][hi] = tr_read<KO + 16 * kRowB>(tr_off[u][hi] + sb);
             }
         // ---- dS^T = P^T (dP^T - D), P^T = exp2(S^T c - lse2)
-        const int qlim = qrow - key0 - 32 * KT - 8 * h;  // mask bounds relative to the lane's first key
-        const int nlim = N - key0 - 32 * KT - 8 * h;
+        // mask bounds relative to the lane's first key
+        const int qlim = GEN ? qrow + off - key0 - 32 * KT - 8 * h : qrow - key0 - 32 * KT - 8 * h;
+        const int nlim = GEN ? nk - key0 - 32 * KT - 8 * h : N - key0 - 32 * KT - 8 * h;
         uint32_t dsw[8];
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
@@ -568,8 +693,10 @@ __device__ __forceinline__ void q_body(const Args& a, int bh, int qb, char* smem
         const uint32_t sb = slot_base<SLOT>();
         auto one = [&](auto kt_c) {
             const int k0 = key0 + 32 * decltype(kt_c)::value;
-            if (k0 >= N || (CAUSAL && k0 > q0 + 31)) return;  // no visible key in this tile
-            const bool need_mask = (CAUSAL && k0 + 31 > q0) || k0 + 32 > N;
+            // no visible key in this tile
+            if (GEN ? k0 >= nk || (CAUSAL && k0 > q0 + 31 + off) : k0 >= N || (CAUSAL && k0 > q0 + 31)) return;
+            const bool need_mask = GEN ? (CAUSAL && k0 + 31 > q0 + off) || k0 + 32 > nk
+                                       : (CAUSAL && k0 + 31 > q0) || k0 + 32 > N;
             if (need_mask) tile(sb, kt_c, Masked{}, key0);
             else tile(sb, kt_c, Unmasked{}, key0);
         };
@@ -579,39 +706,40 @@ __device__ __forceinline__ void q_body(const Args& a, int bh, int qb, char* smem
 
     if (wave_active) {
         char* stage = smem + (nkb % kSlots) * kStage + wave * (2048 * DT);
-        store_rows<T, DT>(dqa, a.scale, a.dq + head + (size_t)q0 * D, D, N - q0, stage);
+        if constexpr (GEN) store_rows<T, DT>(dqa, a.scale, dQb + (size_t)q0 * dq_rs, (int)dq_rs, nq - q0, stage);
+        else store_rows<T, DT>(dqa, a.scale, a.dq + head + (size_t)q0 * D, D, N - q0, stage);
     }
 }
 
-template <typename T, bool CAUSAL, bool SPARSE>
+template <typename T, bool CAUSAL, bool SPARSE, bool GEN = false>
 __global__ __launch_bounds__(kThreads, 1) void bwd128_fused_kernel(Args a) {
     __shared__ __attribute__((aligned(1024))) char smem[kSmem];
     int bh, blk;
     bool is_q;
     map_block(blockIdx.x, a, CAUSAL, bh, is_q, blk);
-    if (is_q) q_body<T, CAUSAL, SPARSE>(a, bh, blk, smem);
-    else kv_body<T, CAUSAL, SPARSE>(a, bh, blk, smem);
+    if (is_q) q_body<T, CAUSAL, SPARSE, GEN>(a, bh, blk, smem);
+    else kv_body<T, CAUSAL, SPARSE, GEN>(a, bh, blk, smem);
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool GEN = false>
 hipError_t launch(Args a, bool causal, int dtype, hipStream_t stream) {
     static_assert(kKvKeys == kQRows, "both kinds of workgroup cover 128 rows");
-    a.nblk = (a.N + kKvKeys - 1) / kKvKeys;
+    a.nblk = ((GEN ? max(a.N, a.Nk) : a.N) + kKvKeys - 1) / kKvKeys;
     a.heads_per_xcd = (a.BH % 8 == 0) ? a.BH / 8 : 0;
     const dim3 grid((unsigned)(a.BH * 2 * a.nblk));
     if (dtype == 0) {
-        if (causal) hipLaunchKernelGGL((bwd128_fused_kernel<Bf16, true, SPARSE>), grid, dim3(kThreads), 0, stream, a);
-        else hipLaunchKernelGGL((bwd128_fused_kernel<Bf16, false, SPARSE>), grid, dim3(kThreads), 0, stream, a);
+        if (causal) hipLaunchKernelGGL((bwd128_fused_kernel<Bf16, true, SPARSE, GEN>), grid, dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((bwd128_fused_kernel<Bf16, false, SPARSE, GEN>), grid, dim3(kThreads), 0, stream, a);
     } else {
-        if (causal) hipLaunchKernelGGL((bwd128_fused_kernel<F16, true, SPARSE>), grid, dim3(kThreads), 0, stream, a);
-        else hipLaunchKernelGGL((bwd128_fused_kernel<F16, false, SPARSE>), grid, dim3(kThreads), 0, stream, a);
+        if (causal) hipLaunchKernelGGL((bwd128_fused_kernel<F16, true, SPARSE, GEN>), grid, dim3(kThreads), 0, stream, a);
+        else hipLaunchKernelGGL((bwd128_fused_kernel<F16, false, SPARSE, GEN>), grid, dim3(kThreads), 0, stream, a);
     }
     return hipGetLastError();
 }
 
 Args make_args(const void* q, const void* k, const void* v, const void* dout, const float* delta, const float* lse2,
                void* dq, void* dk, void* dv, int B, int H, int N, float scale) {
-    Args a;
+    Args a{};
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
@@ -652,6 +780,20 @@ hipError_t bwd128_fused_sparse(const void* q, const void* k, const void* v, cons
     a.nb = (N + kSparseBlock - 1) / kSparseBlock;
     a.head_words = head_words;
     return launch<true>(a, causal, dtype, stream);
+}
+
+hipError_t bwd128_fused_general(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                                const float* lse2, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+                                float scale, bool causal, int dtype, const int64_t (*st)[3], const int* lens_q,
+                                const int* lens_k, hipStream_t stream) {
+    Args a = make_args(q, k, v, dout, delta, lse2, dq, dk, dv, B, H, Nq, scale);
+    for (int t = 0; t < 7; ++t)
+        for (int i = 0; i < 3; ++i) a.st[t][i] = st[t][i];
+    a.H = H;
+    a.Nk = Nk;
+    a.lens_q = lens_q;
+    a.lens_k = lens_k;
+    return launch<false, true>(a, causal, dtype, stream);
 }
 
 }  // namespace fa

@@ -230,6 +230,20 @@ __device__ __forceinline__ i32x4 strided_rows_rsrc(const void* base, int n, int 
                        (uint32_t)(left < 0xFFFFFFFFull ? left : 0xFFFFFFFFull));
 }
 
+// ---------------------------------------------------------------- general shapes
+// Queries, keys and causal offset of sequence b of a padded batch (query i sees
+// keys j <= i + off: the queries are the last positions of the sequence).
+struct SeqShape {
+    int nq, nk, off;
+};
+__device__ __forceinline__ SeqShape seq_shape(const int* lens_q, const int* lens_k, int b, int Nq, int Nk) {
+    SeqShape s;
+    s.nq = lens_q ? min(max(lens_q[b], 0), Nq) : Nq;  // lengths beyond the extents are clamped
+    s.nk = lens_k ? min(max(lens_k[b], 0), Nk) : Nk;
+    s.off = s.nk - s.nq;
+    return s;
+}
+
 // ---------------------------------------------------------------- row stores
 // A wave's 32 x (32 DT) block in MFMA accumulator order (lane l holds column
 // l % 32; register 4g + k of tile u holds element 32u + 8g + 4(l / 32) + k of

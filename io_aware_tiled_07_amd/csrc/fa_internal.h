@@ -60,6 +60,21 @@ hipError_t fwd_general(const void* q, const void* k, const void* v, void* o, flo
                        const int64_t* sv, const int64_t* so, const int* lens_q, const int* lens_k,
                        hipStream_t stream);
 
+// Backward over the same general shapes: prep over strided o / dout (rows past a
+// sequence's queries are skipped), then the fused launch; st holds the strides
+// of q, k, v, dout, dq, dk, dv in that order.
+hipError_t bwd_prep_general(const void* o, const void* dout, const float* lse, int B, int H, int Nq, int d,
+                            int dtype, const int64_t* so, const int64_t* sd, const int* lens_q, float* delta,
+                            float* lse2, hipStream_t stream);
+hipError_t bwd_fused_general(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                             const float* lse2, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+                             float scale, bool causal, int dtype, const int64_t (*st)[3], const int* lens_q,
+                             const int* lens_k, hipStream_t stream);
+hipError_t bwd128_fused_general(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                                const float* lse2, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+                                float scale, bool causal, int dtype, const int64_t (*st)[3], const int* lens_q,
+                                const int* lens_k, hipStream_t stream);
+
 // FP8 (e4m3) forward, d in {64, 128}: O in bf16, lse in fp32; the descale
 // factors turn the stored bytes into the real values.
 hipError_t fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,

@@ -214,3 +214,15 @@ def block_mask(seed: int, tensor_id: int, shape, density: float) -> np.ndarray:
     block-sparse attention."""
     n = int(np.prod(shape))
     return (uniform01(seed, tensor_id, n) < density).astype(np.uint8).reshape(shape)
+
+
+TENSOR_LENS = 9
+
+
+def lengths(seed: int, tensor_id: int, count: int, lo: int, hi: int) -> np.ndarray:
+    """``count`` sequence lengths, independent and uniform over [lo, hi], from the
+    seeded stream (int32): the length mix of a padded batch."""
+    if not 0 <= lo <= hi:
+        raise ValueError("need 0 <= lo <= hi")
+    u = uniform01(seed, tensor_id, count)
+    return np.minimum(lo + np.floor(u * (hi - lo + 1)).astype(np.int64), hi).astype(np.int32)

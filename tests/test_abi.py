@@ -38,7 +38,8 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_prep", "fa_bwd_main",
                           "fa_bwd_workspace_size", "fa_status_string", "fa_fwd_sparse", "fa_bwd_sparse",
                           "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size", "fa_fwd_fp8",
-                          "fa_decode", "fa_decode_workspace_size", "fa_fwd_general"}
+                          "fa_decode", "fa_decode_workspace_size", "fa_fwd_general",
+                          "fa_bwd_general_workspace_size", "fa_bwd_general"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -373,3 +374,50 @@ def gen(lib, B=2, H=3, Nq=100, Nk=200, d=64, causal=1, dtype=0, st=None, lens=(N
 ])
 def test_fwd_general_rejects(lib, kw, code):
     assert gen(lib, **kw) == code
+
+
+def bgen(lib, B=2, H=3, Nq=100, Nk=200, d=64, causal=1, dtype=0, st=None, lens=(None, None), ws_bytes=None,
+         **over):
+    names = ["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws"]
+    p = dict(zip(names, ptrs(10)))
+    p.update({k: v for k, v in over.items() if k in names})
+    bshd = lambda n: fa._Strides(n * H * d, d, H * d)
+    rows = [Nq, Nk, Nk, Nq, Nq, Nq, Nk, Nk]  # q k v o dout dq dk dv
+    ss = st or [bshd(n) for n in rows]
+    need = lib.fa_bwd_general_workspace_size(B, H, Nq)
+    return lib.fa_bwd_general(*[ctypes.c_void_p(p[n]) for n in names[:9]], B, H, Nq, Nk, d, ctypes.c_float(0.125),
+                              causal, dtype, *[ctypes.byref(x) for x in ss],
+                              *[ctypes.c_void_p(x) if x else None for x in lens],
+                              ctypes.c_void_p(p["ws"]), need if ws_bytes is None else ws_bytes, None)
+
+
+def test_bwd_general_workspace_size(lib):
+    assert lib.fa_bwd_general_workspace_size(2, 3, 100) == 2 * 2560  # 600 floats, 256-byte rounded, twice
+    assert lib.fa_bwd_general_workspace_size(0, 3, 100) == 0
+    assert lib.fa_bwd_general_workspace_size(2, 3, 0) == 0
+
+
+def _bshd_strides(Nq, Nk, H=3, d=64, dk_row=None):
+    b = lambda n, r=None: fa._Strides(n * H * d, d, r or H * d)
+    return [b(Nq), b(Nk), b(Nk), b(Nq), b(Nq), b(Nq), b(Nk, dk_row), b(Nk)]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=A + 6 * GAP + 8), fa.FA_ERR_INVALID_ARG),                    # misaligned
+    (dict(st=[fa._Strides(0, 64, 4)] * 8), fa.FA_ERR_INVALID_ARG),        # row stride not a multiple of 8
+    (dict(st=_bshd_strides(100, 200, dk_row=32)), fa.FA_ERR_INVALID_ARG),  # dk rows overlap each other
+    (dict(st=[fa._Strides(0, 1 << 23, 1 << 23)] * 8, B=1, H=1, Nq=1, Nk=1), fa.FA_ERR_INVALID_ARG),  # row stride too large
+    (dict(dq=A), fa.FA_ERR_INVALID_ARG),                                   # dq overlaps q
+    (dict(dv=A + 7 * GAP), fa.FA_ERR_INVALID_ARG),                         # dv overlaps dk
+    (dict(ws=A + 4 * GAP), fa.FA_ERR_INVALID_ARG),                         # workspace overlaps dout
+    (dict(lens=(None, A + 8 * GAP + 64)), fa.FA_ERR_INVALID_ARG),          # lengths inside dv
+    (dict(ws=0), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=8), fa.FA_ERR_WORKSPACE),
+    (dict(ws=A + 9 * GAP + 16), fa.FA_ERR_WORKSPACE),                      # not 256-byte aligned
+])
+def test_bwd_general_rejects(lib, kw, code):
+    assert bgen(lib, **kw) == code

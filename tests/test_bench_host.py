@@ -73,3 +73,14 @@ def test_kept_pairs_by_brute_force():
     assert bench.pairs_per_head(w) == 1024 * 1024 / 2
     w["pairs"] = 1234
     assert bench.flops(w, "fwd") == 4 * 8 * 12 * 64 * 1234
+
+
+def test_varlen_lengths_and_pairs():
+    """The padded-batch workload's lengths are seeded, inside [N/4, N], and its
+    credited pairs are the per-sequence causal rule."""
+    w = dict(bench.WORKLOADS["gpt2_varlen_bshd"])
+    lens = bench.varlen_lengths(w)
+    assert lens.shape == (w["B"],) and lens.min() >= w["N"] // 4 and lens.max() <= w["N"]
+    assert (bench.varlen_lengths(w) == lens).all()
+    w["pairs"] = float(sum(int(L) ** 2 for L in lens) * 0.5 / w["B"])
+    assert bench.flops(w, "step") == 10 * w["H"] * w["d"] * sum(int(L) ** 2 for L in lens) * 0.5

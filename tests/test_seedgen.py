@@ -98,3 +98,13 @@ def test_e4m3_rounding_matches_torch():
     assert d.stored.dtype == np.uint8 and d.f64.shape == (4, 5)
     with pytest.raises(ValueError):
         seedgen.round_f32_to_e4m3_bits(np.array([500.0], dtype=np.float32))
+
+
+def test_lengths_are_seeded_and_cover_their_range():
+    a = seedgen.lengths(3, seedgen.TENSOR_LENS, 4000, 256, 1024)
+    assert a.dtype == np.int32 and a.shape == (4000,)
+    assert np.array_equal(a, seedgen.lengths(3, seedgen.TENSOR_LENS, 4000, 256, 1024))
+    assert not np.array_equal(a, seedgen.lengths(4, seedgen.TENSOR_LENS, 4000, 256, 1024))
+    assert a.min() == 256 and a.max() == 1024
+    assert abs(a.mean() - 640) < 15
+    assert np.all(seedgen.lengths(1, 9, 50, 7, 7) == 7)
