@@ -439,7 +439,8 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
     if (causal && Nq > Nk) return FA_ERR_INVALID_ARG;
     if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
     const int64_t bh = (int64_t)B * H;
-    if ((int64_t)Nk > kMaxN || bh > kMaxGrid || bh * fa::decode_split(B, H, Nk).S > kMaxGrid) return FA_ERR_INVALID_ARG;
+    if ((int64_t)Nk > kMaxN || bh > kMaxGrid || bh * fa::decode_split(B, H, Nk).S > kMaxGrid || bh * Nq > kMaxGrid)
+        return FA_ERR_INVALID_ARG;
     const void* ptrs[] = {q, k, v, o, lse};
     for (const void* p : ptrs)
         if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;

@@ -185,3 +185,24 @@ def test_contiguous_general_bwd_is_the_dense_backward_bitwise(causal, d):
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp16_bshd_queries_against_more_keys(d):
+    """fp16, [B,N,H,d] storage, 350 queries against 900 keys, causal: forward and backward."""
+    B, H, Nq, Nk = 2, 3, 350, 900
+    log(f"general fp16 BSHD Nq={Nq} Nk={Nk} d={d}")
+    q = seedgen.draw(9940 + d, 0, (B, Nq, H, d), "fp16")
+    k = seedgen.draw(9940 + d, 1, (B, Nk, H, d), "fp16")
+    v = seedgen.draw(9940 + d, 2, (B, Nk, H, d), "fp16")
+    do = seedgen.draw(9940 + d, 3, (B, Nq, H, d), "fp16")
+    qg, kg, vg, dog = (x.torch("cuda").transpose(1, 2) for x in (q, k, v, do))
+    o, lse = fa.fwd_general(qg, kg, vg, causal=True)
+    dq, dk, dv = fa.bwd_general(qg, kg, vg, o, dog, lse, causal=True)
+    torch.cuda.synchronize()
+    f = lambda x: np.ascontiguousarray(x.f64.transpose(0, 2, 1, 3))
+    ref = oracle.bwd_kv(f(q), f(k), f(v), f(do), scale_for(d), True)
+    check("o", o, ref["o"], "fp16")
+    check("lse", lse, ref["lse"], "fp16")
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        check(name, g, ref[name], "fp16")
