@@ -223,6 +223,56 @@ def cpu_baseline(w, shape, scale, causal, min_seconds=10.0):
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 
 
+def gfx_clock_mhz(amd_smi_json):
+    """Mean GFX clock (MHz) over the XCDs in the output of `amd-smi metric -g 0 --clock --json`
+    (entries gfx_0, gfx_1, ... of gpu_data[0].clock); None if it lists none."""
+    clk = json.loads(amd_smi_json)["gpu_data"][0]["clock"]
+    vals = [v["clk"]["value"] for key, v in clk.items()
+            if key.startswith("gfx_") and isinstance(v.get("clk", {}).get("value"), (int, float))]
+    return sum(vals) / len(vals) if vals else None
+
+
+def sclk_during(run_steps, seconds=3.0):
+    """Shader clock while the workload runs: `amd-smi metric --clock` is polled from
+    a thread while run_steps() is called back to back for `seconds`; each sample is
+    the mean GFX clock over the XCDs it lists (MHz). Returns None if no sample came back."""
+    import subprocess
+    import threading
+
+    import torch
+    samples, err = [], []
+    stop = threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True,
+                                   text=True, timeout=20)
+                mhz = gfx_clock_mhz(r.stdout)
+                if mhz is not None:
+                    samples.append(mhz)
+            except Exception as e:  # tool missing or output not as expected: report none
+                err.append(f"{type(e).__name__}: {e}"[:200])
+                return
+
+    th = threading.Thread(target=poll, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        run_steps()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30)
+    # samples below the 500 MHz floor amd-smi lists as min_clk are idle (deep sleep) moments
+    busy = [x for x in samples if x >= 500.0]
+    if not busy:
+        return {"mean_mhz": None, "samples": 0, "idle_samples": len(samples), "error": err[0] if err else "no sample"}
+    return {"mean_mhz": round(statistics.mean(busy), 1), "min_mhz": round(min(busy), 1),
+            "max_mhz": round(max(busy), 1), "samples": len(busy), "idle_samples": len(samples) - len(busy),
+            "source": (f"amd-smi metric --clock, mean over the XCDs, polled while steps ran back to back for "
+                       f"{seconds:.0f} s; samples below 500 MHz (idle) left out")}
+
+
 def decode_bytes(w):
     """Compulsory HBM bytes of one call of attention over the cache: read Q, K, V,
     write O and lse."""
@@ -412,6 +462,8 @@ def main():
     ap.add_argument("--workload", default="gpt2_small_causal", choices=sorted(WORKLOADS))
     ap.add_argument("--dq", default="default", choices=["default", "atomic", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="skip the 3 s pass that samples the shader clock with amd-smi (use under a profiler)")
     ap.add_argument("--flush-mall", action="store_true",
                     help="also time K cold steps, each after writing a 512 MiB scratch buffer (evicts L2 and the "
                          "256 MB Infinity Cache)")
@@ -572,6 +624,13 @@ def main():
                 "tflops": round(flops(w, step_rule) / (cms * 1e-3) / 1e12, 3),
                 "note": "each step after a 512 MiB scratch write; events around each step"}
 
+    sclk = None
+    if not args.no_sclk:
+        def many():
+            for _ in range(200):
+                run()
+        sclk = sclk_during(many)
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -610,7 +669,7 @@ def main():
         "dominant_launch_ms": {"median": round(statistics.median(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev), 5),
                                "min": round(min(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev), 5),
                                "max": round(max(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev), 5)},
-        "cold": cold,
+        "cold": cold, "sclk": sclk,
     }
     print(json.dumps(out), flush=True)
 

@@ -84,3 +84,16 @@ def test_varlen_lengths_and_pairs():
     assert (bench.varlen_lengths(w) == lens).all()
     w["pairs"] = float(sum(int(L) ** 2 for L in lens) * 0.5 / w["B"])
     assert bench.flops(w, "step") == 10 * w["H"] * w["d"] * sum(int(L) ** 2 for L in lens) * 0.5
+
+
+def test_gfx_clock_parse():
+    """The clock pass averages the per-XCD GFX clocks of amd-smi's JSON and ignores other clocks."""
+    import json
+
+    import bench
+    xcd = {f"gfx_{i}": {"clk": {"value": 1900 + 10 * i, "unit": "MHz"}, "max_clk": {"value": 2400, "unit": "MHz"}}
+           for i in range(8)}
+    xcd["mem_0"] = {"clk": {"value": 2000, "unit": "MHz"}}
+    doc = json.dumps({"gpu_data": [{"gpu": 0, "clock": xcd}]})
+    assert bench.gfx_clock_mhz(doc) == sum(1900 + 10 * i for i in range(8)) / 8
+    assert bench.gfx_clock_mhz(json.dumps({"gpu_data": [{"gpu": 0, "clock": {"mem_0": {"clk": {"value": 1}}}}]})) is None
