@@ -267,7 +267,8 @@ def gfx_clock_mhz(amd_smi_json):
 def sclk_during(run_steps, seconds=3.0):
     """Shader clock while the workload runs: `amd-smi metric --clock` is polled from
     a thread while run_steps() is called back to back for `seconds`; each sample is
-    the mean GFX clock over the XCDs it lists (MHz). Returns None if no sample came back."""
+    the mean GFX clock over the XCDs it lists (MHz). If no busy sample came back (tool
+    missing, unexpected output), mean_mhz is None and "error" says why."""
     import subprocess
     import threading
 
