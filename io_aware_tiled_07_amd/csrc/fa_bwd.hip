@@ -401,29 +401,25 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         nd[1] = ds_read128f<TO + kKvStatB + 16>(st_base);
         nd[2] = ds_read128f<TO + kKvStatB + 64>(st_base);
         nd[3] = ds_read128f<TO + kKvStatB + 80>(st_base);
-        // lse * log2(e) of the first 8 queries; the other 8 are read when their
-        // chunk comes up
-        f32x4 lv[2];
+        // lse * log2(e) of the lane's 16 queries, in the order of nd
+        f32x4 lv[4];
         lv[0] = ds_read128f<TO>(st_base);
         lv[1] = ds_read128f<TO + 16>(st_base);
-        lgkm_wait<2>();
+        lv[2] = ds_read128f<TO + 64>(st_base);
+        lv[3] = ds_read128f<TO + 80>(st_base);
+        lgkm_wait<0>();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) { settle(qa[ks]); settle(da[ks]); }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) settle(nd[j]);
+        for (int j = 0; j < 4; ++j) { settle(nd[j]); settle(lv[j]); }
         f32x16 s = f32x16{}, dp;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) dp[4 * j + e] = nd[j][e];
+        // S first: P needs only S, so its exponentials run beside the dP MFMAs
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s = T::mfma32(qa[ks], kf[ks], s);
-            dp = T::mfma32(da[ks], vf[ks], dp);
-        }
-        lgkm_wait<0>();
-#pragma unroll
-        for (int j = 0; j < 2; ++j) settle(lv[j]);
+        for (int ks = 0; ks < KS; ++ks) s = T::mfma32(qa[ks], kf[ks], s);
         // transposed operands for dV^T += dO^T P and dK^T += Q^T dS, query chunk
         // 0 first, so they land during the element-wise work
         u32x2 dtr[2][DT][2], qtr[2][DT][2];
@@ -441,50 +437,35 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
                 dtr[1][u][hi] = tr_read<DO + 16 * kRowB>(tr_base[u][hi]);
                 qtr[1][u][hi] = tr_read<QO + 16 * kRowB>(tr_base[u][hi]);
             }
-        // per query chunk c (16 queries): P and dS, then its dV / dK MFMAs, which
-        // run while the next chunk's element-wise work is issued
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) dp = T::mfma32(da[ks], vf[ks], dp);
+        float p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[i] = fast_exp2(__builtin_fmaf(s[i], a.c, -lv[i >> 2][i & 3]));
+        if (need_mask) {
+            // query qt0 + 8h + ci: visible iff ci >= dlim (causal) and ci < nlim;
+            // keys past the end see no query
+            const int dlim = GEN ? key - off - qt0 - 8 * h : key - qt0 - 8 * h;
+            const int nlim = GEN ? (key < nk ? nq - qt0 - 8 * h : -1) : (key < N ? N - qt0 - 8 * h : -1);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int ci = 16 * (i >> 3) + (i & 7);
+                if ((CAUSAL && ci < dlim) || ci >= nlim) p[i] = 0.f;
+            }
+        }
+        // per query chunk c (16 queries): dS = P (dP - D) and the packed P, dS,
+        // then its dV / dK MFMAs, which run while the next chunk is packed
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            if (c == 1) {  // the second chunk's statistics were requested after its operands
-                lgkm_wait<0>();
-#pragma unroll
-                for (int j = 0; j < 2; ++j) settle(lv[j]);
-            }
             uint32_t pw[4], dsw[4];
-            // the element-wise block, with the mask only on tiles that need it
-            // (a branch around the whole block, so it is not turned into selects)
-            auto elementwise = [&](auto mask_c) {
-                // mask bounds relative to the lane's first query qt0 + 8h; keys past
-                // the end see no query
-                const int dlim = GEN ? key - off - qt0 - 8 * h : key - qt0 - 8 * h;
-                const int nlim = GEN ? (key < nk ? nq - qt0 - 8 * h : -1) : (key < N ? N - qt0 - 8 * h : -1);
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    float p[2], ds[2];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int i = 8 * c + 2 * w + e;
-                        const int j = (i >> 2) & 1;
-                        float pv = fast_exp2(__builtin_fmaf(s[i], a.c, -lv[j][i & 3]));
-                        if constexpr (decltype(mask_c)::value) {
-                            // query qt0 + 8h + ci: visible iff ci >= dlim (causal) and ci < nlim
-                            const int ci = 16 * (i >> 3) + (i & 7);
-                            if ((CAUSAL && ci < dlim) || ci >= nlim) pv = 0.f;
-                        }
-                        p[e] = pv;
-                        ds[e] = pv * dp[i];
-                    }
-                    pw[w] = T::pack2(p[0], p[1]);
-                    dsw[w] = T::pack2(ds[0], ds[1]);
-                }
-            };
-            if (need_mask) elementwise(Masked{});
-            else elementwise(Unmasked{});
-            if (c == 0) {
-                lv[0] = ds_read128f<TO + 64>(st_base);
-                lv[1] = ds_read128f<TO + 80>(st_base);
-                lgkm_wait<10>();  // chunk 0's transposed operands (issued first) have landed
+            for (int w = 0; w < 4; ++w) {
+                const int i = 8 * c + 2 * w;
+                pw[w] = T::pack2(p[i], p[i + 1]);
+                dsw[w] = T::pack2(p[i] * dp[i], p[i + 1] * dp[i + 1]);
             }
+            if (c == 0) lgkm_wait<8>();  // chunk 0's transposed operands (issued first) have landed
+            else lgkm_wait<0>();
 #pragma unroll
             for (int u = 0; u < DT; ++u)
 #pragma unroll
