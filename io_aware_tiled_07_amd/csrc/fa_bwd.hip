@@ -437,11 +437,16 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
                 dtr[1][u][hi] = tr_read<DO + 16 * kRowB>(tr_base[u][hi]);
                 qtr[1][u][hi] = tr_read<QO + 16 * kRowB>(tr_base[u][hi]);
             }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) dp = T::mfma32(da[ks], vf[ks], dp);
+        // each dP MFMA followed by four elements of P, held in that order, so a
+        // wave's exponentials run while its matrix core works on dP
         float p[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) p[i] = fast_exp2(__builtin_fmaf(s[i], a.c, -lv[i >> 2][i & 3]));
+        for (int ks = 0; ks < KS; ++ks) {
+            dp = T::mfma32(da[ks], vf[ks], dp);
+#pragma unroll
+            for (int i = 4 * ks; i < 4 * ks + 4; ++i) p[i] = fast_exp2(__builtin_fmaf(s[i], a.c, -lv[i >> 2][i & 3]));
+            __builtin_amdgcn_sched_barrier(0);
+        }
         if (need_mask) {
             // query qt0 + 8h + ci: visible iff ci >= dlim (causal) and ci < nlim;
             // keys past the end see no query
