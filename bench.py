@@ -80,9 +80,9 @@ COPY_PROBE_KIB = 262144
 COUNTERS = {
     # workload: {stage: (FETCH_SIZE KiB, WRITE_SIZE KiB, copy FETCH_SIZE KiB, copy WRITE_SIZE KiB, sources sha)}
     "gpt2_small_causal": {
-        "fwd": (19627.2, 12672.0, 131091.9, 262144.0, "67a35d39f0ef5702"),
-        "prep": (12492.8, 768.0, 131091.9, 262144.0, "f0ce21e4f69172f9"),
-        "main": (67207.0, 36864.0, 131091.9, 262144.0, "f0ce21e4f69172f9"),
+        "fwd": (18542.5, 12672.0, 131092.9, 262144.0, "67a35d39f0ef5702"),
+        "prep": (12492.8, 768.0, 131092.9, 262144.0, "d3a271f65b1cee98"),
+        "main": (63679.8, 36864.0, 131092.9, 262144.0, "d3a271f65b1cee98"),
     },
 }
 
