@@ -154,18 +154,29 @@ def fa_fwd(q, k, v, o, lse, causal: bool = False, scale=None, stream=None) -> No
         raise FaError(st, "fa_fwd")
 
 
-def _bwd_args(q, k, v, o, do, lse, dq, dk, dv, workspace):
+def _workspace(q, need, workspace, stream=None):
+    """The caller's workspace, or a new one of ``need`` bytes allocated on the
+    stream the kernels are enqueued on: the caching allocator then hands the
+    block to later work on that stream only, which runs after the kernels, and
+    never to work on another stream while they may still use it."""
+    import torch
+    if workspace is None:
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        with torch.cuda.stream(s):
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_bhnd("workspace", workspace)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _bwd_args(q, k, v, o, do, lse, dq, dk, dv, workspace, stream):
     import torch
     B, H, N, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)):
         _check_bhnd(name, t, q.shape, q.dtype)
     _check_bhnd("lse", lse, (B, H, N), torch.float32)
     code = dtype_code(q)
-    need = fa_bwd_workspace_size(B, H, N, d, code)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _check_bhnd("workspace", workspace)
-    return code, workspace, workspace.numel() * workspace.element_size()
+    workspace, nbytes = _workspace(q, fa_bwd_workspace_size(B, H, N, d, code), workspace, stream)
+    return code, workspace, nbytes
 
 
 def fa_bwd_dq(q, k, v, o, do, lse, dq, dk, dv, causal: bool = False, scale=None,
@@ -173,7 +184,7 @@ def fa_bwd_dq(q, k, v, o, do, lse, dq, dk, dv, causal: bool = False, scale=None,
     """Enqueue the backward into caller-allocated ``dq``, ``dk``, ``dv``. ``workspace`` is a
     device tensor of at least ``fa_bwd_workspace_size`` bytes (allocated here if None)."""
     B, H, N, d = q.shape
-    code, workspace, nbytes = _bwd_args(q, k, v, o, do, lse, dq, dk, dv, workspace)
+    code, workspace, nbytes = _bwd_args(q, k, v, o, do, lse, dq, dk, dv, workspace, stream)
     st = load().fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
                           _scale(scale, d), int(bool(causal)), code, int(dq_strategy),
@@ -201,7 +212,7 @@ def fa_bwd_main(q, k, v, o, do, lse, dq, dk, dv, workspace, causal: bool = False
                 dq_strategy: int = FA_DQ_DEFAULT, stream=None) -> None:
     """Second backward stage: dQ, dK, dV from a workspace ``fa_bwd_prep`` filled."""
     B, H, N, d = q.shape
-    code, workspace, nbytes = _bwd_args(q, k, v, o, do, lse, dq, dk, dv, workspace)
+    code, workspace, nbytes = _bwd_args(q, k, v, o, do, lse, dq, dk, dv, workspace, stream)
     st = load().fa_bwd_main(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
                             _scale(scale, d), int(bool(causal)), code, int(dq_strategy),
@@ -258,14 +269,6 @@ def _mask_args(block_mask, B, H, N):
     raise ValueError(f"block_mask must be [{nb},{nb}] or [{B},{H},{nb},{nb}], got {tuple(block_mask.shape)}")
 
 
-def _workspace(q, need, workspace):
-    import torch
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _check_bhnd("workspace", workspace)
-    return workspace, workspace.numel() * workspace.element_size()
-
-
 def fa_fwd_sparse(q, k, v, o, lse, block_mask, causal: bool = False, scale=None, workspace=None,
                   stream=None) -> None:
     """Block-sparse forward into caller-allocated ``o`` and ``lse``: 128 x 128 blocks of the
@@ -276,7 +279,7 @@ def fa_fwd_sparse(q, k, v, o, lse, block_mask, causal: bool = False, scale=None,
         _check_bhnd(name, t, q.shape, q.dtype)
     _check_bhnd("lse", lse, (B, H, N), torch.float32)
     mp, stride = _mask_args(block_mask, B, H, N)
-    workspace, nbytes = _workspace(q, fa_fwd_sparse_workspace_size(B, H, N, stride), workspace)
+    workspace, nbytes = _workspace(q, fa_fwd_sparse_workspace_size(B, H, N, stride), workspace, stream)
     st = load().fa_fwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                               B, H, N, d, _scale(scale, d), int(bool(causal)), dtype_code(q), mp, stride,
                               workspace.data_ptr(), nbytes, _stream(stream))
@@ -293,7 +296,7 @@ def fa_bwd_sparse(q, k, v, o, do, lse, dq, dk, dv, block_mask, causal: bool = Fa
         _check_bhnd(name, t, q.shape, q.dtype)
     _check_bhnd("lse", lse, (B, H, N), torch.float32)
     mp, stride = _mask_args(block_mask, B, H, N)
-    workspace, nbytes = _workspace(q, fa_bwd_sparse_workspace_size(B, H, N, stride), workspace)
+    workspace, nbytes = _workspace(q, fa_bwd_sparse_workspace_size(B, H, N, stride), workspace, stream)
     st = load().fa_bwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                               lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
                               _scale(scale, d), int(bool(causal)), dtype_code(q), mp, stride,
@@ -373,7 +376,7 @@ def fa_decode(q, k, v, o, lse, causal: bool = True, scale=None, workspace=None, 
         _check_bhnd(name, t, (B, H, Nk, d), q.dtype)
     _check_bhnd("o", o, q.shape, q.dtype)
     _check_bhnd("lse", lse, (B, H, Nq), torch.float32)
-    workspace, nbytes = _workspace(q, fa_decode_workspace_size(B, H, Nq, Nk, d), workspace)
+    workspace, nbytes = _workspace(q, fa_decode_workspace_size(B, H, Nq, Nk, d), workspace, stream)
     st = load().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
                           _scale(scale, d), int(bool(causal)), dtype_code(q), workspace.data_ptr(), nbytes,
                           _stream(stream))
@@ -467,7 +470,7 @@ def fa_bwd_general(q, k, v, o, do, lse, dq, dk, dv, causal: bool = False, scale=
     _check_bhnd("lse", lse, (B, H, Nq), torch.float32)
     lens = _seqlens(B, seqlens_q, seqlens_k)
     ss = [_strides(t) for t in (q, k, v, o, do, dq, dk, dv)]
-    workspace, wbytes = _workspace(q, fa_bwd_general_workspace_size(B, H, Nq), workspace)
+    workspace, wbytes = _workspace(q, fa_bwd_general_workspace_size(B, H, Nq), workspace, stream)
     st = load().fa_bwd_general(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d,
                                _scale(scale, d), int(bool(causal)), dtype_code(q),

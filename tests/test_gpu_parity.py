@@ -85,17 +85,13 @@ def test_fp16_shapes(shape, causal):
 
 @pytest.mark.parametrize("N", [4096, 8192, 16384])
 def test_long_causal(N):
-    """Full GPU run; the oracle checks one seeded head completely (fwd and bwd)
-    and 32 seeded forward rows of every head."""
+    """Full GPU run, every output of every head against the oracle (fwd and bwd):
+    the oracle's fp64 passes over the 16 heads take about 1, 5 and 20 s at the
+    three lengths on 16 host cores."""
     log(f"long causal N={N}")
     shape = (1, 16, N, 64)
     drawn, outs = run_fwd_bwd(1004, shape, "bf16", True)
-    h = int(seedgen.choice_rows(1004, 17 + N, 16, 1)[0])
-    check_all(drawn, outs, "bf16", True, heads=[(0, h)])
-    rows = np.concatenate([hh * N + seedgen.choice_rows(1004, 40 + hh, N, 32) for hh in range(16)])
-    o_ref, lse_ref = oracle.fwd_rows(drawn[0].f64, drawn[1].f64, drawn[2].f64, scale_for(64), True, rows)
-    check("o_rows", outs[0].reshape(-1, 64)[torch.from_numpy(rows).cuda()], o_ref, "bf16")
-    check("lse_rows", outs[1].reshape(-1)[torch.from_numpy(rows).cuda()], lse_ref, "bf16")
+    check_all(drawn, outs, "bf16", True)
 
 
 def test_wide_64k_forward():
@@ -164,13 +160,12 @@ def test_ragged_backward_d128(N, causal):
 @pytest.mark.parametrize("dtype,causal", [("bf16", True), ("bf16", False), ("fp16", True)])
 def test_backward_d128(dtype, causal):
     """Head dim 128 backward over 2 x 8 heads of 2048 (XCD-grouped mapping,
-    several rounds of the 4-slot ring per workgroup): two seeded heads checked
+    several rounds of the 4-slot ring per workgroup): every head checked
     completely against the oracle."""
     log(f"bwd d=128 2x8x2048 {dtype} causal={causal}")
     shape = (2, 8, 2048, 128)
     drawn, outs = run_fwd_bwd(1128, shape, dtype, causal)
-    h0, h1 = (int(x) for x in seedgen.choice_rows(1128, 7, 8, 2))
-    check_all(drawn, outs, dtype, causal, heads=[(0, h0), (1, h1)])
+    check_all(drawn, outs, dtype, causal)
 
 
 @pytest.mark.parametrize("N", [1, 7, 129])
@@ -303,5 +298,32 @@ def test_staged_backward_matches_fa_bwd():
         if strategy == fa.FA_DQ_SEPARATE:
             assert torch.equal(dq, ref[0]) and torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
         else:  # another strategy: other summation order
+            for x, y in zip((dq, dk, dv), ref):
+                assert (x.float() - y.float()).abs().max().item() < 2e-2
+
+
+def test_backward_on_a_side_stream():
+    """The backward enqueued on a stream that is not the current one, with its
+    workspace allocated by the binding, while the current stream allocates and
+    overwrites memory at once: the results equal those of a run on the current
+    stream bit for bit (the workspace block is not handed to the other stream
+    while the kernels may still use it)."""
+    drawn = inputs(1003, (2, 3, 300, 64), "bf16")
+    q, k, v, do = to_dev(drawn)
+    o, lse = fa.fwd(q, k, v, causal=True)
+    ref = fa.bwd(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    need = fa.fa_bwd_workspace_size(2, 3, 300, 64, fa.FA_BF16)
+    side = torch.cuda.Stream()
+    for strategy in (fa.FA_DQ_SEPARATE, fa.FA_DQ_ATOMIC):
+        side.wait_stream(torch.cuda.current_stream())
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        fa.fa_bwd_dq(q, k, v, o, do, lse, dq, dk, dv, True, None, strategy, None, side)
+        junk = [torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda") for _ in range(4)]
+        torch.cuda.synchronize()
+        del junk
+        if strategy == fa.FA_DQ_SEPARATE:
+            assert torch.equal(dq, ref[0]) and torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
+        else:
             for x, y in zip((dq, dk, dv), ref):
                 assert (x.float() - y.float()).abs().max().item() < 2e-2
