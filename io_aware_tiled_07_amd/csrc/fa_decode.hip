@@ -1,7 +1,7 @@
 // Attention of a few new queries over a long key/value cache (decoding), on
 // gfx950. The cache is named beside the method by the pages (groundtruth.day,
-// payoff paragraph) and told apart from it (michaelc-yu summary, "Flash
-// Attention vs KV cache"); what runs here is still the method: the Nq x Nk
+// payoff paragraph) and told apart from it (arcflow.me "Flash Attention",
+// "Common Confusions"); what runs here is still the method: the Nq x Nk
 // scores are formed tile by tile on chip with an online softmax and never
 // written out, and each row keeps its statistic lse. The queries are the
 // last Nq positions of the sequence (causal: query t sees keys j <= t + Nk - Nq).

@@ -171,6 +171,18 @@ def test_prep_fp32_is_a_validated_no_op(lib):
     assert prep(lib, dtype=fa.FA_FP32) == fa.FA_OK
 
 
+@pytest.mark.parametrize("strategy", [fa.FA_DQ_DEFAULT, fa.FA_DQ_SEPARATE])
+@pytest.mark.parametrize("dtype", [fa.FA_BF16, fa.FA_FP16])
+def test_prep_d64_is_a_validated_no_op(lib, strategy, dtype):
+    """The 16-bit head-dim-64 backward forms D and lse*log2(e) inside its fused
+    kernel, so its first stage only validates: FA_OK without a launch (on this
+    host a launch would fail with FA_ERR_HIP). The atomic strategy and head dim
+    128 still launch their prep kernels."""
+    assert prep(lib, dtype=dtype, strategy=strategy) == fa.FA_OK
+    assert prep(lib, dtype=dtype, strategy=fa.FA_DQ_ATOMIC) == fa.FA_ERR_HIP
+    assert prep(lib, dtype=dtype, d=128, strategy=strategy) == fa.FA_ERR_HIP
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), fa.FA_ERR_INVALID_ARG),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
