@@ -1,7 +1,8 @@
 """Benchmark: exact attention forward + backward through libfa.so on one MI355X.
 
 One step = one pass of the whole path over one batch: fa_fwd (O, lse), then
-fa_bwd_prep (D, lse*log2e) and fa_bwd_main (dQ, dK, dV), on the GPT-2-small
+the backward (dQ, dK, dV; at head dim 64 one launch that forms D and
+lse*log2e itself, otherwise fa_bwd_prep and fa_bwd_main), on the GPT-2-small
 shaped causal workload (B=8, H=12, N=1024, d=64, bf16, scale 1/8) unless
 --workload says otherwise. Inputs are seeded synthetic Gaussians already
 resident in device memory when the timed region starts.
@@ -11,11 +12,17 @@ for causal. The backward alone is credited with its five matrix products,
 10*B*H*N^2*d (halved for causal), whatever the kernels recompute.
 
 The timed region is K whole steps between two HIP events on the stream the
-library enqueues on; inside it only the dominant kernel's launches are
-bracketed by events, which give its average launch duration for the roofline
-entry. The per-stage breakdown comes from a separate pass of K steps with
-events around every launch (each event adds a little to the step, so that
-pass does not set the step time). Prints one JSON line.
+library enqueues on, with nothing else inside it. The dominant kernel's
+average launch duration (for the roofline entry) comes from a pass of K steps
+of its own with events around that kernel's launches only, and the per-stage
+breakdown from another pass with events around every launch (each event adds
+a little to the step, so neither pass sets the step time). Prints one JSON
+line.
+
+``--ceilings`` instead runs the unit microbenchmarks (``fa_ceilings``, built
+from ``csrc/ceilings.hip``: chip-wide bf16 MFMA rate and clock, MFMA / FMA /
+exp issue mixes per SIMD, LDS read bandwidth per CU, HBM read bandwidth) and
+prints their JSON.
 """
 from __future__ import annotations
 
@@ -106,12 +113,15 @@ def traffic_bytes(workload, stage):
     return round((fetch * COPY_PROBE_KIB / copy_fetch + write * COPY_PROBE_KIB / copy_write) * 1024)
 
 
-def algorithmic_bytes(w, stage):
-    """Bytes a launch must move at least: every input read once, every output written once."""
+def algorithmic_bytes(w, stage, fused_prep=True):
+    """Bytes a launch must move at least: every input read once, every output written once.
+    The fused backward (head dim 64) reads q, k, v, o, dout and lse; after a prep pass it reads
+    q, k, v, dout, D and lse*log2e instead."""
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     elt = 4 if w["dtype"] == "fp32" else 2
     t, r = B * H * N * d * elt, B * H * N * 4
-    return {"fwd": 3 * t + t + r, "prep": 2 * t + r + 2 * r, "main": 4 * t + 2 * r + 3 * t}[stage]
+    main = 5 * t + r + 3 * t if fused_prep else 4 * t + 2 * r + 3 * t
+    return {"fwd": 3 * t + t + r, "prep": 2 * t + r + 2 * r, "main": main}[stage]
 
 
 def block_mask(w):
@@ -333,19 +343,24 @@ def run_decode(args, w):
         fa.fa_decode(q, k, v, o, lse, causal, scale, ws, stream)
     torch.cuda.synchronize()
     K = args.steps
+    # per-call durations from a pass of their own (events around every call)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t0.record(stream)
     for i in range(K):
         evs[i][0].record(stream)
         fa.fa_decode(q, k, v, o, lse, causal, scale, ws, stream)
         evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    call_ms = statistics.mean(a.elapsed_time(b) for a, b in evs)
+    # timed region: K calls between two events
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(K):
+        fa.fa_decode(q, k, v, o, lse, causal, scale, ws, stream)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / K
-    call_ms = statistics.mean(a.elapsed_time(b) for a, b in evs)
     nbytes = decode_bytes(w)
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     call_gbs = nbytes / (call_ms * 1e-3) / 1e9
@@ -433,16 +448,19 @@ def run_general(args, w):
     torch.cuda.synchronize()
     stage_ms = {name: statistics.mean(e[name][0].elapsed_time(e[name][1]) for e in brk) for name in stages}
     dom_ev = [{"main": ev_pair()} for _ in range(K)]
+    for i in range(K):
+        run(dom_ev[i])
+    torch.cuda.synchronize()
+    dom_ms = statistics.mean(e["main"][0].elapsed_time(e["main"][1]) for e in dom_ev)
     t_start, t_end = ev_pair()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(K):
-        run(dom_ev[i])
+        run()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / K
-    dom_ms = statistics.mean(e["main"][0].elapsed_time(e["main"][1]) for e in dom_ev)
     tf_step = flops(w, "step") / (ms_step * 1e-3) / 1e12
     dom_tf = flops(w, "bwd") / (dom_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS
@@ -503,7 +521,20 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB (a known-size "
                          "reference for hardware byte counters under a profiler)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="run the unit microbenchmarks (fa_ceilings) instead of a workload and print their JSON")
     args = ap.parse_args()
+    if args.ceilings:
+        import subprocess
+        exe = os.path.join(ROOT, "io_aware_tiled_07_amd", "fa_ceilings")
+        if not os.path.exists(exe):
+            raise RuntimeError(f"{exe} is not built; run __graft_entry__.build() first")
+        r = subprocess.run([exe], capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stderr)
+            sys.exit(r.returncode)
+        print(json.dumps({"ceilings": json.loads(r.stdout)}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the kernels are measured on "
               "one GPU's share of the work at its real shape; see the sharding notes in the design document.",
@@ -553,8 +584,10 @@ def main():
         mask_dev = torch.from_numpy(mask_np).to(dev)
         ws_f = torch.empty(fa.fa_fwd_sparse_workspace_size(B, H, N, 0), dtype=torch.uint8, device=dev)
         ws_b = torch.empty(fa.fa_bwd_sparse_workspace_size(B, H, N, 0), dtype=torch.uint8, device=dev)
-    else:
+    elif args.dq == "atomic" or w["dtype"] == "fp32" or d != 64:
         stages = ("fwd", "prep", "main")
+    else:
+        stages = ("fwd", "main")  # head dim 64: the backward is one launch (fa_bwd_prep enqueues nothing)
 
     def run(evs=None):
         """One step; evs maps a stage name to the (start, end) events recorded around it."""
@@ -592,20 +625,26 @@ def main():
     stage_ms = {name: statistics.mean(e[name][0].elapsed_time(e[name][1]) for e in brk) for name in stages}
     dom = "main" if "main" in stage_ms and stage_ms["main"] >= stage_ms["fwd"] else "fwd"
 
-    # Timed region: K whole steps; only the dominant kernel's launches carry
-    # events, which give its average launch duration for the roofline entry.
+    # Dominant kernel: a pass of K steps with events around its launches only,
+    # which gives its average launch duration for the roofline entry (the
+    # figure includes the dispatch gap in front of each launch).
     dom_ev = [{dom: ev_pair()} for _ in range(K)]
+    for i in range(K):
+        run(dom_ev[i])
+    torch.cuda.synchronize()
+    dom_ms = statistics.mean(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev)
+
+    # Timed region: K whole steps between two events, nothing else inside.
     t_start, t_end = ev_pair()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(K):
-        run(dom_ev[i])
+        run()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / K
-    dom_ms = statistics.mean(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev)
 
     step_rule = "fwd" if fwd_only else "step"
     tf_step = flops(w, step_rule) / (ms_step * 1e-3) / 1e12
@@ -623,9 +662,11 @@ def main():
         "bound": "mfma", "achieved": round(dom_tf, 2), "peak": peak, "unit": "TFLOP/s",
         "frac": round(dom_tf / peak, 4), "traffic": traffic_bytes(args.workload, dom) if args.dq == "default" else None,
         "traffic_unit": "bytes per launch beyond L2 (copy-calibrated FETCH_SIZE + WRITE_SIZE)",
-        "algorithmic_bytes": algorithmic_bytes(w, dom),
+        "algorithmic_bytes": algorithmic_bytes(w, dom, "prep" not in stages),
         "kernel": KERNELS[dom] if single else f"fa_bwd_main ({'atomic main + convert' if not fp32 else 'fp32'})",
         "flop_per_launch": dom_flop, "avg_launch_ms": round(dom_ms, 5),
+        "avg_launch_source": "HIP events around the kernel's launches in a pass of K steps of their own, "
+                             "outside the timed region (includes the dispatch gap in front of each launch)",
         "flop_rule": "fwd 4*B*H*N^2*d, bwd 10*B*H*N^2*d (five products), halved for causal",
     }
     if fp8:

@@ -80,7 +80,25 @@ def build(jobs: int = 4, extra_flags=(), lib_path: str = LIB) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, lib_path)
+    if lib_path == LIB:
+        build_ceilings()
     return lib_path
+
+
+CEILINGS_SRC = "ceilings.hip"
+CEILINGS = os.path.join(HERE, "fa_ceilings")
+
+
+def build_ceilings() -> str:
+    """Compile the unit-ceiling microbenchmarks (``csrc/ceilings.hip``) into the
+    program ``fa_ceilings`` next to the library (``bench.py --ceilings`` runs it)."""
+    tmp = CEILINGS + ".tmp"
+    cmd = [hipcc()] + flags(CEILINGS_SRC) + [os.path.join(CSRC, CEILINGS_SRC), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {CEILINGS_SRC}:\n{r.stderr}")
+    os.replace(tmp, CEILINGS)
+    return CEILINGS
 
 
 if __name__ == "__main__":
