@@ -18,8 +18,9 @@
  * [B, H, N] float array. Every pointer is a device pointer, 16-byte aligned.
  *
  * Ownership: every buffer belongs to the caller. The library keeps no pointer
- * after a call returns, allocates no device memory, has no global mutable
- * state and is reentrant. Outputs must not overlap inputs.
+ * after a call returns, allocates no device memory and is reentrant; its only
+ * global state is the fixed per-device scratch buffer of fa_decode_noalloc (and
+ * that buffer's looked-up address per device). Outputs must not overlap inputs.
  *
  * Execution: a call only enqueues kernels on `stream` (a hipStream_t; NULL is
  * the default stream) and returns without synchronising. Device faults show
@@ -52,7 +53,9 @@ typedef enum {
                                 unknown dQ strategy, FA_DQ_ATOMIC with 16-bit d = 128 */
     FA_ERR_WORKSPACE = 3,    /* workspace null, not 256-byte aligned, or smaller than
                                 fa_bwd_workspace_size() */
-    FA_ERR_HIP = 4           /* a kernel launch failed (hipGetLastError after launch) */
+    FA_ERR_HIP = 4,          /* a kernel launch failed (hipGetLastError after launch) */
+    FA_ERR_SCRATCH = 5       /* fa_decode_noalloc: the shape needs more scratch than the
+                                library's fixed per-device buffer (FA_DECODE_SCRATCH_BYTES) */
 } fa_status;
 
 /* How fa_bwd_dq() forms dQ. */
@@ -209,6 +212,28 @@ size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d);
 int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. The per-split partial results go to a fixed buffer of
+ * FA_DECODE_SCRATCH_BYTES that the library holds in each device's memory for
+ * the life of the process; the call allocates nothing. Same arguments,
+ * semantics and results as fa_decode (the same kernels and split plan), except:
+ *   - shapes whose fa_decode_workspace_size() exceeds FA_DECODE_SCRATCH_BYTES are
+ *     rejected with FA_ERR_SCRATCH (checked before any HIP call);
+ *   - `stream` must belong to the current device (else FA_ERR_INVALID_ARG);
+ *   - every call on a device shares that device's buffer: calls that may overlap
+ *     on one device (several streams, several host threads) race and must be
+ *     serialised by the caller. Calls on different devices do not interact.
+ * The buffer's contents between calls are unspecified (each call writes every
+ * part it reads). On first use on a device the library looks up the buffer's
+ * address there (hipGetSymbolAddress; a failure returns FA_ERR_HIP).
+ */
+#define FA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                      void* stream);
 
 /*
  * General shapes for the 16-bit forward: strided layouts (for instance [B,N,H,d]

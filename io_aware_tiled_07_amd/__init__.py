@@ -9,7 +9,8 @@ The raw entry points keep the C names (``fa_fwd``, ``fa_bwd``, ``fa_bwd_dq``,
 ``fa_bwd_prep``, ``fa_bwd_main``, ``fa_bwd_workspace_size``, ``fa_status_string``,
 for block-sparse attention ``fa_fwd_sparse``, ``fa_bwd_sparse`` and their
 workspace sizes, the FP8 forward ``fa_fwd_fp8``, and attention over a key/value
-cache ``fa_decode`` with ``fa_decode_workspace_size``, and the forward and
+cache ``fa_decode`` with ``fa_decode_workspace_size`` (and ``fa_decode_noalloc``, which
+uses the library's fixed scratch buffer instead of a workspace), and the forward and
 backward over general shapes ``fa_fwd_general``, ``fa_bwd_general``) and take caller-allocated
 torch tensors; ``fwd``, ``bwd``, ``fwd_sparse``, ``bwd_sparse``, ``fwd_fp8``,
 ``decode``, ``fwd_general`` and ``bwd_general`` allocate their outputs.
@@ -27,12 +28,14 @@ __all__ = [
     "fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_prep", "fa_bwd_main", "fwd", "bwd", "dtype_code",
     "FA_SPARSE_BLOCK", "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size", "fa_fwd_sparse",
     "fa_bwd_sparse", "fwd_sparse", "bwd_sparse", "fa_fwd_fp8", "fwd_fp8", "fa_decode_workspace_size",
-    "fa_decode", "decode", "fa_fwd_general", "fwd_general",
+    "fa_decode", "decode", "fa_decode_noalloc", "FA_ERR_SCRATCH", "FA_DECODE_SCRATCH_BYTES",
+    "fa_fwd_general", "fwd_general",
     "fa_bwd_general_workspace_size", "fa_bwd_general", "bwd_general",
 ]
 
 FA_BF16, FA_FP16, FA_FP32 = 0, 1, 2
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_SCRATCH = 0, 1, 2, 3, 4, 5
+FA_DECODE_SCRATCH_BYTES = 16 << 20  # fa.h: the fixed scratch buffer of fa_decode_noalloc
 FA_DQ_DEFAULT, FA_DQ_ATOMIC, FA_DQ_SEPARATE = 0, 1, 2
 FA_SPARSE_BLOCK = 128
 
@@ -89,6 +92,8 @@ def load():
         lib.fa_decode_workspace_size.restype = _sz
         lib.fa_decode.argtypes = [_vp] * 5 + [_i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz, _vp]
         lib.fa_decode.restype = _i
+        lib.fa_decode_noalloc.argtypes = [_vp] * 5 + [_i, _i, _i, _i, _i, _f, _i, _i, _vp]
+        lib.fa_decode_noalloc.restype = _i
         lib.fa_fwd_general.argtypes = [_vp] * 5 + [_i, _i, _i, _i, _i, _f, _i, _i] + [_vp] * 7
         lib.fa_fwd_general.restype = _i
         lib.fa_bwd_general_workspace_size.argtypes = [_i, _i, _i]
@@ -382,6 +387,26 @@ def fa_decode(q, k, v, o, lse, causal: bool = True, scale=None, workspace=None, 
                           _stream(stream))
     if st != FA_OK:
         raise FaError(st, "fa_decode")
+
+
+def fa_decode_noalloc(q, k, v, o, lse, causal: bool = True, scale=None, stream=None) -> None:
+    """``fa_decode`` into caller-allocated ``o`` and ``lse`` with the library's fixed
+    per-device scratch buffer instead of a workspace: allocates nothing. Calls that may
+    overlap on one device share that buffer and must be serialised by the caller."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B,H,N,d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _check_bhnd("q", q)
+    for name, t in (("k", k), ("v", v)):
+        _check_bhnd(name, t, (B, H, Nk, d), q.dtype)
+    _check_bhnd("o", o, q.shape, q.dtype)
+    _check_bhnd("lse", lse, (B, H, Nq), torch.float32)
+    st = load().fa_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq,
+                                  Nk, d, _scale(scale, d), int(bool(causal)), dtype_code(q), _stream(stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode_noalloc")
 
 
 def decode(q, k, v, causal: bool = True, scale=None, stream=None):

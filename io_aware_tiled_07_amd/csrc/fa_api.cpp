@@ -197,6 +197,7 @@ const char* fa_status_string(int status) {
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported dtype / head dim / strategy";
         case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
         case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed";
+        case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: shape needs more than the fixed scratch buffer of fa_decode_noalloc";
         default: return "unknown fa_status";
     }
 }
@@ -433,8 +434,14 @@ size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d) {
     return decode_layout(B, H, Nq, Nk, d).bytes;
 }
 
-int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
-              int d, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of fa_decode except the workspace (shared with fa_decode_noalloc).
+// `extra` is a further output range (the workspace) that must not overlap the others.
+int check_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                 int d, float scale, int causal, int dtype, Range extra) {
     if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (Nq > kDecodeMaxQ) return FA_ERR_UNSUPPORTED;
@@ -448,10 +455,8 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
     const void* ptrs[] = {q, k, v, o, lse};
     for (const void* p : ptrs)
         if (p == nullptr || !aligned16(p)) return FA_ERR_INVALID_ARG;
-    const DecodeLayout L = decode_layout(B, H, Nq, Nk, d);
-    if (workspace == nullptr || !aligned256(workspace) || workspace_bytes < L.bytes) return FA_ERR_WORKSPACE;
     const size_t qbytes = (size_t)bh * Nq * d * 2, kvbytes = (size_t)bh * Nk * d * 2;
-    const Range outs[] = {range(o, qbytes), range(lse, (size_t)bh * Nq * sizeof(float)), range(workspace, L.bytes)};
+    const Range outs[] = {range(o, qbytes), range(lse, (size_t)bh * Nq * sizeof(float)), extra};
     const Range ins[] = {range(q, qbytes), range(k, kvbytes), range(v, kvbytes)};
     for (int i = 0; i < 3; ++i) {
         for (const Range& r : ins)
@@ -459,11 +464,53 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, 
         for (int j = i + 1; j < 3; ++j)
             if (overlap(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
     }
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+              int d, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    const DecodeLayout L = decode_layout(B, H, Nq, Nk, d);
+    int st = check_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype,
+                          workspace ? range(workspace, L.bytes) : Range{0, 0});
+    if (st != FA_OK) return st;
+    if (workspace == nullptr || !aligned256(workspace) || workspace_bytes < L.bytes) return FA_ERR_WORKSPACE;
     char* base = static_cast<char*>(workspace);
     (void)hipGetLastError();
     const hipError_t e = fa::decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype,
                                     reinterpret_cast<float*>(base + L.part_o), reinterpret_cast<float*>(base + L.part_lse),
                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                      int Nk, int d, float scale, int causal, int dtype, void* stream) {
+    int st = check_decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, dtype, Range{0, 0});
+    if (st != FA_OK) return st;
+    const DecodeLayout L = decode_layout(B, H, Nq, Nk, d);
+    if (L.bytes > FA_DECODE_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+    static_assert(FA_DECODE_SCRATCH_BYTES == fa::kDecodeScratchBytes, "the header's limit is the buffer's size");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    int dev = -1, sdev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || hipStreamGetDevice(s, &sdev) != hipSuccess) return FA_ERR_HIP;
+    if (dev != sdev) return FA_ERR_INVALID_ARG;
+    char* base = nullptr;
+    if (fa::decode_scratch(reinterpret_cast<void**>(&base)) != hipSuccess) return FA_ERR_HIP;
+    // the buffer must not overlap the caller's tensors
+    const int64_t bh = (int64_t)B * H;
+    const Range rs = range(base, L.bytes);
+    const Range rt[] = {range(q, (size_t)bh * Nq * d * 2), range(k, (size_t)bh * Nk * d * 2),
+                        range(v, (size_t)bh * Nk * d * 2), range(o, (size_t)bh * Nq * d * 2),
+                        range(lse, (size_t)bh * Nq * sizeof(float))};
+    for (const Range& r : rt)
+        if (overlap(rs, r)) return FA_ERR_INVALID_ARG;
+    const hipError_t e = fa::decode(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal != 0, dtype,
+                                    reinterpret_cast<float*>(base + L.part_o),
+                                    reinterpret_cast<float*>(base + L.part_lse), s);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

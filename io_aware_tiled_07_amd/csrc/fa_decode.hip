@@ -21,8 +21,17 @@
 // merged with the rule above.
 // decode_merge_kernel: merges the splits of every (batch, head, query), one
 // workgroup per row.
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_internal.h"
+
+// Fixed per-device scratch for fa_decode_noalloc (callers that cannot
+// allocate): the split partials of a call live here instead of in a caller's
+// workspace. In host code the name is only a stand-in for the symbol; its
+// device address comes from hipGetSymbolAddress (decode_scratch below), and the
+// kernels receive that address as an argument, as they receive a workspace.
+static __device__ __align__(256) char scratch[fa::kDecodeScratchBytes];
 
 namespace fa {
 
@@ -287,6 +296,28 @@ hipError_t launch_d(const DecArgs& a, bool causal, hipStream_t s) {
 }
 
 }  // namespace
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // address of `scratch` on each device; nullptr until looked up
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // the current device's copy
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 DecodeSplit decode_split(int B, int H, int Nk) {
     // about 1,024 workgroups (4 per CU), each reading at least 256 keys: more

@@ -94,6 +94,10 @@ struct DecodeSplit {
 DecodeSplit decode_split(int B, int H, int Nk);
 hipError_t decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
                   int d, float scale, bool causal, int dtype, float* part_o, float* part_lse, hipStream_t stream);
+// The fixed scratch buffer of fa_decode_noalloc on the current device: its
+// device address, looked up (hipGetSymbolAddress) on first use per device.
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch(void** ptr);
 
 // fp32 forward and backward, d = 64.
 hipError_t fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,

@@ -38,14 +38,14 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_prep", "fa_bwd_main",
                           "fa_bwd_workspace_size", "fa_status_string", "fa_fwd_sparse", "fa_bwd_sparse",
                           "fa_fwd_sparse_workspace_size", "fa_bwd_sparse_workspace_size", "fa_fwd_fp8",
-                          "fa_decode", "fa_decode_workspace_size", "fa_fwd_general",
+                          "fa_decode", "fa_decode_workspace_size", "fa_decode_noalloc", "fa_fwd_general",
                           "fa_bwd_general_workspace_size", "fa_bwd_general"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         assert fa.fa_status_string(code)
     assert "unknown" in fa.fa_status_string(99)
 
@@ -357,6 +357,37 @@ def dec(lib, B=2, H=3, Nq=1, Nk=1000, d=64, causal=1, dtype=0, ws=None, ws_bytes
 ])
 def test_decode_rejects(lib, kw, code):
     assert dec(lib, **kw) == code
+
+
+def dec_noalloc(lib, B=2, H=3, Nq=1, Nk=1000, d=64, causal=1, dtype=0, **over):
+    names = ["q", "k", "v", "o", "lse"]
+    p = dict(zip(names, ptrs(5)))
+    p.update({k: v for k, v in over.items() if k in names})
+    return lib.fa_decode_noalloc(*[ctypes.c_void_p(p[n]) for n in names], B, H, Nq, Nk, d, ctypes.c_float(0.125),
+                                 causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=fa.FA_FP32), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nq=9), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=4, Nk=3), fa.FA_ERR_INVALID_ARG),
+    (dict(k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=A + GAP), fa.FA_ERR_INVALID_ARG),          # o aliases k
+    # 4096 x 64 heads of 8 queries, d = 128: one split each, 2 M partial rows (> 16 MiB);
+    # tensors 2^40 bytes apart so that they do not overlap
+    (dict(B=4096, H=64, Nq=8, Nk=256, d=128, **{n: A + i * (1 << 40) for i, n in enumerate("q k v o lse".split())}),
+     fa.FA_ERR_SCRATCH),
+])
+def test_decode_noalloc_rejects(lib, kw, code):
+    """Every check, including the scratch limit, runs before any HIP call."""
+    assert dec_noalloc(lib, **kw) == code
+
+
+def test_decode_noalloc_limit_is_the_workspace_size():
+    """A shape fits the fixed buffer iff fa_decode's workspace for it does."""
+    assert fa.fa_decode_workspace_size(8, 32, 8, 16384, 128) <= fa.FA_DECODE_SCRATCH_BYTES
+    assert fa.fa_decode_workspace_size(4096, 64, 8, 256, 128) > fa.FA_DECODE_SCRATCH_BYTES
 
 
 # ---------------------------------------------------------------- general shapes
