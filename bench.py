@@ -1,8 +1,7 @@
 """Benchmark: exact attention forward + backward through libfa.so on one MI355X.
 
 One step = one pass of the whole path over one batch: fa_fwd (O, lse), then
-the backward (dQ, dK, dV; at head dim 64 one launch that forms D and
-lse*log2e itself, otherwise fa_bwd_prep and fa_bwd_main), on the GPT-2-small
+the backward (fa_bwd_prep: D and lse*log2e; fa_bwd_main: dQ, dK, dV), on the GPT-2-small
 shaped causal workload (B=8, H=12, N=1024, d=64, bf16, scale 1/8) unless
 --workload says otherwise. Inputs are seeded synthetic Gaussians already
 resident in device memory when the timed region starts.
@@ -48,6 +47,8 @@ WORKLOADS = {
     "gpt2_small_causal": dict(B=8, H=12, N=1024, d=64, causal=True, dtype="bf16", seed=1003, mul=1.0),
     "bert_large": dict(B=8, H=16, N=512, d=64, causal=False, dtype="bf16", seed=1002, mul=1.0),
     "long_causal_16k": dict(B=1, H=16, N=16384, d=64, causal=True, dtype="bf16", seed=1004, mul=1.0),
+    # head dim 128 forward + backward (prep pass + fused launch with accumulators in AGPRs)
+    "long_causal_8k_d128": dict(B=1, H=16, N=8192, d=128, causal=True, dtype="bf16", seed=1010, mul=1.0),
     # 64K tokens, head dim 128, forward only (inputs scaled by 0.5); the CPU baseline
     # times the oracle on 256 seeded rows, 32 per head
     "wide_64k_fwd": dict(B=1, H=8, N=65536, d=128, causal=False, dtype="bf16", seed=1005, mul=0.5,
@@ -113,15 +114,14 @@ def traffic_bytes(workload, stage):
     return round((fetch * COPY_PROBE_KIB / copy_fetch + write * COPY_PROBE_KIB / copy_write) * 1024)
 
 
-def algorithmic_bytes(w, stage, fused_prep=True):
+def algorithmic_bytes(w, stage):
     """Bytes a launch must move at least: every input read once, every output written once.
-    The fused backward (head dim 64) reads q, k, v, o, dout and lse; after a prep pass it reads
-    q, k, v, dout, D and lse*log2e instead."""
+    prep reads o, dout and lse and writes D and lse*log2e; the fused backward reads q, k, v,
+    dout, D and lse*log2e and writes dq, dk and dv."""
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     elt = 4 if w["dtype"] == "fp32" else 2
     t, r = B * H * N * d * elt, B * H * N * 4
-    main = 5 * t + r + 3 * t if fused_prep else 4 * t + 2 * r + 3 * t
-    return {"fwd": 3 * t + t + r, "prep": 2 * t + r + 2 * r, "main": main}[stage]
+    return {"fwd": 3 * t + t + r, "prep": 2 * t + r + 2 * r, "main": 4 * t + 2 * r + 3 * t}[stage]
 
 
 def block_mask(w):
@@ -497,7 +497,8 @@ def run_general(args, w):
                 "tflops_10x": round(flops(w, "bwd") / (stage_ms["main"] * 1e-3) / 1e12, 3)},
         "roofline": {"bound": "mfma", "achieved": round(dom_tf, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(dom_tf / peak, 4), "traffic": None, "algorithmic_bytes": None,
-                     "kernel": "fa_bwd_general: bwd_prep_kernel (general) + bwd_fused_kernel (general)",
+                     "kernel": "fa_bwd_general: bwd_prep_kernel (general) + "
+                               + ("bwd128_fused_kernel" if d == 128 else "bwd_fused_kernel") + " (general)",
                      "flop_per_launch": flops(w, "bwd"), "avg_launch_ms": round(dom_ms, 5),
                      "flop_rule": "bwd 10*H*d per visible query-key pair of each sequence"},
         "cpu_baseline": cpu, "wall_s_timed": round(wall, 4),
@@ -584,10 +585,8 @@ def main():
         mask_dev = torch.from_numpy(mask_np).to(dev)
         ws_f = torch.empty(fa.fa_fwd_sparse_workspace_size(B, H, N, 0), dtype=torch.uint8, device=dev)
         ws_b = torch.empty(fa.fa_bwd_sparse_workspace_size(B, H, N, 0), dtype=torch.uint8, device=dev)
-    elif args.dq == "atomic" or w["dtype"] == "fp32" or d != 64:
-        stages = ("fwd", "prep", "main")
     else:
-        stages = ("fwd", "main")  # head dim 64: the backward is one launch (fa_bwd_prep enqueues nothing)
+        stages = ("fwd", "prep", "main")
 
     def run(evs=None):
         """One step; evs maps a stage name to the (start, end) events recorded around it."""
@@ -662,8 +661,9 @@ def main():
         "bound": "mfma", "achieved": round(dom_tf, 2), "peak": peak, "unit": "TFLOP/s",
         "frac": round(dom_tf / peak, 4), "traffic": traffic_bytes(args.workload, dom) if args.dq == "default" else None,
         "traffic_unit": "bytes per launch beyond L2 (copy-calibrated FETCH_SIZE + WRITE_SIZE)",
-        "algorithmic_bytes": algorithmic_bytes(w, dom, "prep" not in stages),
-        "kernel": KERNELS[dom] if single else f"fa_bwd_main ({'atomic main + convert' if not fp32 else 'fp32'})",
+        "algorithmic_bytes": algorithmic_bytes(w, dom),
+        "kernel": (("bwd128_fused_kernel" if d == 128 else KERNELS[dom]) if dom == "main" else KERNELS[dom]) if single
+                  else f"fa_bwd_main ({'atomic main + convert' if not fp32 else 'fp32'})",
         "flop_per_launch": dom_flop, "avg_launch_ms": round(dom_ms, 5),
         "avg_launch_source": "HIP events around the kernel's launches in a pass of K steps of their own, "
                              "outside the timed region (includes the dispatch gap in front of each launch)",
@@ -675,7 +675,8 @@ def main():
     if sparse:
         roofline.update({
             "traffic": None, "algorithmic_bytes": None,
-            "kernel": ("fa_bwd_sparse: mask packing + bwd_prep_kernel + bwd_fused_kernel (sparse)" if dom == "main"
+            "kernel": ("fa_bwd_sparse: mask packing + bwd_prep_kernel + " + ("bwd128_fused_kernel" if d == 128 else "bwd_fused_kernel")
+                       + " (sparse)" if dom == "main"
                        else "fa_fwd_sparse: mask packing + fwd_kernel (sparse)"),
             "flop_rule": "fwd 4*B*H*d, bwd 10*B*H*d, per query-key pair kept by the block mask",
         })

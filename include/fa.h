@@ -97,10 +97,7 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int dtype);
  * Reads only q, k, v, o, dout and lse; recomputes every score and probability tile
  * on chip from them (michaelc-yu summary of Dao et al., "Backward / recomputation").
  * 16-bit inputs: d in {64, 128}; fp32: d = 64. Uses the default dQ strategy.
- * Equivalent to fa_bwd_prep() followed by fa_bwd_main(). For 16-bit d = 64 (default
- * or separate strategy) it is one kernel launch that forms D_i = dO_i . O_i and
- * lse_i * log2(e) where they are used and leaves the workspace untouched (the
- * workspace is still validated). Returns a fa_status.
+ * Equivalent to fa_bwd_prep() followed by fa_bwd_main(). Returns a fa_status.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv,
@@ -118,9 +115,8 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const 
  * First stage of the backward, for callers that schedule the stages themselves:
  * one pass over o and dout that writes D_i = dO_i . O_i and lse_i * log2(e) into
  * the workspace (and, for FA_DQ_ATOMIC, zeroes its fp32 dQ accumulator). For
- * FA_FP32, and for 16-bit d = 64 with the default or separate strategy, it
- * validates and returns without a launch (those backwards form D themselves in
- * fa_bwd_main). Arguments as fa_bwd_dq(). Returns a fa_status.
+ * FA_FP32 it validates and returns (the fp32 backward forms D in fa_bwd_main).
+ * Arguments as fa_bwd_dq(). Returns a fa_status.
  */
 int fa_bwd_prep(const void* o, const void* dout, const float* lse, int B, int H, int N, int d, int dtype,
                 int dq_strategy, void* workspace, size_t workspace_bytes, void* stream);

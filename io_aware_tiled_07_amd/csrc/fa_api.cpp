@@ -252,9 +252,6 @@ int fa_bwd_prep(const void* o, const void* dout, const float* lse, int B, int H,
         return FA_ERR_INVALID_ARG;
 
     if (dtype == FA_FP32) return FA_OK;  // the fp32 backward forms D itself in fa_bwd_main
-    // the 16-bit d = 64 backward (separate dQ pass) forms D and lse * log2(e)
-    // inside its fused kernel: nothing to enqueue
-    if (d == 64 && dq_strategy != FA_DQ_ATOMIC) return FA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* base = static_cast<char*>(workspace);
     float* delta = reinterpret_cast<float*>(base + w.delta);
@@ -290,7 +287,8 @@ int fa_bwd_main(const void* q, const void* k, const void* v, const void* o, cons
         e = fa::bwd128_fused(q, k, v, dout, delta, reinterpret_cast<const float*>(base + w.lse2), dq, dk, dv, B, H,
                              N, scale, causal != 0, dtype, s);
     } else {
-        e = fa::bwd_fused(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, scale, causal != 0, dtype, s);
+        e = fa::bwd_fused(q, k, v, dout, delta, reinterpret_cast<const float*>(base + w.lse2), dq, dk, dv, B, H, N,
+                          scale, causal != 0, dtype, s);
     }
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -393,16 +391,14 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, co
     (void)hipGetLastError();
     hipError_t e = fa::sparse_mask_bits(static_cast<const uint8_t*>(block_mask), mask_head_stride, L.nm, L.nb, rows,
                                         cols, s);
+    if (e == hipSuccess) e = fa::bwd_prep(o, dout, lse, B, H, N, d, dtype, delta, lse2, s);
     if (e == hipSuccess) {
-        if (d == 128) {
-            e = fa::bwd_prep(o, dout, lse, B, H, N, d, dtype, delta, lse2, s);
-            if (e == hipSuccess)
-                e = fa::bwd128_fused_sparse(q, k, v, dout, delta, lse2, dq, dk, dv, B, H, N, scale, causal != 0,
-                                            dtype, rows, cols, L.W, L.head_words, s);
-        } else {
-            e = fa::bwd_fused_sparse(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, scale, causal != 0, dtype, rows,
+        if (d == 128)
+            e = fa::bwd128_fused_sparse(q, k, v, dout, delta, lse2, dq, dk, dv, B, H, N, scale, causal != 0, dtype,
+                                        rows, cols, L.W, L.head_words, s);
+        else
+            e = fa::bwd_fused_sparse(q, k, v, dout, delta, lse2, dq, dk, dv, B, H, N, scale, causal != 0, dtype, rows,
                                      cols, L.W, L.head_words, s);
-        }
     }
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -614,15 +610,15 @@ int fa_bwd_general(const void* q, const void* k, const void* v, const void* o, c
     float* delta = reinterpret_cast<float*>(base);
     float* lse2 = reinterpret_cast<float*>(base + need / 2);
     (void)hipGetLastError();
-    hipError_t e;
-    if (d == 128) {
-        e = fa::bwd_prep_general(o, dout, lse, B, H, Nq, d, dtype, st[7], st[3], seqlens_q, delta, lse2, s);
-        if (e == hipSuccess)
+    // st[7] (o's strides) serves the prep pass only
+    hipError_t e = fa::bwd_prep_general(o, dout, lse, B, H, Nq, d, dtype, st[7], st[3], seqlens_q, delta, lse2, s);
+    if (e == hipSuccess) {
+        if (d == 128)
             e = fa::bwd128_fused_general(q, k, v, dout, delta, lse2, dq, dk, dv, B, H, Nq, Nk, scale, causal != 0,
                                          dtype, st, seqlens_q, seqlens_k, s);
-    } else {
-        e = fa::bwd_fused_general(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, Nk, scale, causal != 0, dtype, st,
-                                  seqlens_q, seqlens_k, s);
+        else
+            e = fa::bwd_fused_general(q, k, v, dout, delta, lse2, dq, dk, dv, B, H, Nq, Nk, scale, causal != 0, dtype,
+                                      st, seqlens_q, seqlens_k, s);
     }
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -11,26 +11,23 @@
 //   dS_ij = P_ij (dP_ij - D_i)
 //   dV_j  = sum_i P_ij dO_i,   dK_j = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j
 //
-// One launch on the caller's stream, bwd_fused: a grid holding two kinds of
-// workgroups, which share no data and run side by side:
+// Two launches on the caller's stream:
+//  1. bwd_prep: D_i and lse_i * log2(e) for every query row, into the
+//     workspace (memory bound: reads O and dO once).
+//  2. bwd_fused: one grid holding two kinds of workgroups, which share no
+//     data and run side by side:
 //     * key workgroups (128 keys, 32 per wave): K and V rows of the wave stay
 //       in VGPRs, dK^T and dV^T in fp32 accumulators. Query stages (64 rows of
-//       Q and dO and their lse) stream HBM -> LDS through a 4-slot LDS-DMA
-//       ring; each wave also copies the O rows matching the 16 dO rows it
-//       copied and forms D_i = dO_i . O_i for them (and wave 0 lse_i * log2 e
-//       for the stage) into the stage's statistics, one stage ahead of use.
-//       Per 32 queries a wave forms S = Q K^T and dP = dO V^T (lane = key),
-//       then P and dS in registers, then dV^T += dO^T P and dK^T += Q^T dS
-//       with the dO^T / Q^T operands read transposed from LDS
+//       Q and dO and their statistics) stream HBM -> LDS through a 4-slot
+//       LDS-DMA ring; per 32 queries a wave forms S = Q K^T and dP = dO V^T
+//       (lane = key), then P and dS in registers, then dV^T += dO^T P and
+//       dK^T += Q^T dS with the dO^T / Q^T operands read transposed from LDS
 //       (ds_read_b64_tr_b16).
-//     * query workgroups (128 queries, 32 per wave): Q, dO and O rows are read
-//       into VGPRs (D of the lane's row from the last two), K and V blocks of
-//       64 keys stream through the same kind of ring (the forward's layout); a
-//       wave forms S^T = K Q^T and dP^T = V dO^T (lane = query), dS^T in
-//       registers, and dQ^T += K^T dS^T with K^T read transposed from LDS.
-//     D and lse * log2 e are formed where they are used, so the backward needs
-//     no pass of its own over O and dO and no workspace. (bwd_prep_kernel
-//     still writes them to memory for the head-dim-128 backward.)
+//     * query workgroups (128 queries, 32 per wave): Q and dO rows stay in
+//       VGPRs, K and V blocks of 64 keys stream through the same kind of ring
+//       (the forward's layout); a wave forms S^T = K Q^T and dP^T = V dO^T
+//       (lane = query), dS^T in registers, and dQ^T += K^T dS^T with K^T read
+//       transposed from LDS.
 //     Work is handed out longest first, alternating the two kinds, and every
 //     workgroup of one (batch, head) goes to the same XCD so its tensors are
 //     reused from that XCD's L2.
@@ -71,7 +68,7 @@ constexpr int kKvKeys = 128;                 // keys per workgroup (32 per wave)
 constexpr int kKvQRows = 64;                 // query rows per ring stage
 constexpr int kKvTileB = kKvQRows * kRowB;   // bytes of the Q (or dO) part of a stage
 constexpr int kKvTC = kKvTileB / 1024;       // 1 KiB chunks of that part
-constexpr int kKvStatB = 256;                // 64 floats of lse*log2e, then 64 of -D
+constexpr int kKvStatB = 256;                // 64 floats of lse*log2e, then 64 of D
 constexpr int kKvRowsOff = 2 * kKvStatB;     // the Q rows follow the statistics, then the dO rows
 constexpr int kKvStage = 2 * kKvTileB + 2 * kKvStatB;
 constexpr int kKvCpw = 2 * kKvTC / 4;        // 16-byte DMA instructions per wave per stage
@@ -84,12 +81,7 @@ constexpr int kQTC = kQTileB / 1024;
 constexpr int kQStage = 2 * kQTileB;
 constexpr int kQCpw = 2 * kQTC / 4;
 
-// key workgroups: each wave's copy of the O rows of one query stage (the 16
-// rows of the two 1 KiB chunks its Q/dO copies carry), after the ring
-constexpr int kOWave = 2 * 1024;
-constexpr int kOArea = kSlots * (kKvStage > kQStage ? kKvStage : kQStage);
-constexpr int kSmem = kOArea + 4 * kOWave;
-static_assert(kSmem <= 80 * 1024, "two workgroups per CU");
+constexpr int kSmem = kSlots * (kKvStage > kQStage ? kKvStage : kQStage);
 // largest immediate LDS offsets: the last slot's dO rows of the second half plus a
 // 16-row chunk (key workgroups; the row bases carry kKvRowsOff), and the last
 // slot's V rows plus 32 rows or three 16-row chunks (query workgroups)
@@ -120,8 +112,8 @@ struct FusedArgs {
     const uint16_t* k;
     const uint16_t* v;
     const uint16_t* dout;
-    const uint16_t* o;  // the forward's output (D_i = dO_i . O_i is formed here)
-    const float* lse;   // the forward's natural-log lse, [BH][N]
+    const float* lse2;   // lse * log2(e), [BH][N]
+    const float* delta;  // -D (negated), [BH][N]
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
@@ -137,9 +129,9 @@ struct FusedArgs {
     int W, nb;
     int64_t head_words;
     // general shapes: element strides (batch, head, row) of q, k, v, dout, dq,
-    // dk, dv, o (in that order); N is the query extent, Nk the key extent;
+    // dk, dv (in that order); N is the query extent, Nk the key extent;
     // per-sequence lengths (nullptr: the extents); causal alignment at the end
-    int64_t st[8][3];
+    int64_t st[7][3];
     int H, Nk;
     const int* lens_q;
     const int* lens_k;
@@ -240,11 +232,11 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     const size_t head = (size_t)bh * N * D;
     const uint16_t* __restrict__ Q = a.q + head;
     const uint16_t* __restrict__ dO = a.dout + head;
-    const uint16_t* __restrict__ Ob = a.o + head;
-    const float* __restrict__ lse = a.lse + (size_t)bh * N;
+    const float* __restrict__ lse2 = a.lse2 + (size_t)bh * N;
+    const float* __restrict__ delta = a.delta + (size_t)bh * N;
     // general shapes: this sequence's lengths, offset, bases and row strides (elements)
     int nq = N, nk = N, off = 0;
-    int64_t q_rs = D, do_rs = D, o_rs = D, k_rs = D, v_rs = D, dk_rs = D, dv_rs = D;
+    int64_t q_rs = D, do_rs = D, k_rs = D, v_rs = D, dk_rs = D, dv_rs = D;
     const uint16_t* Kb = a.k + head;
     const uint16_t* Vb = a.v + head;
     uint16_t* dKb = a.dk + head;
@@ -260,14 +252,12 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         Kb = a.k + b * a.st[1][0] + hh * a.st[1][1];
         Vb = a.v + b * a.st[2][0] + hh * a.st[2][1];
         dO = a.dout + b * a.st[3][0] + hh * a.st[3][1];
-        Ob = a.o + b * a.st[7][0] + hh * a.st[7][1];
         dKb = a.dk + b * a.st[5][0] + hh * a.st[5][1];
         dVb = a.dv + b * a.st[6][0] + hh * a.st[6][1];
         q_rs = a.st[0][2];
         k_rs = a.st[1][2];
         v_rs = a.st[2][2];
         do_rs = a.st[3][2];
-        o_rs = a.st[7][2];
         dk_rs = a.st[5][2];
         dv_rs = a.st[6][2];
     }
@@ -294,16 +284,12 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
     int slot_unit[kSlots];  // query stage (64 rows) held by each ring slot
 
     // Stage s (query stage g0 + s; rows past the end read as zeros and are
-    // masked) in slot s % kSlots: [lse2 x64][-D x64][Q rows][dO rows]. Chunk c
-    // (1 KiB) of the Q/dO part is written by wave c % 4; lane l of it carries
-    // tile row 8 (c % kKvTC) + l / 8, stored chunk l % 8; the same lane offsets
-    // serve Q and dO. Wave 0 also copies the stage's lse (turned into
-    // lse * log2 e in place once it has landed), and each wave copies the O
-    // rows of its own dO rows into its O area, from which it forms -D of those
-    // rows (stage_stats).
+    // masked) in slot s % kSlots: [lse2 x64][D x64][Q rows][dO rows]. Chunk c (1 KiB)
+    // of the Q/dO part is written by wave c % 4; lane l of it carries tile row
+    // 8 (c % kKvTC) + l / 8, stored chunk l % 8; the same lane offsets serve Q
+    // and dO. Waves 0 and 1 also copy the statistics.
     uint32_t dma_off[kKvTC / 4];
     uint32_t dma_off_d[GEN ? kKvTC / 4 : 1];  // dO rows when strided differently from Q
-    uint32_t dma_off_o[GEN ? kKvTC / 4 : 1];  // O rows when strided differently from Q
 #pragma unroll
     for (int j = 0; j < kKvTC / 4; ++j) {
         const int p = (j * 4 + wave) * 64 + lane;
@@ -311,46 +297,32 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         if constexpr (GEN) {
             dma_off[j] = (uint32_t)(row * q_rs * 2) + c * 16;
             dma_off_d[j] = (uint32_t)(row * do_rs * 2) + c * 16;
-            dma_off_o[j] = (uint32_t)(row * o_rs * 2) + c * 16;
         } else {
             dma_off[j] = (uint32_t)((row * D + c * 8) * 2);
         }
     }
-    // live = false: a stage past the last one, copied as zeros (empty buffer
-    // resources, no memory read), so the prologue issues the same copies on
-    // every path
-    auto issue = [&](int s, int slot, bool live = true) {
-        const int g = !live ? 0 : SPARSE ? walk.next() : g0 + s;
+    auto issue = [&](int s, int slot) {
+        const int g = SPARSE ? walk.next() : g0 + s;
         slot_unit[slot] = g;
         const int r0 = g * kKvQRows;
         char* sb = smem + slot * kKvStage + kKvRowsOff + wave * 1024;
-        i32x4 qr, dr;
-        if (!live) {
-            qr = dr = buffer_rsrc(Q, 0);
-        } else if constexpr (GEN) {
-            qr = strided_rows_rsrc<kRowB>(Q, nq, r0, (uint32_t)(q_rs * 2));
-            dr = strided_rows_rsrc<kRowB>(dO, nq, r0, (uint32_t)(do_rs * 2));
+        if constexpr (GEN) {
+            const i32x4 qr = strided_rows_rsrc<kRowB>(Q, nq, r0, (uint32_t)(q_rs * 2));
+            const i32x4 dr = strided_rows_rsrc<kRowB>(dO, nq, r0, (uint32_t)(do_rs * 2));
+#pragma unroll
+            for (int j = 0; j < kKvTC / 4; ++j) dma16(qr, dma_off[j], sb + j * 4 * 1024);
+#pragma unroll
+            for (int j = 0; j < kKvTC / 4; ++j) dma16(dr, dma_off_d[j], sb + kKvTileB + j * 4 * 1024);
         } else {
-            qr = rows_rsrc<kRowB>(Q, N, r0);
-            dr = rows_rsrc<kRowB>(dO, N, r0);
+            const i32x4 qr = rows_rsrc<kRowB>(Q, N, r0), dr = rows_rsrc<kRowB>(dO, N, r0);
+#pragma unroll
+            for (int j = 0; j < kKvTC / 4; ++j) dma16(qr, dma_off[j], sb + j * 4 * 1024);
+#pragma unroll
+            for (int j = 0; j < kKvTC / 4; ++j) dma16(dr, dma_off[j], sb + kKvTileB + j * 4 * 1024);
         }
-#pragma unroll
-        for (int j = 0; j < kKvTC / 4; ++j) dma16(qr, dma_off[j], sb + j * 4 * 1024);
-#pragma unroll
-        for (int j = 0; j < kKvTC / 4; ++j) dma16(dr, GEN ? dma_off_d[j] : dma_off[j], sb + kKvTileB + j * 4 * 1024);
-        if (wave == 0)
-            dma4(live ? rows_rsrc<4>(lse, nq, r0) : buffer_rsrc(lse, 0), (uint32_t)lane * 4, smem + slot * kKvStage);
-    };
-    // O rows of query stage g matching this wave's dO rows, into its O area
-    auto issue_o = [&](int g, bool live = true) {
-        const int r0 = g * kKvQRows;
-        char* ob = smem + kOArea + wave * kOWave;
-        i32x4 orr;
-        if (!live) orr = buffer_rsrc(Ob, 0);
-        else if constexpr (GEN) orr = strided_rows_rsrc<kRowB>(Ob, nq, r0, (uint32_t)(o_rs * 2));
-        else orr = rows_rsrc<kRowB>(Ob, N, r0);
-#pragma unroll
-        for (int j = 0; j < kKvTC / 4; ++j) dma16(orr, GEN ? dma_off_o[j] : dma_off[j], ob + j * 1024);
+        if (wave < 2)
+            dma4(rows_rsrc<4>(wave == 0 ? lse2 : delta, nq, r0), (uint32_t)lane * 4,
+                 smem + slot * kKvStage + wave * kKvStatB);
     };
 
     // Loop-invariant LDS addresses; the slot, half and chunk parts are immediates.
@@ -372,52 +344,6 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
                                                     (32 * u + 16 * (g16 & 1) + 4 * (L16 & 3)) >> 3) +
                                         (L16 & 1) * 8);
     const uint32_t st_base = smem_addr + (uint32_t)(4 * 8 * h);
-
-    // -D of the stage's rows: lane l of wave w takes local row l / 4 of the 16
-    // rows its copies carry (8 w + l/4, or 32 + 8 w + l/4 - 8) and logical
-    // chunks 2 (l % 4), 2 (l % 4) + 1 of it, from the dO rows of the stage and
-    // from the wave's O area (chunk j of the area holds rows 8 (4 j + w) ..
-    // + 7, stored in the stage's swizzled row layout).
-    const int drl = lane >> 2, dpart = lane & 3;
-    const int drow = drl < 8 ? 8 * wave + drl : 32 + 8 * wave + (drl - 8);
-    uint32_t dd_addr[2], do_addr[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int ch = 2 * dpart + i;
-        dd_addr[i] = smem_addr + (uint32_t)tile_off<D>(drow, ch);
-        do_addr[i] = smem_addr + kOArea + wave * kOWave + (drl >> 3) * 1024 +
-                     (uint32_t)((drow & 7) * kRowB + ((ch ^ swz<D>(drow)) << 4));
-    }
-    const uint32_t dst_addr = smem_addr + (uint32_t)(4 * drow);
-    const uint32_t lse_addr = smem_addr + (uint32_t)(4 * lane);
-    // Called once this wave's copies of the stage in slot SLOT and of its O rows
-    // have landed; the next barrier publishes what it writes.
-    auto stage_stats = [&](auto slot_c) {
-        constexpr int SO = decltype(slot_c)::value * kKvStage;
-        const u32x4 x0 = ds_read128<SO + kKvRowsOff + kKvTileB>(dd_addr[0]);
-        const u32x4 x1 = ds_read128<SO + kKvRowsOff + kKvTileB>(dd_addr[1]);
-        const u32x4 y0 = ds_read128<0>(do_addr[0]);
-        const u32x4 y1 = ds_read128<0>(do_addr[1]);
-        float l = 0.f;
-        if (wave == 0) l = ds_read32f<SO>(lse_addr);
-        lgkm_wait<0>();
-        u32x4 xs0 = x0, xs1 = x1, ys0 = y0, ys1 = y1;
-        settle(xs0);
-        settle(xs1);
-        settle(ys0);
-        settle(ys1);
-        settle(l);
-        float acc = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            acc = T::dot2(xs0[w], ys0[w], acc);
-            acc = T::dot2(xs1[w], ys1[w], acc);
-        }
-        acc = quad_sum(acc);
-        if (dpart == 0) ds_write32f<SO + kKvStatB>(dst_addr, -acc);
-        if (wave == 0) ds_write32f<SO>(lse_addr, l * kLog2e);
-        lgkm_wait<0>();
-    };
 
     // K and V rows (B operands of S = Q K^T and dP = dO V^T, k = head dim)
     // first, then the first kSlots - 1 stages (those that exist); the wait
@@ -444,18 +370,11 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
             }
         }
     }
-    // stage 0 and its O rows, then stages 1 .. kSlots - 2 (zeros past the
-    // last stage), the same copies on every path; stage 0's statistics are
-    // formed once it has landed, each later stage's at the end of the ring
-    // round before it. The wait also tells the compiler's wait pass that the
-    // K/V loads above are complete, so it adds no wait in the loop.
-    issue(0, 0, nst > 0);
-    issue_o(slot_unit[0], nst > 0);
 #pragma unroll
-    for (int i = 1; i < kSlots - 1; ++i) issue(i, i, i < nst);
-    if (wave == 0) wait_vmcnt<(kSlots - 2) * (kKvCpw + 1)>();
-    else wait_vmcnt<(kSlots - 2) * kKvCpw>();
-    stage_stats(Int<0>{});
+    for (int i = 0; i < kSlots - 1; ++i)
+        if (i < nst) issue(i, i);
+    if (wave < 2) wait_stages<kKvCpw + 1, kSlots - 1>(min(kSlots - 1, nst));
+    else wait_stages<kKvCpw, kSlots - 1>(min(kSlots - 1, nst));
 
     // One unit: 32 queries (half HH of the stage in slot SLOT) against the
     // wave's 32 keys.
@@ -570,12 +489,12 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
 
     for_ring<kSlots>(nst, [&](auto slot_c, int s) {
         constexpr int SLOT = decltype(slot_c)::value;
-        // stage s and its statistics are in LDS (every wave waited for its own
-        // copies and wrote its statistics before this barrier); every wave is
-        // done with stage s - 1, whose slot the next issue overwrites, and with
-        // its O area
+        // stage s has landed (the stages after it may still be in flight); every
+        // wave is done with stage s - 1, whose slot the next issue overwrites
+        const int ahead = min(kSlots - 2, nst - 1 - s);  // stages requested after s
+        if (wave < 2) wait_stages<kKvCpw + 1, kSlots - 2>(ahead);
+        else wait_stages<kKvCpw, kSlots - 2>(ahead);
         barrier();
-        if (s + 1 < nst) issue_o(SPARSE ? slot_unit[(SLOT + 1) % kSlots] : g0 + s + 1);
         if (s + kSlots - 1 < nst) issue(s + kSlots - 1, (SLOT + kSlots - 1) % kSlots);
         const int g = SPARSE ? slot_unit[SLOT] : g0 + s;
         auto half = [&](auto hh_c) {
@@ -587,23 +506,10 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         };
         half(Int<0>{});
         half(Int<1>{});
-        if (s + 1 < nst) {
-            // stage s + 1 and its O rows have landed once at most stage s + 3
-            // (issued after them) is in flight
-            if (s + kSlots - 1 < nst) {
-                if (wave == 0) wait_vmcnt<kKvCpw + 1>();
-                else wait_vmcnt<kKvCpw>();
-            } else {
-                wait_vmcnt<0>();
-            }
-            stage_stats(Int<(SLOT + 1) % kSlots>{});
-        }
     });
 
     // dK, dV go out row by row through a ring slot no wave reads any more (the
-    // last stage's barrier retired every earlier stage; the zero copies of
-    // stages past the end are waited for here)
-    wait_vmcnt<0>();
+    // last stage's barrier retired every earlier stage; nothing is in flight)
     {
         char* stage = smem + (nst % kSlots) * kKvStage + wave * (2048 * DT);
         if constexpr (GEN) {
@@ -627,10 +533,9 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
     const uint16_t* __restrict__ V = a.v + head;
     // general shapes: this sequence's lengths, offset, bases and row strides (elements)
     int nq = N, nk = N, off = 0;
-    int64_t q_rs = D, do_rs = D, o_rs = D, k_rs = D, v_rs = D, dq_rs = D;
+    int64_t q_rs = D, do_rs = D, k_rs = D, v_rs = D, dq_rs = D;
     const uint16_t* Qb = a.q + head;
     const uint16_t* dOb = a.dout + head;
-    const uint16_t* Ob = a.o + head;
     uint16_t* dQb = a.dq + head;
     if constexpr (GEN) {
         const int b = bh / a.H, hh = bh % a.H;
@@ -643,13 +548,11 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
         K = a.k + b * a.st[1][0] + hh * a.st[1][1];
         V = a.v + b * a.st[2][0] + hh * a.st[2][1];
         dOb = a.dout + b * a.st[3][0] + hh * a.st[3][1];
-        Ob = a.o + b * a.st[7][0] + hh * a.st[7][1];
         dQb = a.dq + b * a.st[4][0] + hh * a.st[4][1];
         q_rs = a.st[0][2];
         k_rs = a.st[1][2];
         v_rs = a.st[2][2];
         do_rs = a.st[3][2];
-        o_rs = a.st[7][2];
         dq_rs = a.st[4][2];
     }
 
@@ -739,20 +642,17 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
                                                     (L16 & 1) * 8);
 
     // Q and dO rows (B operands of S^T = K Q^T and dP^T = V dO^T, k = head
-    // dim), the O row and the lse first, then the first ring stages, waited
-    // for as in the key workgroups. The lane holds elements 16 ks + 8 h .. + 7
-    // of its row; D of the row is its half of dO . O plus the partner lane's.
-    u32x4 qf[KS], dof[KS], of[KS];
+    // dim) and the row statistics first, then the first ring stages, waited
+    // for as in the key workgroups.
+    u32x4 qf[KS], dof[KS];
     {
         if constexpr (GEN) {
             const uint16_t* qp = Qb + (size_t)qload * q_rs + 8 * h;
             const uint16_t* dp = dOb + (size_t)qload * do_rs + 8 * h;
-            const uint16_t* op = Ob + (size_t)qload * o_rs + 8 * h;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 qf[ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
                 dof[ks] = *reinterpret_cast<const u32x4*>(dp + 16 * ks);
-                of[ks] = *reinterpret_cast<const u32x4*>(op + 16 * ks);
             }
         } else {
             const size_t off = head + (size_t)qload * D + 8 * h;
@@ -760,22 +660,16 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
             for (int ks = 0; ks < KS; ++ks) {
                 qf[ks] = *reinterpret_cast<const u32x4*>(a.q + off + 16 * ks);
                 dof[ks] = *reinterpret_cast<const u32x4*>(a.dout + off + 16 * ks);
-                of[ks] = *reinterpret_cast<const u32x4*>(a.o + off + 16 * ks);
             }
         }
     }
-    const float lse_ld = a.lse[(size_t)bh * N + qload];
+    const float l2q_ld = a.lse2[(size_t)bh * N + qload];
+    const float nd_ld = a.delta[(size_t)bh * N + qload];
 #pragma unroll
     for (int i = 0; i < kSlots - 1; ++i)
         if (i < nkb) issue(i, i);
     wait_stages<kQCpw, kSlots - 1>(min(kSlots - 1, nkb));
-    const float l2q = lse_ld * kLog2e;
-    float dsum = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) dsum = T::dot2(dof[ks][w], of[ks][w], dsum);
-    const float nd = -pair_sum(dsum);
+    const float l2q = l2q_ld, nd = nd_ld;
     // -D of this lane's query, broadcast: the initial dP^T accumulator of every
     // key tile, so the MFMAs produce dP - D directly
     f32x16 nd_init;
@@ -967,16 +861,16 @@ hipError_t bwd_prep(const void* o, const void* dout, const float* lse, int B, in
     return hipGetLastError();
 }
 
-hipError_t bwd_fused(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                     void* dq, void* dk, void* dv, int B, int H, int N, float scale, bool causal, int dtype,
-                     hipStream_t stream) {
+hipError_t bwd_fused(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                     const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale, bool causal,
+                     int dtype, hipStream_t stream) {
     FusedArgs a;
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
     a.dout = static_cast<const uint16_t*>(dout);
-    a.o = static_cast<const uint16_t*>(o);
-    a.lse = lse;
+    a.lse2 = lse2;
+    a.delta = delta;
     a.dq = static_cast<uint16_t*>(dq);
     a.dk = static_cast<uint16_t*>(dk);
     a.dv = static_cast<uint16_t*>(dv);
@@ -992,8 +886,8 @@ hipError_t bwd_fused(const void* q, const void* k, const void* v, const void* o,
     return dtype == 0 ? launch_fused<Bf16, false>(a, causal, stream) : launch_fused<F16, false>(a, causal, stream);
 }
 
-hipError_t bwd_fused_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                            const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, float scale,
+hipError_t bwd_fused_sparse(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                            const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale,
                             bool causal, int dtype, const uint64_t* mask_rows, const uint64_t* mask_cols, int W,
                             int64_t head_words, hipStream_t stream) {
     FusedArgs a;
@@ -1001,8 +895,8 @@ hipError_t bwd_fused_sparse(const void* q, const void* k, const void* v, const v
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
     a.dout = static_cast<const uint16_t*>(dout);
-    a.o = static_cast<const uint16_t*>(o);
-    a.lse = lse;
+    a.lse2 = lse2;
+    a.delta = delta;
     a.dq = static_cast<uint16_t*>(dq);
     a.dk = static_cast<uint16_t*>(dk);
     a.dv = static_cast<uint16_t*>(dv);
@@ -1049,8 +943,8 @@ hipError_t bwd_prep_general(const void* o, const void* dout, const float* lse, i
     return hipGetLastError();
 }
 
-hipError_t bwd_fused_general(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                             const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+hipError_t bwd_fused_general(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                             const float* lse2, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
                              float scale, bool causal, int dtype, const int64_t (*st)[3], const int* lens_q,
                              const int* lens_k, hipStream_t stream) {
     FusedArgs a;
@@ -1058,8 +952,8 @@ hipError_t bwd_fused_general(const void* q, const void* k, const void* v, const 
     a.k = static_cast<const uint16_t*>(k);
     a.v = static_cast<const uint16_t*>(v);
     a.dout = static_cast<const uint16_t*>(dout);
-    a.o = static_cast<const uint16_t*>(o);
-    a.lse = lse;
+    a.lse2 = lse2;
+    a.delta = delta;
     a.dq = static_cast<uint16_t*>(dq);
     a.dk = static_cast<uint16_t*>(dk);
     a.dv = static_cast<uint16_t*>(dv);
@@ -1072,7 +966,7 @@ hipError_t bwd_fused_general(const void* q, const void* k, const void* v, const 
     a.mask_rows = a.mask_cols = nullptr;
     a.W = a.nb = 0;
     a.head_words = 0;
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 7; ++t)
         for (int i = 0; i < 3; ++i) a.st[t][i] = st[t][i];
     a.H = H;
     a.Nk = Nk;

@@ -59,10 +59,6 @@ struct Bf16 {
     __device__ __forceinline__ static float sum2(uint32_t packed, float acc) {
         return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(packed), bitcast<bf16x2>(0x3F803F80u), acc, false);
     }
-    // acc + a.lo b.lo + a.hi b.hi of two packed pairs (the products are exact in fp32)
-    __device__ __forceinline__ static float dot2(uint32_t a, uint32_t b, float acc) {
-        return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(a), bitcast<bf16x2>(b), acc, false);
-    }
 };
 
 struct F16 {
@@ -83,10 +79,6 @@ struct F16 {
     // acc + lo + hi of a packed pair (v_dot2c_f32_f16 against (1, 1))
     __device__ __forceinline__ static float sum2(uint32_t packed, float acc) {
         return __builtin_amdgcn_fdot2(bitcast<f16x2>(packed), bitcast<f16x2>(0x3C003C00u), acc, false);
-    }
-    // acc + a.lo b.lo + a.hi b.hi of two packed pairs (the products are exact in fp32)
-    __device__ __forceinline__ static float dot2(uint32_t a, uint32_t b, float acc) {
-        return __builtin_amdgcn_fdot2(bitcast<f16x2>(a), bitcast<f16x2>(b), acc, false);
     }
 };
 
@@ -351,21 +343,6 @@ __device__ __forceinline__ f32x4 ds_read128f(uint32_t addr) {
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
     return r;
 }
-template <int OFF>
-__device__ __forceinline__ float ds_read32f(uint32_t addr) {
-    static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
-    float r;
-    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-    return r;
-}
-// LDS store issued from inline asm (the compiler's wait pass would otherwise
-// wait for every LDS-DMA copy in flight before it). Completion is tracked by
-// lgkmcnt: wait for it before a barrier that publishes the value.
-template <int OFF>
-__device__ __forceinline__ void ds_write32f(uint32_t addr, float v) {
-    static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
-    asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
-}
 // s_waitcnt lgkmcnt(N): at most N LDS (or scalar-memory) operations of this
 // wave still outstanding; LDS operations complete in issue order.
 template <int N>
@@ -408,13 +385,6 @@ __device__ __forceinline__ float pair_max(float x) {
 __device__ __forceinline__ float pair_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Sum over each group of four adjacent lanes (DPP quad permutations).
-__device__ __forceinline__ float quad_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
-    return x;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

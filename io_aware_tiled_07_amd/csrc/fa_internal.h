@@ -13,16 +13,14 @@ namespace fa {
 hipError_t fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                     int N, int d, float scale, bool causal, int dtype, hipStream_t stream);
 
-// 16-bit backward, default strategy. d = 64: one fused launch for dQ, dK, dV
-// that forms D_i = dO_i . O_i and lse_i * log2(e) itself from o, dout and the
-// forward's lse (bwd_fused). d = 128: -D_i and lse_i * log2(e) into delta /
-// lse2 ([B,H,N] float each) first (bwd_prep), then the fused launch
-// (bwd128_fused).
+// 16-bit backward, default strategy: -D_i = -dO_i . O_i and lse_i * log2(e)
+// into delta / lse2 ([B,H,N] float each; d in {64, 128}), then one fused
+// launch for dQ, dK, dV (bwd_fused: d = 64, bwd128_fused: d = 128).
 hipError_t bwd_prep(const void* o, const void* dout, const float* lse, int B, int H, int N, int d, int dtype,
                     float* delta, float* lse2, hipStream_t stream);
-hipError_t bwd_fused(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                     void* dq, void* dk, void* dv, int B, int H, int N, float scale, bool causal, int dtype,
-                     hipStream_t stream);
+hipError_t bwd_fused(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                     const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale, bool causal,
+                     int dtype, hipStream_t stream);
 hipError_t bwd128_fused(const void* q, const void* k, const void* v, const void* dout, const float* delta,
                         const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale, bool causal,
                         int dtype, hipStream_t stream);
@@ -45,8 +43,8 @@ hipError_t sparse_mask_bits(const uint8_t* mask, int64_t head_stride, int nm, in
 hipError_t fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                       float scale, bool causal, int dtype, const uint64_t* mask_rows, int W, int64_t head_words,
                       hipStream_t stream);
-hipError_t bwd_fused_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                            const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, float scale,
+hipError_t bwd_fused_sparse(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                            const float* lse2, void* dq, void* dk, void* dv, int B, int H, int N, float scale,
                             bool causal, int dtype, const uint64_t* mask_rows, const uint64_t* mask_cols, int W,
                             int64_t head_words, hipStream_t stream);
 hipError_t bwd128_fused_sparse(const void* q, const void* k, const void* v, const void* dout, const float* delta,
@@ -62,15 +60,14 @@ hipError_t fwd_general(const void* q, const void* k, const void* v, void* o, flo
                        const int64_t* sv, const int64_t* so, const int* lens_q, const int* lens_k,
                        hipStream_t stream);
 
-// Backward over the same general shapes: st holds the strides of q, k, v,
-// dout, dq, dk, dv, o in that order. d = 64: one fused launch (D and
-// lse * log2 e formed inside); d = 128: prep over strided o / dout (rows past a
-// sequence's queries are skipped), then the fused launch.
+// Backward over the same general shapes: prep over strided o / dout (rows past a
+// sequence's queries are skipped), then the fused launch; st holds the strides
+// of q, k, v, dout, dq, dk, dv in that order.
 hipError_t bwd_prep_general(const void* o, const void* dout, const float* lse, int B, int H, int Nq, int d,
                             int dtype, const int64_t* so, const int64_t* sd, const int* lens_q, float* delta,
                             float* lse2, hipStream_t stream);
-hipError_t bwd_fused_general(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                             const float* lse, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
+hipError_t bwd_fused_general(const void* q, const void* k, const void* v, const void* dout, const float* delta,
+                             const float* lse2, void* dq, void* dk, void* dv, int B, int H, int Nq, int Nk,
                              float scale, bool causal, int dtype, const int64_t (*st)[3], const int* lens_q,
                              const int* lens_k, hipStream_t stream);
 hipError_t bwd128_fused_general(const void* q, const void* k, const void* v, const void* dout, const float* delta,

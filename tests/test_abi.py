@@ -171,16 +171,16 @@ def test_prep_fp32_is_a_validated_no_op(lib):
     assert prep(lib, dtype=fa.FA_FP32) == fa.FA_OK
 
 
-@pytest.mark.parametrize("strategy", [fa.FA_DQ_DEFAULT, fa.FA_DQ_SEPARATE])
+@pytest.mark.parametrize("strategy", [fa.FA_DQ_DEFAULT, fa.FA_DQ_SEPARATE, fa.FA_DQ_ATOMIC])
 @pytest.mark.parametrize("dtype", [fa.FA_BF16, fa.FA_FP16])
-def test_prep_d64_is_a_validated_no_op(lib, strategy, dtype):
-    """The 16-bit head-dim-64 backward forms D and lse*log2(e) inside its fused
-    kernel, so its first stage only validates: FA_OK without a launch (on this
-    host a launch would fail with FA_ERR_HIP). The atomic strategy and head dim
-    128 still launch their prep kernels."""
-    assert prep(lib, dtype=dtype, strategy=strategy) == fa.FA_OK
-    assert prep(lib, dtype=dtype, strategy=fa.FA_DQ_ATOMIC) == fa.FA_ERR_HIP
-    assert prep(lib, dtype=dtype, d=128, strategy=strategy) == fa.FA_ERR_HIP
+@pytest.mark.parametrize("d", [64, 128])
+def test_prep_launches_for_16bit(lib, strategy, dtype, d):
+    """The 16-bit backward's first stage enqueues its prep kernel for every head
+    dim and strategy: on this host (no GPU) the launch fails with FA_ERR_HIP,
+    after every argument check has passed. (16-bit d = 128 has no atomic
+    strategy.)"""
+    want = fa.FA_ERR_UNSUPPORTED if (d == 128 and strategy == fa.FA_DQ_ATOMIC) else fa.FA_ERR_HIP
+    assert prep(lib, dtype=dtype, d=d, strategy=strategy) == want
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -44,8 +44,7 @@ def test_algorithmic_bytes_by_hand():
     t, r = 1 * 2 * 3 * 4 * 2, 1 * 2 * 3 * 4
     assert bench.algorithmic_bytes(w, "fwd") == 4 * t + r          # read Q, K, V; write O, lse
     assert bench.algorithmic_bytes(w, "prep") == 2 * t + 3 * r     # read O, dO, lse; write D, lse2
-    assert bench.algorithmic_bytes(w, "main") == 8 * t + r         # read Q, K, V, O, dO, lse; write dQ, dK, dV
-    assert bench.algorithmic_bytes(w, "main", fused_prep=False) == 7 * t + 2 * r  # read Q, K, V, dO, lse2, D
+    assert bench.algorithmic_bytes(w, "main") == 7 * t + 2 * r     # read Q, K, V, dO, lse2, D; write dQ, dK, dV
 
 
 def test_traffic_is_calibrated_and_goes_stale(monkeypatch):

@@ -32,7 +32,8 @@ def asm(request):
 
 def kernels(text):
     """(name, body) of every kernel function in the assembly."""
-    names = re.findall(r"^(_Z\w+):\s", text, flags=re.M)
+    funcs = set(re.findall(r"^\s*\.type\s+(_Z\w+),@function", text, flags=re.M))
+    names = [n for n in re.findall(r"^(_Z\w+):\s", text, flags=re.M) if n in funcs]  # not data (e.g. __device__ arrays)
     out = []
     for n in names:
         start = text.index(f"\n{n}:")

@@ -94,6 +94,14 @@ def test_long_causal(N):
     check_all(drawn, outs, "bf16", True)
 
 
+def test_long_causal_d128():
+    """The head-dim-128 backward workload (1 x 16 x 8192 x 128, causal): every output
+    of every head against the oracle."""
+    log("long causal d=128 N=8192")
+    drawn, outs = run_fwd_bwd(1010, (1, 16, 8192, 128), "bf16", True)
+    check_all(drawn, outs, "bf16", True)
+
+
 def test_wide_64k_forward():
     """64K tokens, d = 128, forward only: 256 seeded rows (32 per head) against the oracle."""
     log("64K wide forward")
