@@ -588,10 +588,11 @@ def main():
     else:
         stages = ("fwd", "prep", "main")
 
-    def run(evs=None):
-        """One step; evs maps a stage name to the (start, end) events recorded around it."""
+    def run(evs=None, only=None):
+        """One step (or only the stage named by `only`); evs maps a stage name to the
+        (start, end) events recorded around it."""
         evs = evs or {}
-        for name in stages:
+        for name in (stages if only is None else (only,)):
             if name in evs: evs[name][0].record(stream)
             if fp8:
                 fa.fa_fwd_fp8(q, k, v, o, lse, causal, scale, 1.0, 1.0, 1.0, stream)
@@ -632,6 +633,15 @@ def main():
         run(dom_ev[i])
     torch.cuda.synchronize()
     dom_ms = statistics.mean(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev)
+    # the same kernel launched K times back to back between two events (its inputs
+    # as the step leaves them): the launch duration plus the gap between queued launches
+    b2b = ev_pair()
+    b2b[0].record(stream)
+    for i in range(K):
+        run(only=dom)
+    b2b[1].record(stream)
+    torch.cuda.synchronize()
+    dom_b2b_ms = b2b[0].elapsed_time(b2b[1]) / K
 
     # Timed region: K whole steps between two events, nothing else inside.
     t_start, t_end = ev_pair()
@@ -744,7 +754,8 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "wall_s_timed": round(wall, 4),
         "dominant_launch_ms": {"median": round(statistics.median(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev), 5),
                                "min": round(min(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev), 5),
-                               "max": round(max(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev), 5)},
+                               "max": round(max(e[dom][0].elapsed_time(e[dom][1]) for e in dom_ev), 5),
+                               "back_to_back": round(dom_b2b_ms, 5)},
         "cold": cold, "sclk": sclk,
     }
     print(json.dumps(out), flush=True)
