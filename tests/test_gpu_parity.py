@@ -182,6 +182,16 @@ def test_ragged_fp32(N):
     check_all(drawn, outs, "fp32", True)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_several_blocks(causal):
+    """fp32 over 2 x 3 heads of 300 rows: 19 workgroups of 16 rows per head,
+    five 64-row blocks with a ragged last one, every lane's key subset and the
+    16-lane merge exercised; all tensors against the oracle."""
+    log(f"fp32 2x3x300 causal={causal}")
+    drawn, outs = run_fwd_bwd(4400 + causal, (2, 3, 300, 64), "fp32", causal)
+    check_all(drawn, outs, "fp32", causal)
+
+
 def test_custom_scale():
     drawn = inputs(5000, (2, 2, 200, 64), "bf16", with_do=False)
     q, k, v = to_dev(drawn)
