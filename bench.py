@@ -88,9 +88,9 @@ COPY_PROBE_KIB = 262144
 COUNTERS = {
     # workload: {stage: (FETCH_SIZE KiB, WRITE_SIZE KiB, copy FETCH_SIZE KiB, copy WRITE_SIZE KiB, sources sha)}
     "gpt2_small_causal": {
-        "fwd": (18542.5, 12672.0, 131092.9, 262144.0, "67a35d39f0ef5702"),
-        "prep": (12492.8, 768.0, 131092.9, 262144.0, "d3a271f65b1cee98"),
-        "main": (63679.8, 36864.0, 131092.9, 262144.0, "d3a271f65b1cee98"),
+        "fwd": (18625.5, 12672.0, 131089.0, 262144.0, "67a35d39f0ef5702"),
+        "prep": (12492.7, 768.0, 131089.0, 262144.0, "08c771edc271bfbc"),
+        "main": (76104.4, 36864.0, 131089.0, 262144.0, "08c771edc271bfbc"),
     },
 }
 

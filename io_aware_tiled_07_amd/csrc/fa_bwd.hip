@@ -407,16 +407,11 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
         lv[1] = ds_read128f<TO + 16>(st_base);
         lv[2] = ds_read128f<TO + 64>(st_base);
         lv[3] = ds_read128f<TO + 80>(st_base);
-        lgkm_wait<0>();
+        // the Q rows (issued first) are all the S MFMAs need
+        lgkm_wait<12>();
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) { settle(qa[ks]); settle(da[ks]); }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { settle(nd[j]); settle(lv[j]); }
+        for (int ks = 0; ks < KS; ++ks) settle(qa[ks]);
         f32x16 s = f32x16{}, dp;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dp[4 * j + e] = nd[j][e];
         // S first: P needs only S, so its exponentials run beside the dP MFMAs
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) s = T::mfma32(qa[ks], kf[ks], s);
@@ -437,6 +432,17 @@ __device__ __forceinline__ void kv_body(const FusedArgs& a, int bh, int kb, char
                 dtr[1][u][hi] = tr_read<DO + 16 * kRowB>(tr_base[u][hi]);
                 qtr[1][u][hi] = tr_read<QO + 16 * kRowB>(tr_base[u][hi]);
             }
+        // dO rows, -D and lse * log2(e) have landed once at most 15 LDS reads are
+        // outstanding (the 16 transposed reads were issued after them)
+        lgkm_wait<15>();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) settle(da[ks]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { settle(nd[j]); settle(lv[j]); }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[4 * j + e] = nd[j][e];
         // each dP MFMA followed by four elements of P, held in that order, so a
         // wave's exponentials run while its matrix core works on dP
         float p[16];
@@ -680,50 +686,51 @@ __device__ __forceinline__ void q_body(const FusedArgs& a, int bh, int qb, char*
         constexpr int KO = decltype(slot_c)::value * kQStage;  // K rows of the stage
         constexpr int VO = KO + kQTileB;                        // V rows
         constexpr bool MASK = decltype(mask_c)::value;
-        // ---- S^T = K Q^T and dP^T = V dO^T (64 keys x 32 queries; lane = query)
+        // ---- S^T = K Q^T and dP^T = V dO^T (64 keys x 32 queries; lane = query).
+        // All sixteen operand reads go out at once (K then V of each key tile);
+        // each group of MFMAs waits only for its own operands.
         f32x16 s[2], dp[2];
-        {
-            u32x4 ka[KS], va[KS];
-            ka[0] = ds_read128<KO>(a_base[0]);
-            ka[1] = ds_read128<KO>(a_base[1]);
-            ka[2] = ds_read128<KO>(a_base[2]);
-            ka[3] = ds_read128<KO>(a_base[3]);
-            va[0] = ds_read128<VO>(a_base[0]);
-            va[1] = ds_read128<VO>(a_base[1]);
-            va[2] = ds_read128<VO>(a_base[2]);
-            va[3] = ds_read128<VO>(a_base[3]);
-            lgkm_wait<0>();
+        u32x4 ka[2][KS], va[2][KS];
+        ka[0][0] = ds_read128<KO>(a_base[0]);
+        ka[0][1] = ds_read128<KO>(a_base[1]);
+        ka[0][2] = ds_read128<KO>(a_base[2]);
+        ka[0][3] = ds_read128<KO>(a_base[3]);
+        va[0][0] = ds_read128<VO>(a_base[0]);
+        va[0][1] = ds_read128<VO>(a_base[1]);
+        va[0][2] = ds_read128<VO>(a_base[2]);
+        va[0][3] = ds_read128<VO>(a_base[3]);
+        ka[1][0] = ds_read128<KO + 32 * kRowB>(a_base[0]);
+        ka[1][1] = ds_read128<KO + 32 * kRowB>(a_base[1]);
+        ka[1][2] = ds_read128<KO + 32 * kRowB>(a_base[2]);
+        ka[1][3] = ds_read128<KO + 32 * kRowB>(a_base[3]);
+        va[1][0] = ds_read128<VO + 32 * kRowB>(a_base[0]);
+        va[1][1] = ds_read128<VO + 32 * kRowB>(a_base[1]);
+        va[1][2] = ds_read128<VO + 32 * kRowB>(a_base[2]);
+        va[1][3] = ds_read128<VO + 32 * kRowB>(a_base[3]);
+        lgkm_wait<12>();
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) { settle(ka[ks]); settle(va[ks]); }
-            s[0] = f32x16{};
-            dp[0] = nd_init;
+        for (int ks = 0; ks < KS; ++ks) settle(ka[0][ks]);
+        s[0] = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s[0] = T::mfma32(ka[ks], qf[ks], s[0]);
-                dp[0] = T::mfma32(va[ks], dof[ks], dp[0]);
-            }
-        }
-        {
-            u32x4 ka[KS], va[KS];
-            ka[0] = ds_read128<KO + 32 * kRowB>(a_base[0]);
-            ka[1] = ds_read128<KO + 32 * kRowB>(a_base[1]);
-            ka[2] = ds_read128<KO + 32 * kRowB>(a_base[2]);
-            ka[3] = ds_read128<KO + 32 * kRowB>(a_base[3]);
-            va[0] = ds_read128<VO + 32 * kRowB>(a_base[0]);
-            va[1] = ds_read128<VO + 32 * kRowB>(a_base[1]);
-            va[2] = ds_read128<VO + 32 * kRowB>(a_base[2]);
-            va[3] = ds_read128<VO + 32 * kRowB>(a_base[3]);
-            lgkm_wait<0>();
+        for (int ks = 0; ks < KS; ++ks) s[0] = T::mfma32(ka[0][ks], qf[ks], s[0]);
+        lgkm_wait<8>();
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) { settle(ka[ks]); settle(va[ks]); }
-            s[1] = f32x16{};
-            dp[1] = nd_init;
+        for (int ks = 0; ks < KS; ++ks) settle(va[0][ks]);
+        dp[0] = nd_init;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s[1] = T::mfma32(ka[ks], qf[ks], s[1]);
-                dp[1] = T::mfma32(va[ks], dof[ks], dp[1]);
-            }
-        }
+        for (int ks = 0; ks < KS; ++ks) dp[0] = T::mfma32(va[0][ks], dof[ks], dp[0]);
+        lgkm_wait<4>();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) settle(ka[1][ks]);
+        s[1] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s[1] = T::mfma32(ka[1][ks], qf[ks], s[1]);
+        lgkm_wait<0>();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) settle(va[1][ks]);
+        dp[1] = nd_init;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) dp[1] = T::mfma32(va[1][ks], dof[ks], dp[1]);
         // K^T operands of the whole block (key chunks 0 and 1 first), issued
         // before the element-wise work
         u32x2 ktr[4][DT][2];
