@@ -88,9 +88,9 @@ COPY_PROBE_KIB = 262144
 COUNTERS = {
     # workload: {stage: (FETCH_SIZE KiB, WRITE_SIZE KiB, copy FETCH_SIZE KiB, copy WRITE_SIZE KiB, sources sha)}
     "gpt2_small_causal": {
-        "fwd": (18625.5, 12672.0, 131089.0, 262144.0, "67a35d39f0ef5702"),
-        "prep": (12492.7, 768.0, 131089.0, 262144.0, "08c771edc271bfbc"),
-        "main": (76104.4, 36864.0, 131089.0, 262144.0, "08c771edc271bfbc"),
+        "fwd": (18539.3, 12672.0, 131088.5, 262144.0, "67a35d39f0ef5702"),
+        "prep": (12492.7, 768.0, 131088.5, 262144.0, "772f7ee8ed4a0449"),
+        "main": (63376.6, 36864.0, 131088.5, 262144.0, "772f7ee8ed4a0449"),
     },
 }
 

@@ -153,12 +153,18 @@ struct PrepArgs {
 
 // ---------------------------------------------------------------- 1. prep
 // PD / 8 lanes per row (head dim PD), 8 elements each; a workgroup covers
-// kPrepRounds rounds of rows, every round's loads issued before any sum. One
+// kPrepRounds rounds of rows, every round's loads (O, dO and the row's lse)
+// issued before any sum; the row sum runs over the row's lanes with DPP. One
 // round per workgroup measured fastest: more workgroups in flight beat more
 // rows per lane.
 constexpr int kPrepRounds = 1;
 template <int PD>
 constexpr int kPrepRows = kPrepRounds * kThreads / (PD / 8);
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
 
 template <typename T, int PD, bool GEN = false>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(PrepArgs a) {
@@ -167,6 +173,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(PrepArgs a) {
     const int tid = threadIdx.x, part = tid % LPR;
     const int64_t row0 = (int64_t)blockIdx.x * kPrepRows<PD> + tid / LPR;
     u32x4 ov[kPrepRounds], dv[kPrepRounds];
+    float lv[kPrepRounds];
     bool live[kPrepRounds];  // general shapes: the row belongs to its sequence
 #pragma unroll
     for (int k = 0; k < kPrepRounds; ++k) {
@@ -185,6 +192,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(PrepArgs a) {
             ov[k] = *reinterpret_cast<const u32x4*>(a.o + r * PD + part * 8);
             dv[k] = *reinterpret_cast<const u32x4*>(a.dout + r * PD + part * 8);
         }
+        lv[k] = part == 1 ? a.lse[r] : 0.f;
     }
 #pragma unroll
     for (int k = 0; k < kPrepRounds; ++k) {
@@ -194,12 +202,15 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(PrepArgs a) {
             acc = __builtin_fmaf(T::to_f32((uint16_t)(ov[k][w] & 0xFFFF)), T::to_f32((uint16_t)(dv[k][w] & 0xFFFF)), acc);
             acc = __builtin_fmaf(T::to_f32((uint16_t)(ov[k][w] >> 16)), T::to_f32((uint16_t)(dv[k][w] >> 16)), acc);
         }
-#pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+        // sum over the row's LPR lanes (8 or 16 consecutive lanes of a DPP row)
+        if constexpr (LPR == 16) acc += dpp_f32<0x140>(acc);  // row_mirror
+        acc += dpp_f32<0x141>(acc);                            // row_half_mirror
+        acc += dpp_f32<0xB1>(acc);                             // quad_perm [1,0,3,2]
+        acc += dpp_f32<0x4E>(acc);                             // quad_perm [2,3,0,1]
         const int64_t row = row0 + k * RPR;
         if (live[k]) {
             if (part == 0) a.delta[row] = -acc;  // stored negated: the initial dP accumulator
-            if (part == 1) a.lse2[row] = a.lse[row] * kLog2e;
+            if (part == 1) a.lse2[row] = lv[k] * kLog2e;
         }
     }
 }
