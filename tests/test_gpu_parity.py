@@ -345,3 +345,39 @@ def test_backward_on_a_side_stream():
         else:
             for x, y in zip((dq, dk, dv), ref):
                 assert (x.float() - y.float()).abs().max().item() < 2e-2
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_offsets_beyond_2_31_elements(causal):
+    """1040 x 32 heads of 1024 x 64: 2.18e9 elements per tensor (4.4 GB in bf16), so
+    the last heads start past element 2^31 and their addresses need 64-bit
+    arithmetic everywhere (tensor offsets, lse and workspace rows, grid mapping). The
+    checked heads (first, one past 2^31 elements, last) hold seeded inputs and are
+    compared completely with the oracle; the other heads hold device-generated
+    Gaussians and only have to come out finite."""
+    B, H, N, d = 1040, 32, 1024, 64
+    assert B * H * N * d > 2 ** 31
+    sc = scale_for(d)
+    log(f"large offsets B={B} H={H} N={N} d={d} causal={causal}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(8100 + causal)
+    q, k, v, do = (torch.randn((B, H, N, d), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(4))
+    picks = [(0, 0), (1030, 7), (B - 1, H - 1)]
+    assert all((b * H + h) * N * d > 2 ** 31 for b, h in picks[1:])
+    drawn = {}
+    for i, (b, h) in enumerate(picks):
+        drawn[(b, h)] = inputs(8200 + 10 * causal + i, (1, 1, N, d), "bf16")
+        for t, x in zip((q, k, v, do), drawn[(b, h)]):
+            t[b, h].copy_(x.torch("cuda")[0, 0])
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=sc)
+    dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    for t in (o, dq, dk, dv):
+        assert bool(torch.isfinite(t[-1]).all()) and bool(torch.isfinite(t[:, -1]).all())
+    for (b, h), xs in drawn.items():
+        log(f"  head b={b} h={h}")
+        r = oracle.bwd(*(x.f64 for x in xs), sc, causal)
+        for name, g in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+            check(name, g[b, h], r[name][0, 0], "bf16")
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
