@@ -347,26 +347,28 @@ def test_backward_on_a_side_stream():
                 assert (x.float() - y.float()).abs().max().item() < 2e-2
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_offsets_beyond_2_31_elements(causal):
-    """1040 x 32 heads of 1024 x 64: 2.18e9 elements per tensor (4.4 GB in bf16), so
-    the last heads start past element 2^31 and their addresses need 64-bit
-    arithmetic everywhere (tensor offsets, lse and workspace rows, grid mapping). The
-    checked heads (first, one past 2^31 elements, last) hold seeded inputs and are
-    compared completely with the oracle; the other heads hold device-generated
-    Gaussians and only have to come out finite."""
-    B, H, N, d = 1040, 32, 1024, 64
+def test_offsets_beyond_2_31_elements(causal, d):
+    """B x 32 heads of 1024 x d with B = 1040 (d = 64) or 520 (d = 128): 2.18e9
+    elements per tensor (4.4 GB in bf16), so the last heads start past element 2^31
+    and their addresses need 64-bit arithmetic everywhere (tensor offsets, lse and
+    workspace rows, grid mapping). The checked heads (first, one past 2^31
+    elements, last) hold seeded inputs and are compared completely with the
+    oracle; the other heads hold device-generated Gaussians and only have to come
+    out finite."""
+    B, H, N = (1040 if d == 64 else 520), 32, 1024
     assert B * H * N * d > 2 ** 31
     sc = scale_for(d)
     log(f"large offsets B={B} H={H} N={N} d={d} causal={causal}")
     gen = torch.Generator(device="cuda")
-    gen.manual_seed(8100 + causal)
+    gen.manual_seed(8100 + causal + d)
     q, k, v, do = (torch.randn((B, H, N, d), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(4))
-    picks = [(0, 0), (1030, 7), (B - 1, H - 1)]
+    picks = [(0, 0), (B - 2, 7), (B - 1, H - 1)]
     assert all((b * H + h) * N * d > 2 ** 31 for b, h in picks[1:])
     drawn = {}
     for i, (b, h) in enumerate(picks):
-        drawn[(b, h)] = inputs(8200 + 10 * causal + i, (1, 1, N, d), "bf16")
+        drawn[(b, h)] = inputs(8200 + 10 * causal + i + d, (1, 1, N, d), "bf16")
         for t, x in zip((q, k, v, do), drawn[(b, h)]):
             t[b, h].copy_(x.torch("cuda")[0, 0])
     o, lse = fa.fwd(q, k, v, causal=causal, scale=sc)
