@@ -11,7 +11,11 @@ for causal. The backward alone is credited with its five matrix products,
 10*B*H*N^2*d (halved for causal), whatever the kernels recompute.
 
 The timed region is K whole steps between two HIP events on the stream the
-library enqueues on, with nothing else inside it. The dominant kernel's
+library enqueues on, with nothing else inside it. It comes after the passes
+below, which add to the W warm-up steps: the GPU's clock takes several
+milliseconds of sustained load to settle (the same 50 GPT-2-small steps timed
+right after 10 warm-up steps ran at ~102 us per step against ~85-88 us after the
+passes), and the steady state is what a training loop sees. The dominant kernel's
 average launch duration (for the roofline entry) comes from a pass of K steps
 of its own with events around that kernel's launches only, and the per-stage
 breakdown from another pass with events around every launch (each event adds
